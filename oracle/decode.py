@@ -1,0 +1,207 @@
+"""Oracle for single-token paged-KV GQA decode, unsplit and split-K.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): only tests/, the smoke
+entry and bench.py's cpu_baseline leg use it.
+
+Sources (the pages this restates; no code is taken from them):
+  * PagedAttention V2 Triton page (``paged_attention_v2_triton.py``):
+    ``_partition_attn_kernel`` (paged gather through ``block_tables``, x-packed
+    key layout, GQA head grouping, empty-partition sentinel m=-inf / l=0) and
+    ``_reduce_partitions_kernel`` (partitions per sequence = ceil(len / ps)).
+  * Flash-decode blog post (koas-w, "flashdecode"): token-major K/V layout,
+    ``Decode_Paged_GQAAttention_Kernel`` (unsplit online softmax, o / l),
+    ``_flash_decode_partial_kernel`` (unnormalized partial accumulator) and
+    ``_flash_decode_combine_kernel`` (M = max m_s, f = exp(m_s - M),
+    out = sum f * acc_s / sum f * l_s; zeros for an empty context).
+
+Readings taken where the pages differ or are silent (each listed in the design doc):
+  partial acc is unnormalized; partial m is in natural-log units of the scaled
+  score; partitions are token ranges [p*ps, min((p+1)*ps, len)); an empty
+  sequence gives out = 0 and lse = -inf; query head h reads kv head h // G.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TOKEN_MAJOR = "token_major"
+XPACKED = "xpacked"
+
+
+def _as_f64(x) -> np.ndarray:
+    """Exact upcast to float64 (bf16 and fp32 values are representable in fp64)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu").to(torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float64)
+
+
+def _as_int(x) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu").to(torch.int64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.int64)
+
+
+def gather_sequence(key_cache, value_cache, layout: str, block_table_row, n: int,
+                    block_size: int):
+    """Contiguous K and V, each [num_kv_heads, n, head_dim], of one sequence.
+
+    Token t sits in physical block ``block_table_row[t // block_size]`` at slot
+    ``t % block_size`` (PagedAttention V2 page, ``_partition_attn_kernel``, paged
+    K/V gather; flash-decode post, per-block loop of the unsplit kernel).
+    Token-major pools are [num_blocks, KVH, bs, D]; x-packed K is
+    [num_blocks, KVH, D / x, bs, x] with element (t, d) at [blk, h, d // x, t % bs, d % x]
+    and x-packed V is [num_blocks, KVH, D, bs] with element (t, d) at [blk, h, d, t % bs].
+    """
+    kc = _as_f64(key_cache)
+    vc = _as_f64(value_cache)
+    row = _as_int(block_table_row)
+    t = np.arange(n)
+    blk = row[t // block_size]
+    if n and (blk.min() < 0 or blk.max() >= kc.shape[0]):
+        raise ValueError("block table entry outside the pool for a valid token")
+    off = t % block_size
+    kvh = kc.shape[1]
+    if layout == TOKEN_MAJOR:
+        d_model = kc.shape[3]
+        K = np.empty((kvh, n, d_model))
+        V = np.empty((kvh, n, d_model))
+        for h in range(kvh):
+            K[h] = kc[blk, h, off, :]
+            V[h] = vc[blk, h, off, :]
+    elif layout == XPACKED:
+        x = kc.shape[4]
+        d_model = kc.shape[2] * x
+        d = np.arange(d_model)
+        K = np.empty((kvh, n, d_model))
+        V = np.empty((kvh, n, d_model))
+        for h in range(kvh):
+            K[h] = kc[blk[:, None], h, (d // x)[None, :], off[:, None], (d % x)[None, :]]
+            V[h] = vc[blk[:, None], h, d[None, :], off[:, None]]
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+    return K, V
+
+
+def _kv_head(h: int, group: int) -> int:
+    """Query head h belongs to the contiguous group of kv head h // G (both decode pages)."""
+    return h // group
+
+
+def _scores(q_vec: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
+    """s_t = scale * <q, k_t> for every token t of the sequence."""
+    return scale * (K @ q_vec)
+
+
+def decode(query, key_cache, value_cache, layout: str, block_tables, seq_lens, scale: float,
+           num_kv_heads: int, block_size: int):
+    """Unsplit decode attention. Returns (out [S,H,D], lse [S,H]) in float64.
+
+    out[b,h] = sum_t softmax(s)_t v_t and lse[b,h] = log sum_t exp(s_t), natural log,
+    over the sequence's len_b tokens. len_b = 0 gives zeros and -inf.
+    """
+    q = _as_f64(query)
+    bt = _as_int(block_tables)
+    lens = _as_int(seq_lens)
+    S, H, D = q.shape
+    if H % num_kv_heads:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    G = H // num_kv_heads
+    out = np.zeros((S, H, D))
+    lse = np.full((S, H), -np.inf)
+    for b in range(S):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        K, V = gather_sequence(key_cache, value_cache, layout, bt[b], n, block_size)
+        for h in range(H):
+            kh = _kv_head(h, G)
+            s = _scores(q[b, h], K[kh], scale)
+            M = s.max()
+            e = np.exp(s - M)
+            Z = e.sum()
+            out[b, h] = (e @ V[kh]) / Z
+            lse[b, h] = M + np.log(Z)
+    return out, lse
+
+
+def decode_partials(query, key_cache, value_cache, layout: str, block_tables, seq_lens,
+                    scale: float, num_kv_heads: int, block_size: int, partition_size: int,
+                    max_num_partitions: int):
+    """Split-K partials per (b, h, p): (acc [S,H,P,D], m [S,H,P], l [S,H,P]) in float64.
+
+    Partition p of sequence b covers tokens [p*ps, min((p+1)*ps, len_b)). For each
+    non-empty one, m = max_t s_t, l = sum_t exp(s_t - m) and acc = sum_t exp(s_t - m) v_t
+    (unnormalized, as the flash-decode post's partial kernel keeps it). Partitions with
+    p*ps >= len_b carry the sentinel m = -inf, l = 0 (PagedAttention V2 page, unused-
+    partition branch); their acc is left 0 here and is not part of the contract.
+    """
+    q = _as_f64(query)
+    bt = _as_int(block_tables)
+    lens = _as_int(seq_lens)
+    S, H, D = q.shape
+    G = H // num_kv_heads
+    P = int(max_num_partitions)
+    ps = int(partition_size)
+    if ps < 1:
+        raise ValueError("partition_size must be >= 1")
+    acc = np.zeros((S, H, P, D))
+    m = np.full((S, H, P), -np.inf)
+    l = np.zeros((S, H, P))
+    for b in range(S):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        nparts = -(-n // ps)
+        if nparts > P:
+            raise ValueError("max_num_partitions too small for this sequence")
+        K, V = gather_sequence(key_cache, value_cache, layout, bt[b], n, block_size)
+        for h in range(H):
+            kh = _kv_head(h, G)
+            s = _scores(q[b, h], K[kh], scale)
+            for p in range(nparts):
+                t0, t1 = p * ps, min((p + 1) * ps, n)
+                sp = s[t0:t1]
+                mp = sp.max()
+                e = np.exp(sp - mp)
+                m[b, h, p] = mp
+                l[b, h, p] = e.sum()
+                acc[b, h, p] = e @ V[kh][t0:t1]
+    return acc, m, l
+
+
+def reduce_partials(partial_acc, partial_m, partial_l, seq_lens, partition_size: int):
+    """Cross-partition combine. Returns (out [S,H,D], lse [S,H]) in float64.
+
+    Over the P_b = ceil(len_b / ps) partitions of sequence b: M = max_p m_p,
+    w_p = exp(m_p - M), out = sum_p w_p acc_p / sum_p w_p l_p and
+    lse = M + log(sum_p w_p l_p) (flash-decode post, combine kernel; the partition
+    count per sequence follows the PagedAttention V2 page's reduce kernel).
+    Partitions p >= P_b are never read. len_b = 0 gives zeros and -inf.
+    """
+    acc = _as_f64(partial_acc)
+    m = _as_f64(partial_m)
+    l = _as_f64(partial_l)
+    lens = _as_int(seq_lens)
+    S, H, P, D = acc.shape
+    out = np.zeros((S, H, D))
+    lse = np.full((S, H), -np.inf)
+    for b in range(S):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        nparts = -(-n // int(partition_size))
+        for h in range(H):
+            mp = m[b, h, :nparts]
+            M = mp.max()
+            w = np.exp(mp - M)
+            Z = w @ l[b, h, :nparts]
+            out[b, h] = (w @ acc[b, h, :nparts]) / Z
+            lse[b, h] = M + np.log(Z)
+    return out, lse

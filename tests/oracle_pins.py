@@ -1,0 +1,407 @@
+"""Pins for the float64 oracle: checks against values the oracle does not compute itself.
+
+Each ``pin_*`` takes an oracle module ``orc`` (the real one, or a mutant with a planted
+mistake built by ``test_oracle_mutations.py``) and raises AssertionError when the oracle
+disagrees with:
+  * hand-worked closed-form fixtures under tests/golden/ (each states its derivation);
+  * dense brute force on logical (unpaged) K/V that the pin scatters into a pool with its
+    own explicit loops, evaluated with library routines (scipy softmax / logsumexp,
+    torch repeat_interleave for the head grouping, torch SDPA for MLA);
+  * closed forms for special cases (constant V, one token, zero query);
+  * invariants (page permutation, split count, trailing sentinels, causal perturbation).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import scipy.special as sps
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _close(a, b, tol=1e-12, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    with np.errstate(invalid="ignore"):
+        diff = np.where(both_inf, 0.0, np.abs(a - b))
+    assert np.all(np.isfinite(diff)), f"{what}: non-finite mismatch"
+    assert diff.max(initial=0.0) <= tol * (1.0 + np.abs(np.where(both_inf, 0, b)).max(initial=0.0)), \
+        f"{what}: max diff {diff.max()}"
+
+
+# ----------------------------------------------------------------------------------------
+# Independent construction of paged pools (explicit per-element loops over the layouts)
+# ----------------------------------------------------------------------------------------
+
+def scatter_pool(logical_k, logical_v, lens, block_size, num_blocks, layout, x=4, rng=None,
+                 fill=np.nan):
+    """Scatter per-sequence K/V [KVH, n, D] into a paged pool, one element at a time.
+
+    Token-major K/V: pool[blk, h, slot, d]. x-packed K: pool[blk, h, d // x, slot, d % x];
+    x-packed V: pool[blk, h, d, slot]. Pages are handed out by a random permutation.
+    Every slot never written stays ``fill`` (NaN), so a gather that touches one shows up.
+    """
+    rng = rng if rng is not None else np.random.default_rng(123)
+    S = len(lens)
+    kvh, _, D = logical_k[0].shape
+    pages = [-(-int(n) // block_size) for n in lens]
+    perm = rng.permutation(num_blocks)
+    width = max(1, max(pages))
+    bt = np.full((S, width), -1, dtype=np.int64)
+    cur = 0
+    for b in range(S):
+        bt[b, :pages[b]] = perm[cur:cur + pages[b]]
+        cur += pages[b]
+    if layout == "token_major":
+        kc = np.full((num_blocks, kvh, block_size, D), fill)
+        vc = np.full((num_blocks, kvh, block_size, D), fill)
+    else:
+        kc = np.full((num_blocks, kvh, D // x, block_size, x), fill)
+        vc = np.full((num_blocks, kvh, D, block_size), fill)
+    for b in range(S):
+        for t in range(int(lens[b])):
+            blk = bt[b, t // block_size]
+            slot = t % block_size
+            for h in range(kvh):
+                for d in range(D):
+                    if layout == "token_major":
+                        kc[blk, h, slot, d] = logical_k[b][h, t, d]
+                        vc[blk, h, slot, d] = logical_v[b][h, t, d]
+                    else:
+                        kc[blk, h, d // x, slot, d % x] = logical_k[b][h, t, d]
+                        vc[blk, h, d, slot] = logical_v[b][h, t, d]
+    return kc, vc, bt
+
+
+def _random_logical(rng, lens, kvh, D):
+    K = [rng.standard_normal((kvh, int(n), D)) for n in lens]
+    V = [rng.standard_normal((kvh, int(n), D)) for n in lens]
+    return K, V
+
+
+def _brute_decode(q, K, V, lens, scale, G):
+    """Dense reference: expand kv heads to query heads with repeat_interleave, then
+    scipy softmax / logsumexp per head."""
+    S, H, D = q.shape
+    out = np.zeros((S, H, D))
+    lse = np.full((S, H), -np.inf)
+    for b in range(S):
+        if int(lens[b]) == 0:
+            continue
+        Ke = torch.repeat_interleave(torch.from_numpy(K[b]), G, dim=0).numpy()
+        Ve = torch.repeat_interleave(torch.from_numpy(V[b]), G, dim=0).numpy()
+        for h in range(H):
+            logits = scale * np.einsum("td,d->t", Ke[h], q[b, h])
+            out[b, h] = sps.softmax(logits) @ Ve[h]
+            lse[b, h] = sps.logsumexp(logits)
+    return out, lse
+
+
+def _tiny_case(seed, lens, H, KVH, D, bs, layout, num_blocks=None, x=4):
+    rng = np.random.default_rng(seed)
+    K, V = _random_logical(rng, lens, KVH, D)
+    pages = sum(-(-int(n) // bs) for n in lens)
+    nb = num_blocks if num_blocks is not None else pages + 3
+    kc, vc, bt = scatter_pool(K, V, lens, bs, nb, layout, x=x, rng=rng)
+    q = rng.standard_normal((len(lens), H, D))
+    return q, kc, vc, bt, np.asarray(lens), K, V
+
+
+# ----------------------------------------------------------------------------------------
+# Decode pins
+# ----------------------------------------------------------------------------------------
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _xpack_from_token_major(kc_tm, vc_tm, x):
+    nb, kvh, bs, D = kc_tm.shape
+    kc = np.empty((nb, kvh, D // x, bs, x))
+    vc = np.empty((nb, kvh, D, bs))
+    for blk in range(nb):
+        for h in range(kvh):
+            for s in range(bs):
+                for d in range(D):
+                    kc[blk, h, d // x, s, d % x] = kc_tm[blk, h, s, d]
+                    vc[blk, h, d, s] = vc_tm[blk, h, s, d]
+    return kc, vc
+
+
+def pin_decode_worked_example(orc):
+    g = _load("decode_worked_example.json")
+    q = np.array(g["query"])
+    kc = np.array(g["key_cache_token_major"])
+    vc = np.array(g["value_cache_token_major"])
+    bt = np.array(g["block_tables"])
+    lens = np.array(g["seq_lens"])
+    exp_out = np.array(g["expected_out"])
+    exp_lse = np.array(g["expected_lse"])
+    kx, vx = _xpack_from_token_major(kc, vc, 2)
+    for layout, k, v in (("token_major", kc, vc), ("xpacked", kx, vx)):
+        out, lse = orc.decode(q, k, v, layout, bt, lens, g["scale"], g["num_kv_heads"], g["block_size"])
+        _close(out, exp_out, what=f"worked out {layout}")
+        _close(lse, exp_lse, what=f"worked lse {layout}")
+        acc, m, l = orc.decode_partials(q, k, v, layout, bt, lens, g["scale"], g["num_kv_heads"],
+                                        g["block_size"], g["partition_size"], g["max_num_partitions"])
+        em = np.array([[[(-np.inf if z is None else z) for z in row] for row in b] for b in g["expected_partial_m"]])
+        _close(m, em, what="worked partial m")
+        _close(l, np.array(g["expected_partial_l"]), what="worked partial l")
+        for h in range(2):
+            for p in range(2):
+                _close(acc[0, h, p], np.array(g["expected_partial_acc"][0][h][p]), what="worked partial acc")
+        out2, lse2 = orc.reduce_partials(acc, m, l, lens, g["partition_size"])
+        _close(out2, exp_out, what="worked reduce out")
+        _close(lse2, exp_lse, what="worked reduce lse")
+
+
+def pin_reduce_worked_example(orc):
+    """Reduce on hand-set partials: m=[0, ln3], l=[1, 1] -> weights 1/4, 3/4."""
+    acc = np.zeros((1, 1, 3, 2))
+    acc[0, 0, 0] = [4.0, 0.0]
+    acc[0, 0, 1] = [0.0, 8.0]
+    acc[0, 0, 2] = [np.nan, np.nan]        # sentinel partition: must never be read
+    m = np.array([[[0.0, math.log(3.0), -np.inf]]])
+    l = np.array([[[1.0, 1.0, 0.0]]])
+    out, lse = orc.reduce_partials(acc, m, l, np.array([7]), 4)   # ceil(7/4) = 2 partitions
+    _close(out[0, 0], [1.0, 6.0], what="reduce worked out")
+    _close(lse[0, 0], math.log(4.0), what="reduce worked lse")
+
+
+def pin_decode_brute_force(orc):
+    """Dense brute force on logical K/V, both layouts, several G, block sizes, tails."""
+    shapes = [  # lens, H, KVH, D, bs
+        ([5, 0, 33], 4, 2, 8, 4),
+        ([1, 17, 16], 3, 1, 8, 16),     # MQA, G=3
+        ([9, 2], 2, 2, 4, 2),           # MHA
+        ([40], 6, 2, 8, 16),            # G=3, several pages with a tail
+        ([3, 12, 31], 8, 2, 8, 1),      # block_size 1
+    ]
+    for i, (lens, H, KVH, D, bs) in enumerate(shapes):
+        for layout in ("token_major", "xpacked"):
+            q, kc, vc, bt, lens_a, K, V = _tiny_case(100 + i, lens, H, KVH, D, bs, layout)
+            scale = 0.37 + 0.1 * i
+            out, lse = orc.decode(q, kc, vc, layout, bt, lens_a, scale, KVH, bs)
+            ref_out, ref_lse = _brute_decode(q, K, V, lens_a, scale, H // KVH)
+            _close(out, ref_out, 1e-12, what=f"brute out {i} {layout}")
+            _close(lse, ref_lse, 1e-12, what=f"brute lse {i} {layout}")
+
+
+def pin_decode_special_cases(orc):
+    rng = np.random.default_rng(7)
+    lens = [1, 23, 48]
+    H, KVH, D, bs = 4, 2, 8, 16
+    q, kc, vc, bt, lens_a, K, V = _tiny_case(7, lens, H, KVH, D, bs, "token_major")
+    # constant V = c  ->  out = c for every head
+    c = rng.standard_normal(D)
+    Vc = [np.broadcast_to(c, v.shape).copy() for v in V]
+    kc2, vc2, bt2 = scatter_pool(K, Vc, lens, bs, kc.shape[0], "token_major", rng=np.random.default_rng(9))
+    out, _ = orc.decode(q, kc2, vc2, "token_major", bt2, lens_a, 0.5, KVH, bs)
+    for b in range(3):
+        for h in range(H):
+            _close(out[b, h], c, 1e-12, what="constant V")
+    # len = 1  ->  out = v_0 and lse = scale * q . k_0
+    out, lse = orc.decode(q, kc, vc, "token_major", bt, lens_a, 0.5, KVH, bs)
+    for h in range(H):
+        _close(out[0, h], V[0][h // 2, 0], 1e-12, what="len 1 out")
+        _close(lse[0, h], 0.5 * float(np.dot(q[0, h], K[0][h // 2, 0])), 1e-12, what="len 1 lse")
+    # q = 0  ->  out = mean of the value rows, lse = ln n
+    out, lse = orc.decode(np.zeros_like(q), kc, vc, "token_major", bt, lens_a, 0.5, KVH, bs)
+    for b in range(3):
+        for h in range(H):
+            _close(out[b, h], V[b][h // 2].mean(axis=0), 1e-12, what="q=0 mean")
+            _close(lse[b, h], math.log(lens[b]), 1e-12, what="q=0 lse")
+
+
+def pin_split_invariance(orc):
+    lens = [1, 16, 37, 100, 0]
+    H, KVH, D, bs = 6, 3, 8, 4
+    for layout in ("token_major", "xpacked"):
+        q, kc, vc, bt, lens_a, K, V = _tiny_case(11, lens, H, KVH, D, bs, layout)
+        out, lse = orc.decode(q, kc, vc, layout, bt, lens_a, 0.3, KVH, bs)
+        for ps in (1, 2, 3, 4, 8, 12, 64, 100, 130):
+            P = -(-max(lens) // ps) + 2
+            acc, m, l = orc.decode_partials(q, kc, vc, layout, bt, lens_a, 0.3, KVH, bs, ps, P)
+            o2, lse2 = orc.reduce_partials(acc, m, l, lens_a, ps)
+            _close(o2, out, 1e-12, what=f"split ps={ps}")
+            _close(lse2, lse, 1e-12, what=f"split lse ps={ps}")
+
+
+def pin_partition_stats(orc):
+    """Each partition's (m, l, acc) against scipy on that partition's own scores."""
+    lens = [45, 9]
+    H, KVH, D, bs, ps = 4, 2, 8, 4, 16
+    q, kc, vc, bt, lens_a, K, V = _tiny_case(13, lens, H, KVH, D, bs, "xpacked")
+    scale = 0.8
+    acc, m, l = orc.decode_partials(q, kc, vc, "xpacked", bt, lens_a, scale, KVH, bs, ps, 4)
+    for b, n in enumerate(lens):
+        Ke = torch.repeat_interleave(torch.from_numpy(K[b]), 2, dim=0).numpy()
+        Ve = torch.repeat_interleave(torch.from_numpy(V[b]), 2, dim=0).numpy()
+        for h in range(H):
+            s_all = scale * np.einsum("td,d->t", Ke[h], q[b, h])
+            for p in range(4):
+                t0, t1 = p * ps, min((p + 1) * ps, n)
+                if t0 >= n:
+                    assert m[b, h, p] == -np.inf and l[b, h, p] == 0.0, "sentinel"
+                    continue
+                sp = s_all[t0:t1]
+                _close(m[b, h, p], sp.max(), 1e-12, what="partition max")
+                _close(m[b, h, p] + math.log(l[b, h, p]), sps.logsumexp(sp), 1e-12, what="partition lse")
+                _close(acc[b, h, p] / l[b, h, p], sps.softmax(sp) @ Ve[h][t0:t1], 1e-12,
+                       what="partition normalized acc")
+
+
+def pin_sentinel_padding(orc):
+    """Extra trailing sentinel partitions leave the reduce unchanged, bit for bit."""
+    lens = [30, 5]
+    q, kc, vc, bt, lens_a, K, V = _tiny_case(17, lens, 2, 1, 8, 4, "token_major")
+    a1, m1, l1 = orc.decode_partials(q, kc, vc, "token_major", bt, lens_a, 1.0, 1, 4, 8, 4)
+    a2, m2, l2 = orc.decode_partials(q, kc, vc, "token_major", bt, lens_a, 1.0, 1, 4, 8, 9)
+    assert np.all(m2[:, :, 4:] == -np.inf) and np.all(l2[:, :, 4:] == 0.0)
+    assert np.all(m2[1, :, 1:] == -np.inf) and np.all(l2[1, :, 1:] == 0.0)
+    a2[:, :, 4:] = np.nan      # a reduce that reads past P_b turns this into NaN
+    a2[1, :, 1:] = np.nan
+    o1, s1 = orc.reduce_partials(a1, m1, l1, lens_a, 8)
+    o2, s2 = orc.reduce_partials(a2, m2, l2, lens_a, 8)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+
+
+def pin_page_permutation(orc):
+    """Permuting the pool's block axis (tables remapped) changes nothing, bit for bit."""
+    lens = [21, 50, 7]
+    for layout in ("token_major", "xpacked"):
+        q, kc, vc, bt, lens_a, K, V = _tiny_case(19, lens, 4, 2, 8, 4, layout)
+        out, lse = orc.decode(q, kc, vc, layout, bt, lens_a, 0.7, 2, 4)
+        perm = np.random.default_rng(5).permutation(kc.shape[0])
+        inv = np.empty_like(perm)
+        inv[perm] = np.arange(len(perm))
+        bt2 = np.where(bt >= 0, inv[np.maximum(bt, 0)], -1)
+        out2, lse2 = orc.decode(q, kc[perm], vc[perm], layout, bt2, lens_a, 0.7, 2, 4)
+        assert np.array_equal(out, out2) and np.array_equal(lse, lse2), "page permutation"
+
+
+def pin_empty_sequence(orc):
+    lens = [0, 3]
+    q, kc, vc, bt, lens_a, K, V = _tiny_case(23, lens, 2, 1, 4, 2, "token_major")
+    out, lse = orc.decode(q, kc, vc, "token_major", bt, lens_a, 1.0, 1, 2)
+    assert np.all(out[0] == 0.0) and np.all(lse[0] == -np.inf)
+    acc, m, l = orc.decode_partials(q, kc, vc, "token_major", bt, lens_a, 1.0, 1, 2, 2, 2)
+    assert np.all(m[0] == -np.inf) and np.all(l[0] == 0.0)
+    o2, s2 = orc.reduce_partials(acc, m, l, lens_a, 2)
+    assert np.all(o2[0] == 0.0) and np.all(s2[0] == -np.inf)
+
+
+# ----------------------------------------------------------------------------------------
+# MLA pins
+# ----------------------------------------------------------------------------------------
+
+def pin_mla_worked_example(orc):
+    g = _load("mla_worked_example.json")
+    O, lse2 = orc.mla_prefill(np.array(g["q_nope"]), np.array(g["q_pe"]), np.array(g["ckv_cache"]),
+                              np.array(g["kpe_cache"]), np.array(g["qo_indptr"]), np.array(g["kv_indptr"]),
+                              np.array(g["kv_indices"]), g["sm_scale"])
+    _close(O, np.array(g["expected_out"]), what="mla worked O")
+    _close(lse2, np.array(g["expected_lse2"]), what="mla worked lse2")
+
+
+def _mla_tiny(seed, q_lens, prefixes, H=3, Dc=8, Dp=4, extra=2):
+    rng = np.random.default_rng(seed)
+    kv_lens = [a + b for a, b in zip(q_lens, prefixes)]
+    qo = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
+    kv = np.concatenate([[0], np.cumsum(kv_lens)]).astype(np.int64)
+    n_pages = int(kv[-1]) + extra
+    idx = rng.permutation(n_pages)[: int(kv[-1])]
+    T = int(qo[-1])
+    qn = rng.standard_normal((T, H, Dc))
+    qp = rng.standard_normal((T, H, Dp))
+    ckv = rng.standard_normal((n_pages, 1, Dc))
+    kpe = rng.standard_normal((n_pages, 1, Dp))
+    return qn, qp, ckv, kpe, qo, kv, idx
+
+
+def _sdpa_rows(qn, qp, ckv, kpe, tok, q_len, sm_scale):
+    """torch float64 SDPA on [q_nope|q_pe] x [ckv|kpe] with an explicit bottom-right mask."""
+    kv_len = len(tok)
+    q = torch.from_numpy(np.concatenate([qn, qp], axis=-1)).permute(1, 0, 2)       # [H, q_len, Dc+Dp]
+    kk = torch.from_numpy(np.concatenate([ckv[tok, 0], kpe[tok, 0]], axis=-1))      # [kv_len, Dc+Dp]
+    vv = torch.from_numpy(ckv[tok, 0])                                              # [kv_len, Dc]
+    H = q.shape[0]
+    k = kk.unsqueeze(0).expand(H, -1, -1).contiguous()
+    v = vv.unsqueeze(0).expand(H, -1, -1).contiguous()
+    i = torch.arange(q_len)[:, None]
+    j = torch.arange(kv_len)[None, :]
+    mask = j <= (kv_len - q_len) + i
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=sm_scale)
+    logits = sm_scale * torch.matmul(q, k.transpose(-1, -2))
+    logits = logits.masked_fill(~mask, -math.inf)
+    lse2 = torch.logsumexp(logits, dim=-1) / math.log(2.0)
+    return o.permute(1, 0, 2).numpy(), lse2.permute(1, 0).numpy()
+
+
+def pin_mla_sdpa(orc):
+    """Ragged batch with permuted page ids against per-batch torch SDPA (float64)."""
+    q_lens, prefixes = [3, 1, 7, 4], [5, 0, 0, 11]
+    qn, qp, ckv, kpe, qo, kv, idx = _mla_tiny(29, q_lens, prefixes)
+    sm = 0.41
+    O, lse2 = orc.mla_prefill(qn, qp, ckv, kpe, qo, kv, idx, sm)
+    for b in range(len(q_lens)):
+        r0, r1 = qo[b], qo[b + 1]
+        ro, rl = _sdpa_rows(qn[r0:r1], qp[r0:r1], ckv, kpe, idx[kv[b]:kv[b + 1]], r1 - r0, sm)
+        _close(O[r0:r1], ro, 1e-12, what=f"mla sdpa O b={b}")
+        _close(lse2[r0:r1], rl, 1e-12, what=f"mla sdpa lse b={b}")
+
+
+def pin_mla_causal_perturbation(orc):
+    q_lens, prefixes = [6], [4]
+    qn, qp, ckv, kpe, qo, kv, idx = _mla_tiny(31, q_lens, prefixes, extra=0)
+    O, L = orc.mla_prefill(qn, qp, ckv, kpe, qo, kv, idx, 0.5)
+    for r in range(6):
+        abs_pos = 4 + r
+        ck2, kp2 = ckv.copy(), kpe.copy()
+        for j in range(abs_pos + 1, 10):
+            ck2[idx[j]] += 100.0
+            kp2[idx[j]] -= 50.0
+        O2, L2 = orc.mla_prefill(qn, qp, ck2, kp2, qo, kv, idx, 0.5)
+        assert np.array_equal(O2[r], O[r]) and np.array_equal(L2[r], L[r]), f"future key leaked into row {r}"
+        ck3 = ckv.copy()
+        ck3[idx[abs_pos]] += 1.0
+        O3, _ = orc.mla_prefill(qn, qp, ck3, kpe, qo, kv, idx, 0.5)
+        assert not np.array_equal(O3[r], O[r]), f"diagonal key ignored in row {r}"
+
+
+def pin_mla_special_cases(orc):
+    q_lens, prefixes = [5, 2], [3, 0]
+    qn, qp, ckv, kpe, qo, kv, idx = _mla_tiny(37, q_lens, prefixes)
+    O, L = orc.mla_prefill(np.zeros_like(qn), np.zeros_like(qp), ckv, kpe, qo, kv, idx, 0.9)
+    for b in range(2):
+        for i in range(q_lens[b]):
+            r = qo[b] + i
+            vis = prefixes[b] + i + 1
+            mean = torch.from_numpy(ckv[idx[kv[b]:kv[b] + vis], 0]).mean(dim=0).numpy()
+            for h in range(qn.shape[1]):
+                _close(O[r, h], mean, 1e-12, what="mla q=0 mean")
+                _close(L[r, h], math.log2(vis), 1e-12, what="mla q=0 lse2")
+    # a batch with no keys at all gives zeros and -inf (its rows see nothing)
+    qo_e = np.array([0, 2, 2 + q_lens[0]])
+    kv_e = np.array([0, 0, kv[1]])
+    rows = 2 + q_lens[0]
+    qn_e = np.concatenate([np.ones((2,) + qn.shape[1:]), qn[:q_lens[0]]])
+    qp_e = np.concatenate([np.ones((2,) + qp.shape[1:]), qp[:q_lens[0]]])
+    O, L = orc.mla_prefill(qn_e, qp_e, ckv, kpe, qo_e, kv_e, idx[:kv[1]], 0.9)
+    assert O.shape[0] == rows
+    assert np.all(O[:2] == 0.0) and np.all(L[:2] == -np.inf)
+
+
+DECODE_PINS = [pin_decode_worked_example, pin_reduce_worked_example, pin_decode_brute_force,
+               pin_decode_special_cases, pin_split_invariance, pin_partition_stats,
+               pin_sentinel_padding, pin_page_permutation, pin_empty_sequence]
+MLA_PINS = [pin_mla_worked_example, pin_mla_sdpa, pin_mla_causal_perturbation,
+            pin_mla_special_cases]
+ALL_PINS = DECODE_PINS + MLA_PINS
