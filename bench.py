@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark: achieved KV-cache HBM bandwidth and time per split-K paged decode step on one
+MI355X, with the roofline of the dominant kernel and the float64 CPU oracle beside it.
+
+A step is one pass of the decode hot path over one batch: paged_decode_partial followed by
+paged_decode_reduce on the same stream. The headline workload is the Llama-style GQA batch
+(B=32, H=32, KVH=8, D=128, bf16, lengths U[512, 4096], partition 512). The batch's KV pool
+is kept in R copies at different HBM addresses and the steps cycle through them (as
+successive layers of a model would), so that the 256 MB Infinity Cache cannot serve one
+step's KV from the previous step; every copy is resident before timing starts.
+
+Prints exactly one JSON line (rank 0, N = 1). ``--gpus N`` with N > 1 exits with a message:
+this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
+MALL_BYTES = 256 * 2**20
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama_gqa4",
+                    choices=["llama_gqa4", "wide_gqa6", "skewed_gqa8", "tiny_fp32", "mla_prefill_b8"])
+    ap.add_argument("--copies", type=int, default=0, help="KV pool copies to cycle (0 = auto)")
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time to spend")
+    return ap.parse_args()
+
+
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def bench_decode(case, steps, warmup, copies=0):
+    """Time `steps` decode steps; returns a dict of measurements."""
+    import torch
+    import paged_kv_gqa_table_amd as pkv
+
+    dev = "cuda"
+    q = case.query.to(dev)
+    bt = case.block_tables.to(dev)
+    lens = case.seq_lens.to(dev)
+    k0 = case.key_cache.to(dev)
+    v0 = case.value_cache.to(dev)
+    pool_bytes = 2 * k0.numel() * k0.element_size()
+    if copies <= 0:
+        copies = max(1, min(8, math.ceil(3 * MALL_BYTES / max(1, pool_bytes))))
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+    S, H, D = case.num_seqs, case.num_heads, case.head_dim
+    ps = case.partition_size
+    max_len = case.max_seq_len
+    P = case.num_partitions()
+    acc = torch.empty((S, H, P, D), dtype=torch.float32, device=dev)
+    m = torch.empty((S, H, P), dtype=torch.float32, device=dev)
+    l = torch.empty((S, H, P), dtype=torch.float32, device=dev)
+    out = torch.empty((S, H, D), dtype=case.query.dtype, device=dev)
+
+    def step(i, ev=None):
+        kc, vc = pools[i % copies]
+        if ev is not None:
+            ev[0].record()
+        pkv.paged_decode_partial(q, kc, vc, bt, lens, case.scale, case.num_kv_heads, ps, max_len,
+                                 acc, m, l, layout=case.layout)
+        if ev is not None:
+            ev[1].record()
+        pkv.paged_decode_reduce(acc, m, l, lens, ps, out)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Region 1 (the contract): exactly `steps` back-to-back steps between two synchronizes.
+    t_start, t_end = _events(2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = t_start.elapsed_time(t_end)
+
+    # Region 2: the same steps with HIP events around every phase-1 launch, on the stream
+    # the kernel runs on, for the dominant kernel's own average duration.
+    evs = [_events(2) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    part_ms = [a.elapsed_time(b) for a, b in evs]
+    part_ms.sort()
+    avg_part_ms = sum(part_ms) / len(part_ms)
+    med_part_ms = part_ms[len(part_ms) // 2]
+
+    kv_bytes = case.kv_bytes()
+    return dict(
+        copies=copies, pool_bytes=pool_bytes, kv_bytes=kv_bytes,
+        wall_ms_per_step=wall * 1e3 / steps, gpu_ms_per_step=gpu_ms / steps,
+        partial_avg_ms=avg_part_ms, partial_median_ms=med_part_ms,
+        partial_p10_ms=part_ms[len(part_ms) // 10], partial_p90_ms=part_ms[(9 * len(part_ms)) // 10],
+    )
+
+
+def bench_mla(case, steps, warmup):
+    import torch
+    import paged_kv_gqa_table_amd as pkv
+    dev = "cuda"
+    t = {k: getattr(case, k).to(dev) for k in ("q_nope", "q_pe", "ckv_cache", "kpe_cache", "qo_indptr",
+                                                "kv_indptr", "kv_indices")}
+    out = torch.empty_like(t["q_nope"])
+    lse = torch.empty(t["q_nope"].shape[:2], dtype=torch.float32, device=dev)
+    mql = case.max_q_len
+
+    def step():
+        pkv.mla_paged_prefill(t["q_nope"], t["q_pe"], t["ckv_cache"], t["kpe_cache"], t["qo_indptr"],
+                              t["kv_indptr"], t["kv_indices"], case.sm_scale, max_q_len=mql, out=out, lse=lse)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [_events(2) for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    avg = sum(ms) / len(ms)
+    flops = 16 * case.visible_pairs() * 2 * (512 + 64 + 512)
+    return dict(ms=avg, median_ms=ms[len(ms) // 2], flops=flops, tflops=flops / (avg * 1e-3) / 1e12)
+
+
+def cpu_baseline_decode(case, budget_s):
+    """The float64 oracle as it stands, timed on this host over whole sequences of the batch."""
+    import numpy as np
+    import oracle
+    import torch
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = os.cpu_count() or 1
+    threads = max(blas_threads, torch.get_num_threads())
+    lens = case.seq_lens.numpy()
+    order = list(range(case.num_seqs))
+    done_bytes = 0
+    done_seqs = 0
+    t0 = time.perf_counter()
+    per_tok = case.num_kv_heads * 2 * case.head_dim * (2 if case.dtype == "bf16" else 4)
+    for b in order:
+        idx = torch.tensor([b])
+        oracle.decode(case.query[idx], case.key_cache, case.value_cache, case.layout, case.block_tables[idx],
+                      case.seq_lens[idx], case.scale, case.num_kv_heads, case.block_size)
+        done_bytes += int(lens[b]) * per_tok
+        done_seqs += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done_seqs} of {case.num_seqs} sequences of the same batch (float64 numpy oracle, "
+                      f"{dt:.1f} s wall, all {case.num_heads} heads each)",
+            "seconds": round(dt, 2), "ms_per_step_equiv": dt * 1e3 * (case.kv_bytes() / max(done_bytes, 1))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(each GPU would run its own share of sequences with no exchange).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    from paged_kv_gqa_table_amd import inputs
+    import paged_kv_gqa_table_amd as pkv
+    pkv.lib()  # fail loudly if the HIP library is missing
+
+    result = {}
+    if args.workload == "mla_prefill_b8":
+        case = inputs.mla_prefill_b8()
+        r = bench_mla(case, args.steps, args.warmup)
+        result = {
+            "metric": "MLA causal paged prefill TFLOP/s (causal-visible flops) and us per prefill, 1x MI355X",
+            "value": r["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": r["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": case.name, "batch": case.batch, "total_q": case.total_q,
+                       "num_pages": case.num_pages},
+            "roofline": {"bound": "mfma", "achieved": r["tflops"], "peak": BF16_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": r["tflops"] / BF16_MFMA_PEAK_TFLOPS, "traffic": None},
+        }
+        print(json.dumps(result), flush=True)
+        return
+
+    _log(f"generating workload {args.workload}")
+    case = inputs.decode_workload(args.workload)
+    r = bench_decode(case, args.steps, args.warmup, args.copies)
+    kv = r["kv_bytes"]
+    ms = r["wall_ms_per_step"]
+    gbs = kv / (ms * 1e-3) / 1e9
+    achieved = kv / (r["partial_avg_ms"] * 1e-3) / 1e9
+    result = {
+        "metric": "achieved KV-cache HBM GB/s (% of peak) and us per decode step, 1x MI355X",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "us_per_step": ms * 1e3, "pct_of_peak": 100.0 * gbs / HBM_PEAK_GBS,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": case.dtype, "data": "synthetic",
+        "config": {"workload": case.name, "num_seqs": case.num_seqs, "num_heads": case.num_heads,
+                   "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
+                   "block_size": case.block_size, "partition_size": case.partition_size,
+                   "layout": case.layout, "kv_bytes_per_step": kv, "pool_copies_cycled": r["copies"],
+                   "seq_len_total": int(case.seq_lens.sum())},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "paged_decode_partial", "kernel_avg_us": r["partial_avg_ms"] * 1e3,
+                     "kernel_median_us": r["partial_median_ms"] * 1e3,
+                     "kernel_p10_us": r["partial_p10_ms"] * 1e3, "kernel_p90_us": r["partial_p90_ms"] * 1e3},
+        "gpu_event_ms_per_step": r["gpu_ms_per_step"],
+    }
+    if not args.no_extra and args.workload == "llama_gqa4":
+        extra = {}
+        for name in ("wide_gqa6", "skewed_gqa8"):
+            _log(f"secondary workload {name}")
+            c2 = inputs.decode_workload(name)
+            r2 = bench_decode(c2, max(10, args.steps // 4), 5)
+            extra[name] = {"us_per_step": r2["wall_ms_per_step"] * 1e3,
+                           "GB_s": c2.kv_bytes() / (r2["wall_ms_per_step"] * 1e-3) / 1e9,
+                           "partial_GB_s": c2.kv_bytes() / (r2["partial_avg_ms"] * 1e-3) / 1e9,
+                           "layout": c2.layout}
+            extra[name]["pct_of_peak"] = 100.0 * extra[name]["GB_s"] / HBM_PEAK_GBS
+            del c2
+            torch.cuda.empty_cache()
+        try:
+            _log("secondary workload mla_prefill_b8")
+            mc = inputs.mla_prefill_b8()
+            rm = bench_mla(mc, 20, 3)
+            extra["mla_prefill_b8"] = {"us": rm["ms"] * 1e3, "TFLOP_s": rm["tflops"],
+                                       "frac_of_bf16_mfma_peak": rm["tflops"] / BF16_MFMA_PEAK_TFLOPS}
+        except NotImplementedError as e:
+            extra["mla_prefill_b8"] = {"error": str(e)}
+        result["extra"] = extra
+    if not args.no_cpu:
+        _log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline_decode(case, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

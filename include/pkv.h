@@ -1,0 +1,170 @@
+/*
+ * pkv.h -- C ABI of the paged-KV attention library for AMD Instinct MI355X (gfx950).
+ *
+ * Three operations:
+ *   paged_decode_partial  split-K single-token decode over a paged KV cache with
+ *                         grouped-query heads: per-partition online-softmax partials
+ *   paged_decode_reduce   log-sum-exp weighted combine of those partials
+ *   mla_paged_prefill     MLA causal paged prefill (page_size 1), base-2 LSE
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer (HIP global memory) owned by the
+ *     caller; every scalar is a host value. The library allocates nothing, keeps no
+ *     pointer after returning, and launches asynchronously on `stream` (a hipStream_t
+ *     passed as void*; NULL means the default stream). Results are ready when that
+ *     stream has drained up to the launch.
+ *   - Tensors are dense and row-major (C order) in the shapes given below.
+ *   - The return value is a pkv_status. On any status other than PKV_OK nothing was
+ *     launched (argument errors are found on the host before any HIP call), except
+ *     PKV_EHIP, which reports a launch failure from the HIP runtime. pkv_last_error()
+ *     returns a message for the calling thread's last non-OK status.
+ *   - The library is stateless and reentrant; calls on different streams may overlap.
+ *   - Values that live in device memory (lengths, page ids, index pointers) cannot be
+ *     checked on the host. Kernels clamp every such value into the range that keeps
+ *     their memory accesses inside the buffers described here, so a caller that breaks
+ *     the stated contract gets unspecified numbers, never an out-of-bounds access.
+ *
+ * Sources for what is computed (pages named by title; no code taken from them):
+ *   [PAv2]  "paged_attention_v2_triton.py -- CCCL-derived Triton PagedAttention V2"
+ *           (dev.modelhub.org.cn, project_6): the two-kernel split design, the
+ *           x-packed key layout, the empty-partition sentinel, the launcher arguments.
+ *   [FD]    koas-w.github.io flash-decode post (2026-05-25): the token-major K/V
+ *           layout, the unnormalized split partials and the combine formula.
+ *   [MLA]   kernelindex.com, gemini-2.5-pro Triton MLA paged prefill
+ *           (_mla_paged_prefill_causal_h16_ckv512_kpe64_ps1_kernel and _forward).
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,        /* an argument breaks the documented contract              */
+  PKV_EUNSUPPORTED = 2,  /* a well-formed combination with no compiled kernel       */
+  PKV_EHIP = 3           /* the HIP runtime reported an error for the launch        */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+typedef enum {
+  /* K and V: [num_blocks, num_kv_heads, block_size, head_dim]            ([FD] kernel arguments) */
+  PKV_KV_TOKEN_MAJOR = 0,
+  /* K: [num_blocks, num_kv_heads, head_dim / x, block_size, x], x = 16 / sizeof(elem);
+     V: [num_blocks, num_kv_heads, head_dim, block_size]                 ([PAv2] kernel arguments) */
+  PKV_KV_XPACKED = 1
+} pkv_kv_layout;
+
+/*
+ * paged_decode_partial -- phase 1 of split-K decode ([PAv2] _partition_attn_kernel,
+ * [FD] _flash_decode_partial_kernel).
+ *
+ * For sequence b (length len_b = seq_lens[b]), query head h and partition p covering
+ * tokens [p*ps, min((p+1)*ps, len_b)), with s_t = scale * <query[b,h,:], K_t> and kv
+ * head h / G (G = num_heads / num_kv_heads):
+ *   partial_m[b,h,p]     = max_t s_t                       (natural-log units)
+ *   partial_l[b,h,p]     = sum_t exp(s_t - m)
+ *   partial_acc[b,h,p,:] = sum_t exp(s_t - m) * V_t        (NOT divided by l)
+ * Token t of sequence b is slot t % block_size of physical block
+ * block_tables[b, t / block_size]. Each K/V page is read once for all G query heads.
+ * A partition with p*ps >= len_b gets partial_m = -inf and partial_l = 0; its
+ * partial_acc row is not written. Partitions p >= ceil(max_seq_len / ps) are not
+ * touched at all.
+ *
+ *   query         [num_seqs, num_heads, head_dim], element type `dtype`
+ *   key_cache,
+ *   value_cache   page pools in `layout`, element type `dtype`, num_blocks blocks
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32; entries past
+ *                 ceil(len_b / block_size) are never read (may be -1)
+ *   seq_lens      [num_seqs] int32, 0 <= len_b <= max_seq_len
+ *   partial_acc   [num_seqs, num_heads, max_num_partitions, head_dim] float32
+ *   partial_m,
+ *   partial_l     [num_seqs, num_heads, max_num_partitions] float32
+ * PKV_EINVAL: a NULL pointer (NULL is allowed only when num_seqs == 0), a negative
+ *   size, num_heads % num_kv_heads != 0, partition_size not a positive multiple of
+ *   block_size, max_num_partitions < ceil(max_seq_len / partition_size),
+ *   max_seq_len > max_blocks_per_seq * block_size.
+ * PKV_EUNSUPPORTED: block_size != 16; head_dim not in {64, 128, 256} (f32: {64, 128});
+ *   G > 16, or G > 8 for f32.
+ * num_seqs == 0 or max_seq_len == 0 launches nothing except the sentinel writes that
+ *   the length rule above asks for.
+ */
+int paged_decode_partial(const void* query, int dtype,
+                         const void* key_cache, const void* value_cache, int layout,
+                         const int32_t* block_tables, int max_blocks_per_seq,
+                         const int32_t* seq_lens,
+                         int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                         int block_size, int num_blocks,
+                         float scale, int partition_size, int max_num_partitions,
+                         int max_seq_len,
+                         float* partial_acc, float* partial_m, float* partial_l,
+                         void* stream);
+
+/*
+ * paged_decode_reduce -- phase 2 of split-K decode ([FD] _flash_decode_combine_kernel;
+ * partition count per sequence as in [PAv2] _reduce_partitions_kernel).
+ *
+ * For each (b, h) over the P_b = ceil(len_b / partition_size) partitions of sequence b
+ * (capped at max_num_partitions; partitions past P_b are never read):
+ *   M = max_p m_p,  w_p = exp(m_p - M)
+ *   out[b,h,:] = sum_p w_p * acc_p / sum_p w_p * l_p     rounded to out_dtype (RNE)
+ *   lse[b,h]   = M + ln(sum_p w_p * l_p)                 natural log (if lse != NULL)
+ * len_b == 0 gives out = 0 and lse = -inf.
+ *
+ *   partial_*  as written by paged_decode_partial
+ *   out        [num_seqs, num_heads, head_dim], element type `out_dtype`
+ *   lse        [num_seqs, num_heads] float32, or NULL
+ * PKV_EINVAL: NULL pointers (other than lse), negative sizes, partition_size <= 0,
+ *   max_num_partitions <= 0 with num_seqs > 0.
+ * PKV_EUNSUPPORTED: head_dim not in {64, 128, 256}.
+ */
+int paged_decode_reduce(const float* partial_acc, const float* partial_m,
+                        const float* partial_l, const int32_t* seq_lens,
+                        int num_seqs, int num_heads, int head_dim,
+                        int partition_size, int max_num_partitions,
+                        void* out, int out_dtype, float* lse, void* stream);
+
+/*
+ * mla_paged_prefill -- MLA causal paged prefill, page_size 1 ([MLA]).
+ *
+ * Batch b owns query rows r in [qo_indptr[b], qo_indptr[b+1]) and key tokens
+ * kv_indices[kv_indptr[b] + j], j in [0, kv_len), kv_len = kv_indptr[b+1]-kv_indptr[b].
+ * Row r = qo_indptr[b] + i sees keys j <= kv_len - q_len + i (bottom-right causal).
+ *   x_j  = sm_scale * (q_nope[r,h,:] . ckv[tok_j,0,:] + q_pe[r,h,:] . kpe[tok_j,0,:])
+ *   out[r,h,:] = sum_j softmax(x)_j * ckv[tok_j,0,:]         bfloat16 (RNE)
+ *   lse[r,h]   = log2(sum_j exp(x_j))                         float32, base 2
+ * A row that sees no key (kv_len == 0) gets out = 0 and lse = -inf.
+ *
+ *   q_nope     [total_q, num_heads, ckv_dim] bf16       q_pe  [total_q, num_heads, kpe_dim] bf16
+ *   ckv_cache  [num_pages, page_size, ckv_dim] bf16     kpe_cache [num_pages, page_size, kpe_dim] bf16
+ *   qo_indptr, kv_indptr  [batch + 1] int32, non-decreasing, qo_indptr[0] = kv_indptr[0] = 0,
+ *              qo_indptr[batch] = total_q, kv_len >= q_len per batch, q_len <= max_q_len
+ *   kv_indices [kv_indptr[batch]] int32 in [0, num_pages)
+ *   out        [total_q, num_heads, ckv_dim] bf16        lse [total_q, num_heads] float32
+ * PKV_EINVAL: NULL pointers with total_q > 0, negative sizes, sm_scale not finite.
+ * PKV_EUNSUPPORTED: anything but num_heads = 16, ckv_dim = 512, kpe_dim = 64, page_size = 1
+ *   (the shapes [MLA]'s _forward asserts).
+ */
+int mla_paged_prefill(const void* q_nope, const void* q_pe,
+                      const void* ckv_cache, const void* kpe_cache,
+                      const int32_t* qo_indptr, const int32_t* kv_indptr,
+                      const int32_t* kv_indices,
+                      int batch, int total_q, int max_q_len, int num_pages,
+                      int num_heads, int ckv_dim, int kpe_dim, int page_size,
+                      float sm_scale, void* out, float* lse, void* stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). Never NULL. */
+const char* pkv_last_error(void);
+
+/* Library version string, e.g. "pkv 0.1.0 gfx950". */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -48,42 +48,54 @@ def _as_int(x) -> np.ndarray:
     return np.asarray(x, dtype=np.int64)
 
 
+def _index(pool, idx):
+    """pool[idx] upcast to float64; the pool may be a torch tensor (any dtype) or numpy."""
+    try:
+        import torch
+        if isinstance(pool, torch.Tensor):
+            tidx = tuple(torch.as_tensor(i) if isinstance(i, np.ndarray) else i for i in idx)
+            return pool[tidx].detach().to("cpu").to(torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(pool[idx], dtype=np.float64)
+
+
 def gather_sequence(key_cache, value_cache, layout: str, block_table_row, n: int,
                     block_size: int):
-    """Contiguous K and V, each [num_kv_heads, n, head_dim], of one sequence.
+    """Contiguous K and V, each [num_kv_heads, n, head_dim] float64, of one sequence.
 
     Token t sits in physical block ``block_table_row[t // block_size]`` at slot
-    ``t % block_size`` (PagedAttention V2 page, ``_partition_attn_kernel``, paged
-    K/V gather; flash-decode post, per-block loop of the unsplit kernel).
+    ``t % block_size`` (PagedAttention V2 page, ``_partition_attn_kernel``, paged K/V
+    gather; flash-decode post, per-block loop of the unsplit kernel).
     Token-major pools are [num_blocks, KVH, bs, D]; x-packed K is
     [num_blocks, KVH, D / x, bs, x] with element (t, d) at [blk, h, d // x, t % bs, d % x]
     and x-packed V is [num_blocks, KVH, D, bs] with element (t, d) at [blk, h, d, t % bs].
+    Only the sequence's own slots are read (then upcast exactly to float64).
     """
-    kc = _as_f64(key_cache)
-    vc = _as_f64(value_cache)
     row = _as_int(block_table_row)
     t = np.arange(n)
     blk = row[t // block_size]
-    if n and (blk.min() < 0 or blk.max() >= kc.shape[0]):
+    nblocks = key_cache.shape[0]
+    if n and (blk.min() < 0 or blk.max() >= nblocks):
         raise ValueError("block table entry outside the pool for a valid token")
     off = t % block_size
-    kvh = kc.shape[1]
+    kvh = key_cache.shape[1]
     if layout == TOKEN_MAJOR:
-        d_model = kc.shape[3]
+        d_model = key_cache.shape[3]
         K = np.empty((kvh, n, d_model))
         V = np.empty((kvh, n, d_model))
         for h in range(kvh):
-            K[h] = kc[blk, h, off, :]
-            V[h] = vc[blk, h, off, :]
+            K[h] = _index(key_cache, (blk, h, off, slice(None)))
+            V[h] = _index(value_cache, (blk, h, off, slice(None)))
     elif layout == XPACKED:
-        x = kc.shape[4]
-        d_model = kc.shape[2] * x
+        x = key_cache.shape[4]
+        d_model = key_cache.shape[2] * x
         d = np.arange(d_model)
         K = np.empty((kvh, n, d_model))
         V = np.empty((kvh, n, d_model))
         for h in range(kvh):
-            K[h] = kc[blk[:, None], h, (d // x)[None, :], off[:, None], (d % x)[None, :]]
-            V[h] = vc[blk[:, None], h, d[None, :], off[:, None]]
+            K[h] = _index(key_cache, (blk[:, None], h, (d // x)[None, :], off[:, None], (d % x)[None, :]))
+            V[h] = _index(value_cache, (blk[:, None], h, d[None, :], off[:, None]))
     else:
         raise ValueError(f"unknown layout {layout!r}")
     return K, V

@@ -1,0 +1,255 @@
+"""Paged-KV attention for AMD Instinct MI355X (gfx950): Python binding of libpkv.so.
+
+This module only marshals arguments: it checks devices, dtypes, shapes and contiguity
+of torch tensors, then passes raw device pointers, sizes and the current HIP stream to
+the C ABI declared in ``include/pkv.h``. Every step of the computation runs in the HIP
+kernels of ``libpkv.so``; there is no fallback. If the library is missing, every entry
+point raises.
+
+Entry points (same names as the C ABI):
+  paged_decode_partial(...)   split-K partials (acc, m, l) per (seq, head, partition)
+  paged_decode_reduce(...)    LSE-weighted combine of the partials
+  mla_paged_prefill(...)      MLA causal paged prefill, page_size 1, base-2 LSE
+and the convenience wrapper paged_decode(...) that allocates the partials and runs both
+decode phases on the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["paged_decode_partial", "paged_decode_reduce", "paged_decode", "mla_paged_prefill",
+           "lib", "library_path", "PkvError", "TOKEN_MAJOR", "XPACKED", "num_partitions"]
+
+TOKEN_MAJOR = "token_major"
+XPACKED = "xpacked"
+_LAYOUT = {TOKEN_MAJOR: 0, XPACKED: 1}
+_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP = 0, 1, 2, 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libpkv.so"
+_lib = None
+
+
+class PkvError(RuntimeError):
+    """HIP runtime failure reported by the library (status PKV_EHIP)."""
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpkv.so (built in-tree by ``python -m paged_kv_gqa_table_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_gqa_table_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.paged_decode_partial.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                       f32, i32, i32, i32, vp, vp, vp, vp]
+    L.paged_decode_partial.restype = i32
+    L.paged_decode_reduce.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp, vp]
+    L.paged_decode_reduce.restype = i32
+    L.mla_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                    f32, vp, vp, vp]
+    L.mla_paged_prefill.restype = i32
+    L.pkv_last_error.argtypes = []
+    L.pkv_last_error.restype = ctypes.c_char_p
+    L.pkv_version.argtypes = []
+    L.pkv_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str) -> None:
+    if status == PKV_OK:
+        return
+    msg = lib().pkv_last_error().decode(errors="replace")
+    if status == PKV_EINVAL:
+        raise ValueError(f"{what}: {msg}")
+    if status == PKV_EUNSUPPORTED:
+        raise NotImplementedError(f"{what}: {msg}")
+    raise PkvError(f"{what}: {msg}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(name: str, t: torch.Tensor, dtype=None, ndim=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def num_partitions(max_seq_len: int, partition_size: int) -> int:
+    return max(1, -(-int(max_seq_len) // int(partition_size)))
+
+
+def _pool_geometry(key_cache: torch.Tensor, layout: str) -> Tuple[int, int, int]:
+    """(num_blocks, block_size, head_dim) of a K pool."""
+    if layout == TOKEN_MAJOR:
+        if key_cache.dim() != 4:
+            raise ValueError("token-major key_cache must be [num_blocks, kv_heads, block_size, head_dim]")
+        return key_cache.shape[0], key_cache.shape[2], key_cache.shape[3]
+    if layout == XPACKED:
+        if key_cache.dim() != 5:
+            raise ValueError("x-packed key_cache must be [num_blocks, kv_heads, head_dim/x, block_size, x]")
+        return key_cache.shape[0], key_cache.shape[3], key_cache.shape[2] * key_cache.shape[4]
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def paged_decode_partial(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                         block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                         num_kv_heads: int, partition_size: int, max_seq_len: int,
+                         partial_acc: torch.Tensor, partial_m: torch.Tensor, partial_l: torch.Tensor,
+                         layout: str = TOKEN_MAJOR) -> None:
+    """Phase 1 of split-K decode into caller-allocated partials (asynchronous)."""
+    if query.dtype not in _DTYPE:
+        raise ValueError(f"query dtype {query.dtype} not supported")
+    _dev("query", query, ndim=3)
+    _dev("key_cache", key_cache, query.dtype)
+    _dev("value_cache", value_cache, query.dtype)
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("seq_lens", seq_lens, torch.int32, 1)
+    _dev("partial_acc", partial_acc, torch.float32, 4)
+    _dev("partial_m", partial_m, torch.float32, 3)
+    _dev("partial_l", partial_l, torch.float32, 3)
+    S, H, D = query.shape
+    nb, bs, kd = _pool_geometry(key_cache, layout)
+    if kd != D:
+        raise ValueError(f"key_cache head_dim {kd} != query head_dim {D}")
+    if key_cache.shape[1] != num_kv_heads or value_cache.shape[1] != num_kv_heads:
+        raise ValueError("kv cache head axis does not match num_kv_heads")
+    if layout == XPACKED:
+        if key_cache.shape[4] != 16 // key_cache.element_size():
+            raise ValueError("x-packed key_cache needs x = 16 / element size in its last axis")
+        v_shape = (nb, num_kv_heads, D, bs)
+    else:
+        v_shape = (nb, num_kv_heads, bs, D)
+    if tuple(value_cache.shape) != v_shape:
+        raise ValueError(f"value_cache must be {v_shape}, got {tuple(value_cache.shape)}")
+    P = partial_m.shape[2]
+    if tuple(partial_acc.shape) != (S, H, P, D) or tuple(partial_m.shape) != (S, H, P) \
+            or tuple(partial_l.shape) != (S, H, P):
+        raise ValueError("partials must be [S, H, P, D] and [S, H, P]")
+    if seq_lens.shape[0] != S or block_tables.shape[0] != S:
+        raise ValueError("seq_lens / block_tables do not match the batch")
+    st = lib().paged_decode_partial(
+        _ptr(query), _DTYPE[query.dtype], _ptr(key_cache), _ptr(value_cache), _LAYOUT[layout],
+        _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, H, num_kv_heads, D, bs, nb,
+        float(scale), int(partition_size), P, int(max_seq_len), _ptr(partial_acc), _ptr(partial_m),
+        _ptr(partial_l), _stream(query.device))
+    _check(st, "paged_decode_partial")
+
+
+def paged_decode_reduce(partial_acc: torch.Tensor, partial_m: torch.Tensor, partial_l: torch.Tensor,
+                        seq_lens: torch.Tensor, partition_size: int, out: torch.Tensor,
+                        lse: Optional[torch.Tensor] = None) -> None:
+    """Phase 2 of split-K decode into caller-allocated out (and lse) (asynchronous)."""
+    _dev("partial_acc", partial_acc, torch.float32, 4)
+    _dev("partial_m", partial_m, torch.float32, 3)
+    _dev("partial_l", partial_l, torch.float32, 3)
+    _dev("seq_lens", seq_lens, torch.int32, 1)
+    if out.dtype not in _DTYPE:
+        raise ValueError(f"out dtype {out.dtype} not supported")
+    _dev("out", out, ndim=3)
+    S, H, P, D = partial_acc.shape
+    if tuple(out.shape) != (S, H, D):
+        raise ValueError("out must be [S, H, D]")
+    if lse is not None:
+        _dev("lse", lse, torch.float32, 2)
+        if tuple(lse.shape) != (S, H):
+            raise ValueError("lse must be [S, H]")
+    st = lib().paged_decode_reduce(_ptr(partial_acc), _ptr(partial_m), _ptr(partial_l), _ptr(seq_lens),
+                                   S, H, D, int(partition_size), P, _ptr(out), _DTYPE[out.dtype],
+                                   _ptr(lse), _stream(out.device))
+    _check(st, "paged_decode_reduce")
+
+
+def paged_decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                 block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float, num_kv_heads: int,
+                 partition_size: int = 512, layout: str = TOKEN_MAJOR,
+                 max_seq_len: Optional[int] = None, return_lse: bool = False,
+                 max_num_partitions: Optional[int] = None):
+    """Split-K decode: allocates the partials, runs both phases on the current stream.
+
+    ``max_seq_len`` defaults to ``seq_lens.max()`` (one device-to-host read).
+    Returns ``out`` [S, H, D] in the query dtype, or ``(out, lse)``.
+    """
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0
+    S, H, D = query.shape
+    P = max_num_partitions or num_partitions(max_seq_len, partition_size)
+    dev = query.device
+    acc = torch.empty((S, H, P, D), dtype=torch.float32, device=dev)
+    m = torch.empty((S, H, P), dtype=torch.float32, device=dev)
+    l = torch.empty((S, H, P), dtype=torch.float32, device=dev)
+    out = torch.empty((S, H, D), dtype=query.dtype, device=dev)
+    lse = torch.empty((S, H), dtype=torch.float32, device=dev) if return_lse else None
+    paged_decode_partial(query, key_cache, value_cache, block_tables, seq_lens, scale, num_kv_heads,
+                         partition_size, max_seq_len, acc, m, l, layout=layout)
+    paged_decode_reduce(acc, m, l, seq_lens, partition_size, out, lse)
+    return (out, lse) if return_lse else out
+
+
+def mla_paged_prefill(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.Tensor,
+                      kpe_cache: torch.Tensor, qo_indptr: torch.Tensor, kv_indptr: torch.Tensor,
+                      kv_indices: torch.Tensor, sm_scale: float, max_q_len: Optional[int] = None,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """MLA causal paged prefill. Returns (out [total_q, H, ckv] bf16, lse [total_q, H] base 2).
+
+    Same argument order as the page's ``_forward``. ``max_q_len`` defaults to the largest
+    q_len in ``qo_indptr`` (one device-to-host read, as the page's host-side batch map).
+    """
+    _dev("q_nope", q_nope, torch.bfloat16, 3)
+    _dev("q_pe", q_pe, torch.bfloat16, 3)
+    _dev("ckv_cache", ckv_cache, torch.bfloat16, 3)
+    _dev("kpe_cache", kpe_cache, torch.bfloat16, 3)
+    _dev("qo_indptr", qo_indptr, torch.int32, 1)
+    _dev("kv_indptr", kv_indptr, torch.int32, 1)
+    _dev("kv_indices", kv_indices, torch.int32, 1)
+    total_q, H, Dc = q_nope.shape
+    Dp = q_pe.shape[2]
+    num_pages, page_size, _ = ckv_cache.shape
+    if q_pe.shape[:2] != q_nope.shape[:2] or kpe_cache.shape[:2] != ckv_cache.shape[:2] \
+            or ckv_cache.shape[2] != Dc or kpe_cache.shape[2] != Dp:
+        raise ValueError("inconsistent MLA shapes")
+    batch = qo_indptr.shape[0] - 1
+    if kv_indptr.shape[0] != batch + 1 or batch < 0:
+        raise ValueError("qo_indptr and kv_indptr must both be [batch + 1]")
+    if max_q_len is None:
+        max_q_len = int((qo_indptr[1:] - qo_indptr[:-1]).max().item()) if batch > 0 else 0
+    if out is None:
+        out = torch.empty((total_q, H, Dc), dtype=torch.bfloat16, device=q_nope.device)
+    if lse is None:
+        lse = torch.empty((total_q, H), dtype=torch.float32, device=q_nope.device)
+    _dev("out", out, torch.bfloat16, 3)
+    _dev("lse", lse, torch.float32, 2)
+    st = lib().mla_paged_prefill(_ptr(q_nope), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache),
+                                 _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices), batch, total_q,
+                                 int(max_q_len), num_pages, H, Dc, Dp, page_size, float(sm_scale),
+                                 _ptr(out), _ptr(lse), _stream(q_nope.device))
+    _check(st, "mla_paged_prefill")
+    return out, lse

@@ -1,0 +1,100 @@
+// Split-K paged decode, phase 2: log-sum-exp weighted combine of the partials.
+//
+// Computes what the flash-decode post's _flash_decode_combine_kernel computes
+// (M = max m_p, w_p = exp(m_p - M), out = sum w_p acc_p / sum w_p l_p, zeros for an
+// empty sequence), over ceil(len / ps) partitions per sequence as in the PagedAttention
+// V2 Triton page's _reduce_partitions_kernel. The optional natural-log LSE
+// M + ln(sum w_p l_p) is written as well.
+//
+// One wave per (sequence, head); each lane owns D / 64 contiguous output dims, so every
+// partition row of acc is one coalesced 256 B - 1 KiB read. Partitions past P_b are
+// never read (their acc rows are not even written by phase 1).
+#include "common.h"
+#include "decode_args.h"
+
+namespace pkv {
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeReduceArgs a) {
+  constexpr int DPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // b * H + h
+  if (row >= a.S * a.H) return;
+  const int b = row / a.H;
+  int len = a.lens[b];
+  len = len < 0 ? 0 : len;
+  int np = (len + a.ps - 1) / a.ps;
+  np = np > a.P ? a.P : np;
+
+  float o[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) o[i] = 0.f;
+  float M = kNegInf, Z = 0.f;
+
+  if (np > 0) {
+    const float* mrow = a.m + (size_t)row * a.P;
+    const float* lrow = a.l + (size_t)row * a.P;
+    const float* arow = a.acc + (size_t)row * a.P * D + lane * DPL;
+    for (int i = lane; i < np; i += 64) M = fmaxf(M, mrow[i]);
+    M = uniform(strided_max<1>(M));
+    for (int i = lane; i < np; i += 64) Z += __expf(mrow[i] - M) * lrow[i];
+    Z = strided_sum<1>(Z);
+#pragma unroll 4
+    for (int p = 0; p < np; ++p) {
+      const float wgt = __expf(mrow[p] - M);
+      const float* src = arow + (size_t)p * D;
+      if constexpr (DPL == 4) {
+        const float4 v = *reinterpret_cast<const float4*>(src);
+        o[0] = fmaf(wgt, v.x, o[0]); o[1] = fmaf(wgt, v.y, o[1]);
+        o[2] = fmaf(wgt, v.z, o[2]); o[3] = fmaf(wgt, v.w, o[3]);
+      } else if constexpr (DPL == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(src);
+        o[0] = fmaf(wgt, v.x, o[0]); o[1] = fmaf(wgt, v.y, o[1]);
+      } else {
+        o[0] = fmaf(wgt, src[0], o[0]);
+      }
+    }
+    const float inv = 1.f / Z;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) o[i] *= inv;
+  }
+
+  const size_t ob = (size_t)row * D + lane * DPL;
+  if constexpr (OUT_BF16) {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ob;
+    if constexpr (DPL == 4) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+    } else if constexpr (DPL == 2) {
+      *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(o[0], o[1]);
+    } else {
+      dst[0] = (uint16_t)f32_to_bf16_bits(o[0]);
+    }
+  } else {
+    float* dst = reinterpret_cast<float*>(a.out) + ob;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) dst[i] = o[i];
+  }
+  if (a.lse != nullptr && lane == 0) a.lse[row] = (np > 0) ? M + __logf(Z) : kNegInf;
+}
+
+template <int D>
+static hipError_t launch_reduce_d(const DecodeReduceArgs& a, bool out_bf16, hipStream_t s) {
+  const int rows = a.S * a.H;
+  dim3 grid((rows + 3) / 4);
+  if (out_bf16)
+    hipLaunchKernelGGL((decode_reduce_kernel<D, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_reduce_kernel<D, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_reduce(const DecodeReduceArgs& a, bool out_bf16, hipStream_t s) {
+  switch (a.D) {
+    case 64: return launch_reduce_d<64>(a, out_bf16, s);
+    case 128: return launch_reduce_d<128>(a, out_bf16, s);
+    case 256: return launch_reduce_d<256>(a, out_bf16, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pkv

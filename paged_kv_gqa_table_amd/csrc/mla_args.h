@@ -1,0 +1,25 @@
+// Launch arguments of the MLA causal paged-prefill kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct MlaArgs {
+  const void* q_nope;        // [total_q, 16, 512] bf16
+  const void* q_pe;          // [total_q, 16, 64] bf16
+  const void* ckv;           // [num_pages, 1, 512] bf16
+  const void* kpe;           // [num_pages, 1, 64] bf16
+  const int32_t* qo_indptr;  // [batch + 1]
+  const int32_t* kv_indptr;  // [batch + 1]
+  const int32_t* kv_indices; // [kv_indptr[batch]]
+  int batch, total_q, max_q_len, num_pages;
+  float sm_scale_log2;       // sm_scale * log2(e)
+  void* out;                 // [total_q, 16, 512] bf16
+  float* lse;                // [total_q, 16] base 2
+};
+
+hipError_t launch_mla_prefill(const MlaArgs& a, hipStream_t s);
+
+}  // namespace pkv

@@ -1,0 +1,133 @@
+"""C-ABI boundary on the host: the library loads, exports what include/pkv.h declares,
+and rejects bad arguments with the documented status before any HIP call.
+
+No compute is launched here: every call either fails validation or is a documented
+no-op (empty batch), so these tests run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_gqa_table_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+OK, EINVAL, EUNSUP = 0, 1, 2
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails (or no-ops) first
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pkv.library_path()):
+        pytest.skip("libpkv.so not built")
+    return pkv.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert {"paged_decode_partial", "paged_decode_reduce", "mla_paged_prefill", "pkv_last_error",
+            "pkv_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"libpkv.so does not export {n}"
+
+
+def test_version(L):
+    assert L.pkv_version().decode().startswith("pkv ")
+
+
+def _partial(L, **kw):
+    a = dict(query=FAKE, dtype=1, kc=FAKE, vc=FAKE, layout=0, bt=FAKE, mb=8, lens=FAKE, S=2, H=8, KVH=2,
+             D=128, bs=16, nb=64, scale=0.1, ps=512, P=1, max_seq_len=128, acc=FAKE, m=FAKE, l=FAKE,
+             stream=None)
+    a.update(kw)
+    return L.paged_decode_partial(a["query"], a["dtype"], a["kc"], a["vc"], a["layout"], a["bt"], a["mb"],
+                                  a["lens"], a["S"], a["H"], a["KVH"], a["D"], a["bs"], a["nb"], a["scale"],
+                                  a["ps"], a["P"], a["max_seq_len"], a["acc"], a["m"], a["l"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=6, KVH=4), EINVAL),                      # H not a multiple of KVH
+    (dict(ps=500), EINVAL),                           # partition not a multiple of block_size
+    (dict(ps=0), EINVAL),
+    (dict(P=1, max_seq_len=1024), EINVAL),            # too few partitions for max_seq_len
+    (dict(mb=4, max_seq_len=65), EINVAL),             # max_seq_len beyond the table width
+    (dict(query=None), EINVAL),
+    (dict(acc=None), EINVAL),
+    (dict(dtype=7), EINVAL),
+    (dict(layout=3), EINVAL),
+    (dict(S=-1), EINVAL),
+    (dict(max_seq_len=-1), EINVAL),
+    (dict(scale=float("nan")), EINVAL),
+    (dict(bs=8, ps=512, mb=32), EUNSUP),
+    (dict(D=96), EUNSUP),
+    (dict(dtype=0, D=256), EUNSUP),
+    (dict(H=34, KVH=2), EUNSUP),                      # G = 17
+    (dict(dtype=0, H=18, KVH=2), EUNSUP),             # f32 G = 9
+    (dict(S=0, query=None), OK),                      # empty batch: nothing to do
+    (dict(max_seq_len=0), OK),                        # every sequence empty: nothing touched
+])
+def test_decode_partial_validation(L, kw, code):
+    assert _partial(L, **kw) == code
+    if code != OK:
+        assert len(L.pkv_last_error()) > 0
+
+
+def _reduce(L, **kw):
+    a = dict(acc=FAKE, m=FAKE, l=FAKE, lens=FAKE, S=2, H=8, D=128, ps=512, P=4, out=FAKE, dt=1, lse=None,
+             stream=None)
+    a.update(kw)
+    return L.paged_decode_reduce(a["acc"], a["m"], a["l"], a["lens"], a["S"], a["H"], a["D"], a["ps"], a["P"],
+                                 a["out"], a["dt"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=None), EINVAL),
+    (dict(ps=0), EINVAL),
+    (dict(P=0), EINVAL),
+    (dict(dt=5), EINVAL),
+    (dict(D=0), EINVAL),
+    (dict(D=96), EUNSUP),
+    (dict(S=0, acc=None), OK),
+])
+def test_decode_reduce_validation(L, kw, code):
+    assert _reduce(L, **kw) == code
+
+
+def _mla(L, **kw):
+    a = dict(qn=FAKE, qp=FAKE, ckv=FAKE, kpe=FAKE, qo=FAKE, kvp=FAKE, idx=FAKE, batch=2, total_q=10,
+             max_q_len=6, num_pages=40, H=16, Dc=512, Dp=64, ps=1, sm=0.07, out=FAKE, lse=FAKE, stream=None)
+    a.update(kw)
+    return L.mla_paged_prefill(a["qn"], a["qp"], a["ckv"], a["kpe"], a["qo"], a["kvp"], a["idx"], a["batch"],
+                               a["total_q"], a["max_q_len"], a["num_pages"], a["H"], a["Dc"], a["Dp"], a["ps"],
+                               a["sm"], a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=8), EUNSUP),
+    (dict(Dc=256), EUNSUP),
+    (dict(Dp=32), EUNSUP),
+    (dict(ps=16), EUNSUP),
+    (dict(out=None), EINVAL),
+    (dict(max_q_len=0), EINVAL),
+    (dict(batch=-1), EINVAL),
+    (dict(sm=float("inf")), EINVAL),
+    (dict(total_q=0, qn=None), OK),
+])
+def test_mla_validation(L, kw, code):
+    assert _mla(L, **kw) == code
+
+
+def test_python_layer_maps_statuses(L):
+    import torch
+    with pytest.raises((ValueError, TypeError)):
+        pkv.paged_decode_partial(torch.zeros(2, 8, 128), None, None, None, None, 0.1, 2, 512, 128,
+                                 None, None, None)

@@ -21,9 +21,11 @@ ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file
 MUTATIONS = [
     ("decode.py", "return h // group", "return h % group", 0, "kv head index h % G"),
     ("decode.py", "off = t % block_size", "off = (t + 1) % block_size", 0, "slot off by one"),
-    ("decode.py", "K[h] = kc[blk, h, off, :]", "K[h] = kc[blk, 0, off, :]", 0, "token-major K always head 0"),
-    ("decode.py", "V[h] = vc[blk[:, None], h, d[None, :], off[:, None]]",
-     "V[h] = vc[blk[:, None], h, (d_model - 1 - d)[None, :], off[:, None]]", 0, "x-packed V dim reversed"),
+    ("decode.py", "K[h] = _index(key_cache, (blk, h, off, slice(None)))",
+     "K[h] = _index(key_cache, (blk, 0, off, slice(None)))", 0, "token-major K always head 0"),
+    ("decode.py", "V[h] = _index(value_cache, (blk[:, None], h, d[None, :], off[:, None]))",
+     "V[h] = _index(value_cache, (blk[:, None], h, (d_model - 1 - d)[None, :], off[:, None]))", 0,
+     "x-packed V dim reversed"),
     ("decode.py", "(d // x)[None, :], off[:, None], (d % x)[None, :]",
      "(d % x * 0 + d // x)[None, :], off[:, None], (x - 1 - d % x)[None, :]", 0, "x-packed K lane reversed"),
     ("decode.py", "return scale * (K @ q_vec)", "return (K @ q_vec)", 0, "scale dropped"),
