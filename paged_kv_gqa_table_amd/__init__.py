@@ -42,7 +42,8 @@ class PkvError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, _LIB_NAME)
+    """In-tree libpkv.so, or the file named by PKV_LIBRARY (for comparing builds)."""
+    return os.environ.get("PKV_LIBRARY") or os.path.join(_HERE, _LIB_NAME)
 
 
 def lib() -> ctypes.CDLL:

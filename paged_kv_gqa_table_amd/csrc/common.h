@@ -24,8 +24,12 @@ PKV_DEVICE uint32_t f32_to_bf16_bits(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
 }
+// Two floats to a bf16 pair with v_cvt_pk_bf16_f32 (round to nearest even).
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
 PKV_DEVICE uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const f32x2v_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
 }
 
 // v_dot2c_f32_bf16: acc + a.lo*b.lo + a.hi*b.hi with bf16 pairs, f32 accumulate.
@@ -113,6 +117,22 @@ PKV_DEVICE float strided_max(float v) {
   if constexpr (STRIDE <= 16) v = fmaxf(v, xor_lanes(v, 16));
   if constexpr (STRIDE <= 32) v = fmaxf(v, xor_lanes(v, 32));
   return v;
+}
+
+// Wave-wide max made uniform. `v` must already agree inside each group of STRIDE
+// consecutive lanes (STRIDE in {1,...,16}, power of two); the remaining lane bits are
+// folded with DPP (row_ror:8 inside a row, then row_bcast:15 / row_bcast:31 across rows,
+// which leaves the full max in lane 63) and broadcast with readlane.
+template <int STRIDE>
+PKV_DEVICE float wave_max_uniform(float v) {
+  if constexpr (STRIDE <= 1) v = fmaxf(v, dpp<kDppQuadXor1>(v));
+  if constexpr (STRIDE <= 2) v = fmaxf(v, dpp<kDppQuadXor2>(v));
+  if constexpr (STRIDE <= 4) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  if constexpr (STRIDE <= 8) v = fmaxf(v, dpp<kDppRor8>(v));
+  // rows 1 and 3 take lane 15 of the row below; then rows 2 and 3 take lane 31
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x142, 0xA, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x143, 0xC, 0xF, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 PKV_DEVICE float uniform(float v) {

@@ -9,6 +9,8 @@
 // One wave per (sequence, head); each lane owns D / 64 contiguous output dims, so every
 // partition row of acc is one coalesced 256 B - 1 KiB read. Partitions past P_b are
 // never read (their acc rows are not even written by phase 1).
+#include <type_traits>
+
 #include "common.h"
 #include "decode_args.h"
 
@@ -16,15 +18,16 @@ namespace pkv {
 
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeReduceArgs a) {
-  constexpr int DPL = D / 64;
+  constexpr int DPL = D / 64;  // output dims per lane
+  constexpr int CH = 8;        // partition rows of acc in flight per lane
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // b * H + h
+  const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);  // b * H + h
   if (row >= a.S * a.H) return;
   const int b = row / a.H;
   int len = a.lens[b];
   len = len < 0 ? 0 : len;
   int np = (len + a.ps - 1) / a.ps;
-  np = np > a.P ? a.P : np;
+  np = uniform(np > a.P ? a.P : np);
 
   float o[DPL];
 #pragma unroll
@@ -35,23 +38,38 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeReduceArgs a) 
     const float* mrow = a.m + (size_t)row * a.P;
     const float* lrow = a.l + (size_t)row * a.P;
     const float* arow = a.acc + (size_t)row * a.P * D + lane * DPL;
-    for (int i = lane; i < np; i += 64) M = fmaxf(M, mrow[i]);
-    M = uniform(strided_max<1>(M));
-    for (int i = lane; i < np; i += 64) Z += __expf(mrow[i] - M) * lrow[i];
-    Z = strided_sum<1>(Z);
-#pragma unroll 4
-    for (int p = 0; p < np; ++p) {
-      const float wgt = __expf(mrow[p] - M);
-      const float* src = arow + (size_t)p * D;
-      if constexpr (DPL == 4) {
-        const float4 v = *reinterpret_cast<const float4*>(src);
-        o[0] = fmaf(wgt, v.x, o[0]); o[1] = fmaf(wgt, v.y, o[1]);
-        o[2] = fmaf(wgt, v.z, o[2]); o[3] = fmaf(wgt, v.w, o[3]);
-      } else if constexpr (DPL == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(src);
-        o[0] = fmaf(wgt, v.x, o[0]); o[1] = fmaf(wgt, v.y, o[1]);
-      } else {
-        o[0] = fmaf(wgt, src[0], o[0]);
+    using VecT = typename std::conditional<DPL == 4, float4, typename std::conditional<DPL == 2, float2, float>::type>::type;
+    // m, l of the first 64 partitions (one per lane) and the first CH acc rows all go out
+    // before anything waits on them: one memory round trip for the common case.
+    const float m0 = lane < np ? mrow[lane] : kNegInf;  // partition `lane`
+    const float l0 = lane < np ? lrow[lane] : 0.f;
+    VecT buf[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u)
+      if (u < np) buf[u] = *reinterpret_cast<const VecT*>(arow + (size_t)u * D);
+    float mv = m0;
+    for (int i = lane + 64; i < np; i += 64) mv = fmaxf(mv, mrow[i]);  // more than 64 partitions
+    M = uniform(strided_max<1>(mv));
+    const float wl = __expf(m0 - M);  // weight of partition `lane` (0 past np)
+    float zl = wl * l0;
+    for (int i = lane + 64; i < np; i += 64) zl += __expf(mrow[i] - M) * lrow[i];
+    Z = strided_sum<1>(zl);
+    for (int c0 = 0; c0 < np; c0 += CH) {
+      if (c0 > 0) {
+#pragma unroll
+        for (int u = 0; u < CH; ++u)
+          if (c0 + u < np) buf[u] = *reinterpret_cast<const VecT*>(arow + (size_t)(c0 + u) * D);
+      }
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const int pidx = c0 + u;
+        if (pidx < np) {
+          const float wgt = pidx < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), pidx))
+                                      : __expf(mrow[pidx] - M);
+          const float* f = reinterpret_cast<const float*>(&buf[u]);
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) o[i] = fmaf(wgt, f[i], o[i]);
+        }
       }
     }
     const float inv = 1.f / Z;

@@ -7,124 +7,127 @@
 // exp(score - m) and acc = sum of exp(score - m) * V over the partition's tokens.
 //
 // gfx950 design (not the pages'):
-//  * One workgroup per (partition, kv head, sequence), W waves. Each page of 16 tokens
-//    is read from HBM exactly once and used for all G heads. Waves take the partition's
-//    pages round-robin and keep independent softmax states, merged once through LDS.
-//  * K is read straight into registers with 16-byte loads. A token's row is split over
-//    LPT lanes (LPT * 16 B >= 128 B, so every load instruction consumes whole 128-byte
-//    lines in both layouts). Scores are reduced across those LPT lanes with DPP.
-//  * The running max is wave-uniform per head (readfirstlane), so the rescale of l and
-//    acc is a scalar branch that is skipped whenever a page does not raise the max.
-//  * Scores live in base 2 (scale * log2 e folded once) so exp is a single v_exp_f32;
-//    the stored m is converted back to natural-log units.
-//  * bf16: q.K uses v_dot2c_f32_bf16 on raw bf16 pairs (no unpacking); P.V uses the same
-//    instruction on P rounded to bf16 (as both decode pages do before their P.V product).
-//    f32: plain FMAs, P stays f32.
-//  * Token-major V has the same lane layout as K, so P never leaves the lane. x-packed V
-//    ([D, 16] per page) is read linearly (lane i takes 16-byte chunk i, i.e. one d and
-//    8 (bf16) or 4 (f32) consecutive tokens) and P reaches it through a small per-wave
-//    LDS row.
-//  * Page ids of a partition are cached one per lane and broadcast with readlane.
-//  * Single register buffer with early re-issue: the next page's K loads go out as soon
-//    as the current scores are formed, its V loads as soon as P.V is done.
+//  * Work items are (sequence, kv head, partition) triples with real tokens, taken from a
+//    dense list (worklist.h) so no workgroup is spent on empty partitions; the empty ones
+//    get their sentinel from a grid-stride pass. Each workgroup has W waves; every page of
+//    16 tokens is read from HBM exactly once and used for all G heads. Waves take the
+//    partition's pages round-robin with independent softmax states, merged through LDS.
+//  * K goes straight into registers with 16-byte loads. A token's row is split over LPT
+//    lanes (LPT * 16 B >= 128 B, so each load instruction consumes whole 128-byte lines in
+//    both layouts); scores are summed across those lanes with DPP.
+//  * The running max is wave-uniform per head (readfirstlane), so the rescale of l and acc
+//    is a scalar branch, skipped whenever a page does not raise the max.
+//  * Scores are kept in base 2 (scale * log2 e folded once), so exp is one v_exp_f32; the
+//    stored m is converted back to natural-log units.
+//  * bf16: q.K uses v_dot2c_f32_bf16 on raw bf16 pairs; P.V uses the same instruction on P
+//    rounded to bf16 by v_cvt_pk_bf16_f32 (both decode pages also round P to the V type
+//    before their P.V product). f32: plain FMAs and f32 P.
+//  * Token-major V has K's lane layout, so P never leaves the lane. x-packed V ([D][16] per
+//    page) is read linearly (lane i takes 16-byte chunk i: one d, 8 (bf16) or 4 (f32)
+//    consecutive tokens) and P reaches it through a per-wave LDS row.
+//  * Page ids are cached one per lane (lane j: the wave's j-th page) and broadcast with
+//    v_readlane, so the page loop issues no dependent vector loads. Single register buffer
+//    with early re-issue: the next page's K loads leave as soon as the current scores are
+//    formed, its V loads as soon as P.V is done.
 #pragma once
 
 #include "common.h"
 #include "decode_args.h"
+#include "worklist.h"
 
 namespace pkv {
 
+constexpr float kRebase = 8.f;  // log2 headroom of the lazy softmax rescale
+
 template <bool BF16, int D, int G, bool XP, int LPT, int W>
-__global__ __launch_bounds__(64 * W) void decode_partial_valu_kernel(DecodePartialArgs a) {
-  constexpr int BS = 16;
-  constexpr int E = BF16 ? 8 : 4;      // elements per 16-byte chunk
-  constexpr int EB = BF16 ? 2 : 4;     // bytes per element
-  constexpr int ROWB = D * EB;         // bytes of one token's K (or V) row
-  constexpr int NC = ROWB / 16;        // chunks per token row
-  constexpr int CPL = NC / LPT;        // chunks per lane per token
-  constexpr int TPI = 64 / LPT;        // tokens covered by one load instruction
-  constexpr int TPL = BS / TPI;        // tokens per lane per page
-  constexpr int PAGEB = BS * ROWB;     // bytes of one (page, kv head) block of K (or V)
-  // x-packed V: [D][16] per page; 16-byte chunk = one d, TPC consecutive tokens.
-  constexpr int TPC = 16 / EB;         // tokens per V chunk
-  constexpr int CPD = BS / TPC;        // chunks per d
-  constexpr int NVC = D * CPD / 64;    // V chunks per lane per page (x-packed)
+struct ValuCfg {
+  static constexpr int BS = 16;
+  static constexpr int E = BF16 ? 8 : 4;      // elements per 16-byte chunk
+  static constexpr int EB = BF16 ? 2 : 4;     // bytes per element
+  static constexpr int ROWB = D * EB;         // bytes of one token's K (or V) row
+  static constexpr int NC = ROWB / 16;        // chunks per token row
+  static constexpr int CPL = NC / LPT;        // chunks per lane per token
+  static constexpr int TPI = 64 / LPT;        // tokens covered by one load instruction
+  static constexpr int TPL = BS / TPI;        // tokens per lane per page
+  static constexpr int PAGEB = BS * ROWB;     // bytes of one (page, kv head) block of K or V
+  static constexpr int TPC = 16 / EB;         // x-packed V: tokens per chunk
+  static constexpr int CPD = BS / TPC;        // x-packed V: chunks per d
+  static constexpr int NVC = D * CPD / 64;    // x-packed V: chunks per lane per page
+  static constexpr int NACC = XP ? NVC : CPL * E;
+  static constexpr int NVREG = XP ? NVC : TPL * CPL;
   static_assert(NC % LPT == 0 && CPL >= 1, "row must split evenly over LPT lanes");
   static_assert(TPL >= 1 && (!BF16 || XP || TPL % 2 == 0), "token pairs for bf16 P.V");
   static_assert(!XP || NVC >= 1, "x-packed V needs at least one chunk per lane");
+};
 
-  __shared__ float red_acc[W][G][D];
-  __shared__ float red_m[W][G];
-  __shared__ float red_l[W][G];
-  __shared__ __attribute__((aligned(16))) float p_lds[XP ? W : 1][G][BS];
+template <int W, int G, int D, bool XP>
+struct ValuSmem {
+  __attribute__((aligned(16))) uint32_t q_lds[G][D];  // query rows of the item (D*4 bytes >= a row)
+  float red_acc[W][G][D];
+  float red_m[W][G];     // exact max of the wave's scores (base 2)
+  float red_mref[W][G];  // reference max that the wave's l and acc are relative to
+  float red_l[W][G];
+  __attribute__((aligned(16))) float p_lds[XP ? W : 1][G][16];
+};
+
+// One work item: partials of (b, kvh, p) for the G heads of kv head kvh.
+template <bool BF16, int D, int G, bool XP, int LPT, int W>
+__device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const int b, const int kvh,
+                                               const int p, const int len, ValuSmem<W, G, D, XP>& sm) {
+  using C = ValuCfg<BF16, D, G, XP, LPT, W>;
+  constexpr int BS = C::BS, E = C::E, ROWB = C::ROWB, CPL = C::CPL, TPI = C::TPI, TPL = C::TPL;
+  constexpr int PAGEB = C::PAGEB, TPC = C::TPC, CPD = C::CPD, NVC = C::NVC, NACC = C::NACC;
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = uniform((int)(threadIdx.x >> 6));
   const int c = lane % LPT;   // chunk column of the token row
   const int tg = lane / LPT;  // token group (token index within a load row)
-
-  const int p = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
   const int H = a.H;
-
-  int len = a.lens[b];
-  len = len < 0 ? 0 : len;
-  len = len > a.mb * BS ? a.mb * BS : len;
-  const int tok0 = p * a.ps;
-  const size_t stat_base = ((size_t)b * H + (size_t)kvh * G) * a.P + p;  // + g * P
-
-  if (tok0 >= len) {  // empty partition: sentinel (PagedAttention V2, unused-partition branch)
-    if (threadIdx.x < G) {
-      a.m[stat_base + (size_t)threadIdx.x * a.P] = kNegInf;
-      a.l[stat_base + (size_t)threadIdx.x * a.P] = 0.f;
-    }
-    return;
-  }
 
   const int npages_seq = (len + BS - 1) / BS;
   const int pg_begin = p * a.ppp;
   const int pg_end = min(pg_begin + a.ppp, npages_seq);
+  // pages of this wave: pg_begin + w + W * i, i < n_my
+  const int n_my = pg_end - pg_begin - w > 0 ? (pg_end - pg_begin - w + W - 1) / W : 0;
   const int32_t* bt_row = a.bt + (size_t)b * a.mb;
 
-  // Page ids of this partition, one per lane (the common case ps <= 1024 tokens).
   int pid_cache = 0;
-  if (pg_begin + lane < pg_end) pid_cache = bt_row[pg_begin + lane];
-  auto page_id = [&](int pg) -> int {
-    int rel = pg - pg_begin;
-    int id = rel < 64 ? __builtin_amdgcn_readlane(pid_cache, rel) : bt_row[pg];
+  auto load_ids = [&](int i0) {  // lane j <- id of the wave's page i0 + j
+    const int i = i0 + lane;
+    int id = (i < n_my) ? bt_row[pg_begin + w + W * i] : 0;
     id = id < 0 ? 0 : id;
-    return id >= a.NB ? a.NB - 1 : id;
+    pid_cache = id >= a.NB ? a.NB - 1 : id;
   };
+  load_ids(0);
 
-  // ---- query registers: lane holds dims of chunk columns c + LPT*k
-  uint32_t qv[G][CPL][4];
+  // ---- the G query rows go to LDS once per item; lanes re-read their chunks per page
+  // (broadcast reads), which keeps them out of the register budget.
   {
     const char* qb = reinterpret_cast<const char*>(a.q) + ((size_t)b * H + (size_t)kvh * G) * ROWB;
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        uint4 v = ld16(qb + (size_t)g * ROWB + (c + LPT * k) * 16);
-        qv[g][k][0] = v.x; qv[g][k][1] = v.y; qv[g][k][2] = v.z; qv[g][k][3] = v.w;
-      }
+    for (int i = threadIdx.x; i < G * (ROWB / 16); i += 64 * W) {
+      const int g = i / (ROWB / 16), ch = i - g * (ROWB / 16);
+      *reinterpret_cast<uint4*>(&sm.q_lds[g][ch * 4]) = ld16(qb + (size_t)g * ROWB + ch * 16);
+    }
   }
+  __syncthreads();
 
-  constexpr int NACC = XP ? NVC : CPL * E;  // accumulator floats per lane per head
+  // Softmax state per head: l and acc are relative to m_ref (base 2); m_true is the exact
+  // running max. m_ref is re-based only when m_true outgrows it by kRebase, so p stays
+  // below 2^kRebase and the rescale of acc is rare; the exact max is what gets stored.
   float acc[G][NACC];
-  float m2[G], lsum[G];
+  float m_ref[G], m_true[G], lsum[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    m2[g] = kNegInf;
+    m_ref[g] = kNegInf;
+    m_true[g] = kNegInf;
     lsum[g] = 0.f;
 #pragma unroll
     for (int i = 0; i < NACC; ++i) acc[g][i] = 0.f;
   }
 
-  const size_t head_off = (size_t)kvh * PAGEB;
   const size_t block_stride = (size_t)a.KVH * PAGEB;
-  const char* kbase = reinterpret_cast<const char*>(a.kc) + head_off;
-  const char* vbase = reinterpret_cast<const char*>(a.vc) + head_off;
+  const char* kbase = reinterpret_cast<const char*>(a.kc) + (size_t)kvh * PAGEB;
+  const char* vbase = reinterpret_cast<const char*>(a.vc) + (size_t)kvh * PAGEB;
 
   // Byte offset of (token-in-page t, chunk column cc) inside a (page, head) K block.
   auto k_off = [&](int t, int cc) -> int {
@@ -132,22 +135,25 @@ __global__ __launch_bounds__(64 * W) void decode_partial_valu_kernel(DecodeParti
     else return t * ROWB + cc * 16;                // [16][D]
   };
 
-  constexpr int NVREG = XP ? NVC : TPL * CPL;
   uint4 kr[TPL][CPL];
-  uint4 vr[NVREG];
+  uint4 vr[C::NVREG];
 
-  auto issue_k = [&](int pg) {
-    const char* kp = kbase + (size_t)page_id(pg) * block_stride;
+  auto page_ptr = [&](const char* base, int i) -> const char* {
+    const int id = __builtin_amdgcn_readlane(pid_cache, i & 63);
+    return base + (size_t)id * block_stride;
+  };
+  auto issue_k = [&](int i) {
+    const char* kp = page_ptr(kbase, i);
 #pragma unroll
     for (int j = 0; j < TPL; ++j)
 #pragma unroll
       for (int k = 0; k < CPL; ++k) kr[j][k] = ld16(kp + k_off(tg + TPI * j, c + LPT * k));
   };
-  auto issue_v = [&](int pg) {
-    const char* vp = vbase + (size_t)page_id(pg) * block_stride;
+  auto issue_v = [&](int i) {
+    const char* vp = page_ptr(vbase, i);
     if constexpr (XP) {
 #pragma unroll
-      for (int i = 0; i < NVC; ++i) vr[i] = ld16(vp + (size_t)(64 * i + lane) * 16);
+      for (int q = 0; q < NVC; ++q) vr[q] = ld16(vp + (size_t)(64 * q + lane) * 16);
     } else {
 #pragma unroll
       for (int j = 0; j < TPL; ++j)
@@ -156,19 +162,25 @@ __global__ __launch_bounds__(64 * W) void decode_partial_valu_kernel(DecodeParti
     }
   };
 
-  int pg = pg_begin + w;
-  if (pg < pg_end) {
-    issue_k(pg);
-    issue_v(pg);
+  if (n_my > 0) {
+    issue_k(0);
+    issue_v(0);
   }
-  while (pg < pg_end) {
-    const int nxt = pg + W;
-    const int ntok = min(BS, len - pg * BS);  // valid tokens in this page
+#pragma unroll 2
+  for (int i = 0; i < n_my; ++i) {
+    const int pg = pg_begin + w + W * i;
+    const int ntok = min(BS, len - pg * BS);  // valid tokens in this page (uniform)
+    const bool more = i + 1 < n_my;
+    if (more && ((i + 1) & 63) == 0) load_ids(i + 1);  // next 64 pages of this wave (rare)
 
-    // ---- scores s[g][j] for this lane's tokens, summed over the LPT lanes of the row
+    // ---- scores for this lane's tokens, summed over the LPT lanes of the row
+    asm volatile("" ::: "memory");  // keep the q reads inside the loop (registers are scarce)
     float s[G][TPL];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
+      uint4 qv[CPL];
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) qv[k] = *reinterpret_cast<const uint4*>(&sm.q_lds[g][(c + LPT * k) * 4]);
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
         float d0 = 0.f, d1 = 0.f;
@@ -176,20 +188,24 @@ __global__ __launch_bounds__(64 * W) void decode_partial_valu_kernel(DecodeParti
         for (int k = 0; k < CPL; ++k) {
           const uint4 kv = kr[j][k];
           if constexpr (BF16) {
-            d0 = dot2_bf16(qv[g][k][0], kv.x, d0);
-            d1 = dot2_bf16(qv[g][k][1], kv.y, d1);
-            d0 = dot2_bf16(qv[g][k][2], kv.z, d0);
-            d1 = dot2_bf16(qv[g][k][3], kv.w, d1);
+            d0 = dot2_bf16(qv[k].x, kv.x, d0);
+            d1 = dot2_bf16(qv[k].y, kv.y, d1);
+            d0 = dot2_bf16(qv[k].z, kv.z, d0);
+            d1 = dot2_bf16(qv[k].w, kv.w, d1);
           } else {
-            d0 = fmaf(__uint_as_float(qv[g][k][0]), __uint_as_float(kv.x), d0);
-            d1 = fmaf(__uint_as_float(qv[g][k][1]), __uint_as_float(kv.y), d1);
-            d0 = fmaf(__uint_as_float(qv[g][k][2]), __uint_as_float(kv.z), d0);
-            d1 = fmaf(__uint_as_float(qv[g][k][3]), __uint_as_float(kv.w), d1);
+            d0 = fmaf(__uint_as_float(qv[k].x), __uint_as_float(kv.x), d0);
+            d1 = fmaf(__uint_as_float(qv[k].y), __uint_as_float(kv.y), d1);
+            d0 = fmaf(__uint_as_float(qv[k].z), __uint_as_float(kv.z), d0);
+            d1 = fmaf(__uint_as_float(qv[k].w), __uint_as_float(kv.w), d1);
           }
         }
         s[g][j] = d0 + d1;
       }
-    if (nxt < pg_end) issue_k(nxt);  // K registers are free again
+    }
+    // K registers are free again: the next page's loads leave now. The load is issued
+    // unconditionally (the last iteration re-reads its own page, an L2 hit) so the
+    // registers need no merge copy at the loop back edge.
+    issue_k(more ? i + 1 : i);
 
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -206,27 +222,29 @@ __global__ __launch_bounds__(64 * W) void decode_partial_valu_kernel(DecodeParti
       float pm = s[g][0];
 #pragma unroll
       for (int j = 1; j < TPL; ++j) pm = fmaxf(pm, s[g][j]);
-      pm = uniform(strided_max<LPT>(pm));
-      if (pm > m2[g]) {  // uniform branch: only when this page raises the max
-        const float alpha = fast_exp2(m2[g] - pm);
-        lsum[g] *= alpha;
+      pm = wave_max_uniform<LPT>(pm);
+      m_true[g] = fmaxf(m_true[g], pm);
+      // Re-base when the max outgrows the reference by kRebase (and on the wave's first
+      // page, where l = acc = 0). Branch-free: alpha is exactly 1 when nothing changes, and
+      // a uniform multiply costs less than the register copies a branch would force.
+      const float new_ref = (m_true[g] > m_ref[g] + kRebase) ? m_true[g] : m_ref[g];
+      const float alpha = fast_exp2(m_ref[g] - new_ref);  // -inf - x -> 0 on the first page
+      m_ref[g] = new_ref;
+      lsum[g] *= alpha;
 #pragma unroll
-        for (int i = 0; i < NACC; ++i) acc[g][i] *= alpha;
-        m2[g] = pm;
-      }
-      float ps = 0.f;
+      for (int q = 0; q < NACC; ++q) acc[g][q] *= alpha;
+      float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
-        pr[g][j] = fast_exp2(s[g][j] - m2[g]);
-        ps += pr[g][j];
+        pr[g][j] = fast_exp2(s[g][j] - m_ref[g]);
+        psum += pr[g][j];
       }
-      lsum[g] += ps;
+      lsum[g] += psum;
     }
 
-    // ---- tail page: zero V of invalid tokens (their slots may hold anything, even NaN)
-    const bool tail = ntok < BS;
-
+    const bool tail = ntok < BS;  // uniform
     if constexpr (!XP) {
+      // ---- tail page: zero V of invalid tokens (their slots may hold anything, even NaN)
       if (tail) {
 #pragma unroll
         for (int j = 0; j < TPL; ++j)
@@ -278,14 +296,14 @@ __global__ __launch_bounds__(64 * W) void decode_partial_valu_kernel(DecodeParti
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
-          for (int j = 0; j < TPL; ++j) p_lds[w][g][tg + TPI * j] = pr[g][j];
+          for (int j = 0; j < TPL; ++j) sm.p_lds[w][g][tg + TPI * j] = pr[g][j];
       }
       wave_lds_fence();
       const int u = lane % CPD;  // which TPC-token slice of the page this lane's chunks hold
       if (tail) {
 #pragma unroll
-        for (int i = 0; i < NVC; ++i) {
-          uint32_t x[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+        for (int q = 0; q < NVC; ++q) {
+          uint32_t x[4] = {vr[q].x, vr[q].y, vr[q].z, vr[q].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             if constexpr (BF16) {
@@ -296,40 +314,39 @@ __global__ __launch_bounds__(64 * W) void decode_partial_valu_kernel(DecodeParti
               x[e] = (t >= ntok) ? 0u : x[e];
             }
           }
-          vr[i] = make_uint4(x[0], x[1], x[2], x[3]);
+          vr[q] = make_uint4(x[0], x[1], x[2], x[3]);
         }
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float4 pf = *reinterpret_cast<const float4*>(&p_lds[w][g][u * TPC]);
+        const float4 pf = *reinterpret_cast<const float4*>(&sm.p_lds[w][g][u * TPC]);
         if constexpr (BF16) {
-          const float4 pf2 = *reinterpret_cast<const float4*>(&p_lds[w][g][u * TPC + 4]);
+          const float4 pf2 = *reinterpret_cast<const float4*>(&sm.p_lds[w][g][u * TPC + 4]);
           const uint32_t p01 = pack_bf16x2(pf.x, pf.y), p23 = pack_bf16x2(pf.z, pf.w);
           const uint32_t p45 = pack_bf16x2(pf2.x, pf2.y), p67 = pack_bf16x2(pf2.z, pf2.w);
 #pragma unroll
-          for (int i = 0; i < NVC; ++i) {
-            float t0 = dot2_bf16(p01, vr[i].x, acc[g][i]);
-            float t1 = dot2_bf16(p23, vr[i].y, 0.f);
-            t0 = dot2_bf16(p45, vr[i].z, t0);
-            t1 = dot2_bf16(p67, vr[i].w, t1);
-            acc[g][i] = t0 + t1;
+          for (int q = 0; q < NVC; ++q) {
+            float t0 = dot2_bf16(p01, vr[q].x, acc[g][q]);
+            float t1 = dot2_bf16(p23, vr[q].y, 0.f);
+            t0 = dot2_bf16(p45, vr[q].z, t0);
+            t1 = dot2_bf16(p67, vr[q].w, t1);
+            acc[g][q] = t0 + t1;
           }
         } else {
 #pragma unroll
-          for (int i = 0; i < NVC; ++i) {
-            float t = acc[g][i];
-            t = fmaf(pf.x, __uint_as_float(vr[i].x), t);
-            t = fmaf(pf.y, __uint_as_float(vr[i].y), t);
-            t = fmaf(pf.z, __uint_as_float(vr[i].z), t);
-            t = fmaf(pf.w, __uint_as_float(vr[i].w), t);
-            acc[g][i] = t;
+          for (int q = 0; q < NVC; ++q) {
+            float t = acc[g][q];
+            t = fmaf(pf.x, __uint_as_float(vr[q].x), t);
+            t = fmaf(pf.y, __uint_as_float(vr[q].y), t);
+            t = fmaf(pf.z, __uint_as_float(vr[q].z), t);
+            t = fmaf(pf.w, __uint_as_float(vr[q].w), t);
+            acc[g][q] = t;
           }
         }
       }
-      wave_lds_fence();  // reads of this page's P finish before the next page overwrites it
+      wave_lds_fence();  // this page's P reads finish before the next page overwrites it
     }
-    if (nxt < pg_end) issue_v(nxt);  // V registers are free again
-    pg = nxt;
+    issue_v(more ? i + 1 : i);  // V registers are free again (unconditional, as for K)
   }
 
   // ---- merge this wave's lanes, then the waves, through LDS
@@ -338,10 +355,10 @@ __global__ __launch_bounds__(64 * W) void decode_partial_valu_kernel(DecodeParti
     lsum[g] = strided_sum<LPT>(lsum[g]);  // over token groups (lanes of a group agree)
     if constexpr (XP) {
 #pragma unroll
-      for (int i = 0; i < NVC; ++i) acc[g][i] = group_sum<CPD>(acc[g][i]);
+      for (int q = 0; q < NVC; ++q) acc[g][q] = group_sum<CPD>(acc[g][q]);
     } else {
 #pragma unroll
-      for (int i = 0; i < NACC; ++i) acc[g][i] = strided_sum<LPT>(acc[g][i]);
+      for (int q = 0; q < NACC; ++q) acc[g][q] = strided_sum<LPT>(acc[g][q]);
     }
   }
   if constexpr (XP) {
@@ -349,7 +366,7 @@ __global__ __launch_bounds__(64 * W) void decode_partial_valu_kernel(DecodeParti
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int i = 0; i < NVC; ++i) red_acc[w][g][(64 * i + lane) / CPD] = acc[g][i];
+        for (int q = 0; q < NVC; ++q) sm.red_acc[w][g][(64 * q + lane) / CPD] = acc[g][q];
     }
   } else {
     if (tg == 0) {
@@ -358,30 +375,32 @@ __global__ __launch_bounds__(64 * W) void decode_partial_valu_kernel(DecodeParti
 #pragma unroll
         for (int k = 0; k < CPL; ++k)
 #pragma unroll
-          for (int e = 0; e < E; ++e) red_acc[w][g][(c + LPT * k) * E + e] = acc[g][k * E + e];
+          for (int e = 0; e < E; ++e) sm.red_acc[w][g][(c + LPT * k) * E + e] = acc[g][k * E + e];
     }
   }
   if (lane == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      red_m[w][g] = m2[g];
-      red_l[w][g] = lsum[g];
+      sm.red_m[w][g] = m_true[g];
+      sm.red_mref[w][g] = m_ref[g];
+      sm.red_l[w][g] = lsum[g];
     }
   }
   __syncthreads();
 
+  const size_t stat_base = ((size_t)b * H + (size_t)kvh * G) * a.P + p;  // + g * P
   for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) {
     const int g = idx / D;
     const int d = idx - g * D;
-    float M = red_m[0][g];
+    float M = sm.red_m[0][g];
 #pragma unroll
-    for (int v = 1; v < W; ++v) M = fmaxf(M, red_m[v][g]);
+    for (int v = 1; v < W; ++v) M = fmaxf(M, sm.red_m[v][g]);
     float o = 0.f, L = 0.f;
 #pragma unroll
     for (int v = 0; v < W; ++v) {
-      const float f = fast_exp2(red_m[v][g] - M);  // waves without pages carry -inf: f = 0
-      o = fmaf(f, red_acc[v][g][d], o);
-      L = fmaf(f, red_l[v][g], L);
+      const float f = fast_exp2(sm.red_mref[v][g] - M);  // waves without pages carry -inf: f = 0
+      o = fmaf(f, sm.red_acc[v][g][d], o);
+      L = fmaf(f, sm.red_l[v][g], L);
     }
     const size_t si = stat_base + (size_t)g * a.P;
     a.acc[si * D + d] = o;
@@ -390,16 +409,69 @@ __global__ __launch_bounds__(64 * W) void decode_partial_valu_kernel(DecodeParti
       a.l[si] = L;
     }
   }
+  __syncthreads();  // LDS is reused by the next item
 }
 
-// Instantiation helper: picks LPT / W for a (dtype, D) pair and launches.
+template <bool BF16, int D, int G, bool XP, int LPT, int W, bool DENSE, int WPE>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(WPE, 8))) void decode_partial_valu_kernel(DecodePartialArgs a, int grid_parts) {
+  __shared__ ValuSmem<W, G, D, XP> sm;
+  if constexpr (DENSE) {
+    __shared__ int s_prefix[kMaxDenseSeqs + 1];
+    __shared__ int s_wave[W];
+    const int n_items = build_worklist<64 * W>(a.lens, a.S, a.mb * 16, a.ps, a.KVH, s_prefix, s_wave);
+    write_sentinels(s_prefix, a.S, a.H, a.KVH, grid_parts, a.P, a.m, a.l);
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+      const int b = uniform(find_seq(s_prefix, a.S, item));
+      const int r = item - s_prefix[b];
+      const int nparts = (s_prefix[b + 1] - s_prefix[b]) / a.KVH;
+      const int kvh = uniform(r / nparts);
+      const int p = uniform(r - kvh * nparts);
+      int len = a.lens[b];
+      len = len > a.mb * 16 ? a.mb * 16 : len;
+      valu_partition<BF16, D, G, XP, LPT, W>(a, b, kvh, p, uniform(len), sm);
+    }
+  } else {
+    const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    int len = a.lens[b];
+    len = len < 0 ? 0 : (len > a.mb * 16 ? a.mb * 16 : len);
+    if (p * a.ps >= len) {  // empty partition: sentinel (PagedAttention V2, unused-partition branch)
+      if (threadIdx.x < G) {
+        const size_t si = ((size_t)b * a.H + (size_t)kvh * G + threadIdx.x) * a.P + p;
+        a.m[si] = kNegInf;
+        a.l[si] = 0.f;
+      }
+      return;
+    }
+    valu_partition<BF16, D, G, XP, LPT, W>(a, b, kvh, p, len, sm);
+  }
+}
+
+// Upper bound of resident workgroups the dense launch uses (persistent-style cap).
+int dense_grid_cap();
+
 template <bool BF16, bool XP, int D, int G>
 hipError_t launch_valu_one(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
   constexpr int EB = BF16 ? 2 : 4;
-  constexpr int LPT = (D * EB >= 512) ? 16 : 8;
+#ifndef PKV_VALU_ROW_BYTES_LPT16
+#define PKV_VALU_ROW_BYTES_LPT16 256
+#endif
+#ifndef PKV_VALU_WPE
+#define PKV_VALU_WPE 1
+#endif
+  // Token rows of >= 256 bytes are split over 16 lanes, shorter ones over 8.
+  constexpr int LPT = (D * EB >= PKV_VALU_ROW_BYTES_LPT16) ? 16 : 8;
   constexpr int W = 4;
-  dim3 grid(grid_parts, a.KVH, a.S);
-  hipLaunchKernelGGL((decode_partial_valu_kernel<BF16, D, G, XP, LPT, W>), grid, dim3(64 * W), 0, s, a);
+  constexpr int WPE = PKV_VALU_WPE;  // target waves per SIMD (4 caps VGPRs at 128)
+  if (a.S <= kMaxDenseSeqs) {
+    const long upper = (long)a.S * a.KVH * grid_parts;
+    const int grid = (int)(upper < dense_grid_cap() ? upper : dense_grid_cap());
+    hipLaunchKernelGGL((decode_partial_valu_kernel<BF16, D, G, XP, LPT, W, true, WPE>), dim3(grid), dim3(64 * W),
+                       0, s, a, grid_parts);
+  } else {
+    dim3 grid(grid_parts, a.KVH, a.S);
+    hipLaunchKernelGGL((decode_partial_valu_kernel<BF16, D, G, XP, LPT, W, false, WPE>), grid, dim3(64 * W), 0, s,
+                       a, grid_parts);
+  }
   return hipGetLastError();
 }
 
@@ -414,7 +486,7 @@ hipError_t launch_valu_d(const DecodePartialArgs& a, int G, int grid_parts, hipS
     case 6: return launch_valu_one<BF16, XP, D, 6>(a, grid_parts, s);
     case 7: return launch_valu_one<BF16, XP, D, 7>(a, grid_parts, s);
     case 8: return launch_valu_one<BF16, XP, D, 8>(a, grid_parts, s);
-    default: return hipErrorInvalidValue;
+    default: return hipErrorNotSupported;
   }
 }
 
@@ -425,8 +497,8 @@ hipError_t launch_valu(const DecodePartialArgs& a, int G, int grid_parts, hipStr
     case 128: return launch_valu_d<BF16, XP, 128>(a, G, grid_parts, s);
     case 256:
       if constexpr (BF16) return launch_valu_d<BF16, XP, 256>(a, G, grid_parts, s);
-      else return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
+      else return hipErrorNotSupported;
+    default: return hipErrorNotSupported;
   }
 }
 

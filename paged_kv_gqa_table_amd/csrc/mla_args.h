@@ -22,4 +22,7 @@ struct MlaArgs {
 
 hipError_t launch_mla_prefill(const MlaArgs& a, hipStream_t s);
 
+// Workgroup cap for persistent-style grids on the current device (host side).
+int dense_grid_cap();
+
 }  // namespace pkv

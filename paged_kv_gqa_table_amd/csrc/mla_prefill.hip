@@ -1,6 +1,286 @@
-// MLA causal paged prefill (placeholder until the MFMA kernel lands).
+// MLA causal paged prefill (page_size 1) on gfx950 matrix cores.
+//
+// What it computes is the kernel of the kernelindex gemini-2.5-pro Triton page
+// (_mla_paged_prefill_causal_h16_ckv512_kpe64_ps1_kernel): for query row r of batch b
+// (row i of that batch) and head h, over the keys j <= kv_len - q_len + i of the batch,
+//   x_j = sm_scale * (q_nope . ckv_j + q_pe . kpe_j),   O = sum_j softmax(x)_j ckv_j,
+//   lse = log2 sum_j exp(x_j),
+// with O = 0 and lse = -inf for a row that sees no key.
+//
+// gfx950 design (not the page's: it recomputes the 576-wide logits once per 512-dim
+// output slice and runs two passes; here it is one pass with an online softmax):
+//  * A workgroup is 4 waves = 4 consecutive query tokens of one batch; a wave owns the
+//    16 heads of its token (16 MFMA rows). Tiles are handed out last-first inside each
+//    batch so the longest causal rows start early.
+//  * Keys come in tiles of 32: the 32 [ckv | kpe] rows (1152 B each) are gathered through
+//    kv_indices straight into LDS with global_load_lds_dwordx4 (no staging registers),
+//    double-buffered so the next tile streams in while this one is used.
+//  * S^T = K . Q^T with v_mfma_f32_16x16x32_bf16: A = a K row slice read from LDS, B = the
+//    wave's Q^T kept in registers for the whole key loop (18 k-steps over 576 dims).
+//  * The S^T accumulator layout (lane = head, 4 keys per lane) is exactly the B operand
+//    of O^T = V^T . P^T, so P never moves. V^T operands are built from 16-byte LDS reads
+//    of 8 consecutive dims of 8 keys with byte permutes: output tile n of a 128-dim block
+//    holds dims 8 * row + n, which makes each lane's V chunk feed 8 tiles.
+//  * Softmax in base 2 (sm_scale * log2 e folded into one multiply), so lse comes out in
+//    base 2 directly. The per-head max is reduced across the 4 lanes of a head with
+//    lane permutes; l and O are re-based lazily (only when the max outgrows the
+//    reference by 2^8), with a wave-uniform branch.
+#include "common.h"
 #include "mla_args.h"
 
 namespace pkv {
-hipError_t launch_mla_prefill(const MlaArgs&, hipStream_t) { return hipErrorNotSupported; }
+
+namespace {
+
+constexpr int kH = 16;          // heads (MFMA rows / cols)
+constexpr int kDc = 512;        // ckv dims (also V dims)
+constexpr int kDp = 64;         // kpe dims
+constexpr int kQT = 4;          // query tokens per workgroup (one per wave)
+constexpr int kKT = 32;         // keys per tile
+constexpr int kRowChunks = (kDc + kDp) * 2 / 16;  // 72 16-byte chunks of a key row
+constexpr int kRowStride = kRowChunks + 1;        // padded LDS row (chunks): spreads banks
+constexpr int kTileChunks = kKT * kRowStride;     // 2336 slots that hold the tile
+constexpr int kTileAlloc = (kTileChunks + 63) / 64 * 64;  // whole 64-slot DMA rows
+constexpr int kMaxBatch = 512;
+constexpr float kMlaRebase = 8.f;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+PKV_DEVICE f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+PKV_DEVICE void vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Element e (0..7) of two 16-byte bf16 chunks, paired as (x[e], y[e]).
+PKV_DEVICE uint32_t pick_pair(const uint4& x, const uint4& y, int e) {
+  const uint32_t xa = e < 2 ? x.x : e < 4 ? x.y : e < 6 ? x.z : x.w;
+  const uint32_t ya = e < 2 ? y.x : e < 4 ? y.y : e < 6 ? y.z : y.w;
+  return (e & 1) ? pair_hi(xa, ya) : pair_lo(xa, ya);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
+  __shared__ __attribute__((aligned(16))) uint4 s_kv[2][kTileAlloc];
+  __shared__ int s_tiles[kMaxBatch + 1];  // exclusive prefix of query tiles per batch
+  __shared__ int s_wave[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform((int)(tid >> 6));
+  const int B = a.batch;
+
+  // ---- tile list: tiles of kQT query tokens, per batch
+  {
+    const int per = (B + 255) / 256;
+    const int i0 = tid * per;
+    int local = 0;
+    for (int i = i0; i < i0 + per && i < B; ++i) {
+      const int ql = a.qo_indptr[i + 1] - a.qo_indptr[i];
+      local += ql > 0 ? (ql + kQT - 1) / kQT : 0;
+    }
+    int x = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wave[w] = x;
+    __syncthreads();
+    int base = 0;
+    for (int v = 0; v < w; ++v) base += s_wave[v];
+    int run = base + x - local;
+    for (int i = i0; i < i0 + per && i < B; ++i) {
+      s_tiles[i] = run;
+      const int ql = a.qo_indptr[i + 1] - a.qo_indptr[i];
+      run += ql > 0 ? (ql + kQT - 1) / kQT : 0;
+    }
+    if (tid == 0) s_tiles[B] = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+    __syncthreads();
+  }
+  const int n_tiles = s_tiles[B];
+  (void)n_tiles_bound;
+
+  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    // batch of this tile
+    int lo = 0, hi = B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_tiles[mid] <= tile) lo = mid; else hi = mid;
+    }
+    const int b = uniform(lo);
+    const int q0 = a.qo_indptr[b], q1 = a.qo_indptr[b + 1];
+    const int k0 = a.kv_indptr[b];
+    const int q_len = q1 - q0;
+    int kv_len = a.kv_indptr[b + 1] - k0;
+    kv_len = kv_len < 0 ? 0 : kv_len;
+    const int nt_b = s_tiles[b + 1] - s_tiles[b];
+    const int t_in_b = uniform(nt_b - 1 - (tile - s_tiles[b]));  // last tile of the batch first
+    const int i_tok = t_in_b * kQT + w;                             // this wave's query token
+    const bool has_row = i_tok < q_len;
+    const int r = q0 + i_tok;
+    const int prefix = kv_len - q_len;
+    // keys visible to this wave's row: [0, vis)
+    int vis = has_row ? prefix + i_tok + 1 : 0;
+    vis = vis < 0 ? 0 : (vis > kv_len ? kv_len : vis);
+    // keys the workgroup needs: up to its last valid row
+    const int i_last = min(t_in_b * kQT + kQT - 1, q_len - 1);
+    int n_keys = prefix + i_last + 1;
+    n_keys = n_keys < 0 ? 0 : (n_keys > kv_len ? kv_len : n_keys);
+    n_keys = uniform(n_keys);
+    const int n_kt = (n_keys + kKT - 1) / kKT;
+
+    // ---- Q^T operands (B of S^T = K Q^T): lane = (head l%16, dims (l/16)*8 .. +8 of each k-step)
+    const int hq = lane & 15;
+    const int g = lane >> 4;
+    uint4 qb[18];
+    if (has_row) {
+      const char* qn = reinterpret_cast<const char*>(a.q_nope) + ((size_t)r * kH + hq) * kDc * 2;
+      const char* qp = reinterpret_cast<const char*>(a.q_pe) + ((size_t)r * kH + hq) * kDp * 2;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) qb[s] = ld16(qn + (s * 32 + g * 8) * 2);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) qb[16 + s] = ld16(qp + (s * 32 + g * 8) * 2);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 18; ++s) qb[s] = make_uint4(0, 0, 0, 0);
+    }
+
+    // ---- gather of one key tile into LDS buffer `buf`: 2336 chunk slots, 256 threads
+    auto issue_tile = [&](int kt, int buf) {
+      const int key0 = kt * kKT;
+      for (int c0 = w * 64; c0 < kTileAlloc; c0 += 256) {
+        const int slot = c0 + lane;  // this lane's chunk slot (the DMA writes slot c0 + lane)
+        int key = slot / kRowStride;
+        int ch = slot - key * kRowStride;
+        int kj = key0 + key;
+        kj = kj < n_keys ? kj : (n_keys > 0 ? n_keys - 1 : 0);  // clamp tail / pad to a valid key
+        int tok = a.kv_indices[k0 + kj];
+        tok = tok < 0 ? 0 : (tok >= a.num_pages ? a.num_pages - 1 : tok);
+        ch = ch < kRowChunks ? ch : 0;  // the pad chunk re-reads chunk 0
+        const char* src = ch < 64 ? reinterpret_cast<const char*>(a.ckv) + (size_t)tok * (kDc * 2) + ch * 16
+                                  : reinterpret_cast<const char*>(a.kpe) + (size_t)tok * (kDp * 2) + (ch - 64) * 16;
+        // lane i of the wave lands in slot c0 + i (slots past the tile fill the pad rows)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(&s_kv[buf][c0]), 16, 0, 0);
+      }
+    };
+
+    // O^T accumulators: tile (dblk, n) holds rows j -> dim dblk*128 + 8*j + n, cols = heads
+    f32x4_t acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_ref = kNegInf, m_true = kNegInf, lsum = 0.f;  // per head (lane's column)
+
+    if (n_kt > 0) issue_tile(0, 0);
+    for (int kt = 0; kt < n_kt; ++kt) {
+      const int buf = kt & 1;
+      vmcnt0();
+      __syncthreads();  // tile kt landed in LDS; everyone is done with tile kt-1
+      if (kt + 1 < n_kt) issue_tile(kt + 1, buf ^ 1);
+      const int key0 = kt * kKT;
+      if (key0 >= vis) continue;  // uniform: this wave's row sees none of these keys
+
+      // ---- S^T for two 16-key halves
+      f32x4_t st[2];
+      const uint4* kv = s_kv[buf];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const uint4* row = kv + (hf * 16 + hq) * kRowStride;  // A: key row (l%16), dims (l/16)*8..
+#pragma unroll
+        for (int s = 0; s < 18; ++s) c = mfma16x16x32(row[s * 4 + g], qb[s], c);
+        st[hf] = c;
+      }
+      // lane holds keys key0 + hf*16 + 4g + i for head hq
+      float x[8];
+      float tmax = kNegInf;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kj = key0 + hf * 16 + 4 * g + i;
+          const float v = (kj < vis) ? st[hf][i] * a.sm_scale_log2 : kNegInf;
+          x[hf * 4 + i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, xor_lanes(tmax, 16));
+      tmax = fmaxf(tmax, xor_lanes(tmax, 32));
+      m_true = fmaxf(m_true, tmax);
+      const bool rebase = m_true > m_ref + kMlaRebase;  // also true on the first tile (m_ref = -inf)
+      if (__builtin_amdgcn_ballot_w64(rebase) != 0) {   // wave-uniform branch
+        const float nref = rebase ? m_true : m_ref;
+        const float alpha = fast_exp2(m_ref - nref);
+        m_ref = nref;
+        lsum *= alpha;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) acc[i] *= alpha;
+      }
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(x[e] - m_ref);
+        lsum += p[e];
+      }
+      // P^T as the B operand: k-slot e <-> key (e < 4 ? 4g + e : 16 + 4g + e - 4)
+      const uint4 pb = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                  pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+
+      // ---- O^T += V^T P^T over 4 blocks of 128 dims
+#pragma unroll
+      for (int dblk = 0; dblk < 4; ++dblk) {
+        uint4 vv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
+          vv[e] = kv[key * kRowStride + dblk * 16 + hq];  // dims dblk*128 + 8*hq .. +8
+        }
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          const uint4 av = make_uint4(pick_pair(vv[0], vv[1], n), pick_pair(vv[2], vv[3], n),
+                                      pick_pair(vv[4], vv[5], n), pick_pair(vv[6], vv[7], n));
+          acc[dblk * 8 + n] = mfma16x16x32(av, pb, acc[dblk * 8 + n]);
+        }
+      }
+    }
+
+    // ---- finish: total l per head over the 4 lanes of the column, normalize, store
+    lsum += xor_lanes(lsum, 16);
+    lsum += xor_lanes(lsum, 32);
+    if (has_row) {
+      const bool any = lsum > 0.f;
+      const float inv = any ? 1.f / lsum : 0.f;
+      // lane: head hq, rows j = 4g + i of every tile -> dims dblk*128 + 8*(4g+i) + n
+      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((size_t)r * kH + hq) * kDc;
+#pragma unroll
+      for (int dblk = 0; dblk < 4; ++dblk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint4 o;
+          o.x = pack_bf16x2(acc[dblk * 8 + 0][i] * inv, acc[dblk * 8 + 1][i] * inv);
+          o.y = pack_bf16x2(acc[dblk * 8 + 2][i] * inv, acc[dblk * 8 + 3][i] * inv);
+          o.z = pack_bf16x2(acc[dblk * 8 + 4][i] * inv, acc[dblk * 8 + 5][i] * inv);
+          o.w = pack_bf16x2(acc[dblk * 8 + 6][i] * inv, acc[dblk * 8 + 7][i] * inv);
+          *reinterpret_cast<uint4*>(orow + dblk * 128 + 8 * (4 * g + i)) = o;
+        }
+      if (g == 0) a.lse[(size_t)r * kH + hq] = any ? m_ref + __log2f(lsum) : kNegInf;
+    }
+    __syncthreads();  // LDS buffers are reused by the next tile of work
+  }
+}
+
+hipError_t launch_mla_prefill(const MlaArgs& a, hipStream_t s) {
+  if (a.batch > kMaxBatch) return hipErrorNotSupported;
+  // upper bound of query tiles: total_q / 4 + one partial tile per batch
+  const long bound = (long)a.total_q / kQT + a.batch;
+  const int cap = dense_grid_cap();
+  const int grid = (int)(bound < cap ? bound : cap);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mla_prefill_kernel, dim3(grid), dim3(256), 0, s, a, (int)bound);
+  return hipGetLastError();
+}
+
 }  // namespace pkv

@@ -37,6 +37,23 @@ constexpr int kMaxGridYZ = 65535;
 
 }  // namespace
 
+namespace pkv {
+// Workgroup cap of the dense decode launches: 16 per compute unit of the current device
+// (queried once per device). Grids up to this size are dispatched whole and balanced by
+// the hardware; larger work lists are strided over the capped grid.
+int dense_grid_cap() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 4096;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = cus * 16;
+  }
+  return cached[dev];
+}
+}  // namespace pkv
+
 extern "C" int paged_decode_partial(const void* query, int dtype, const void* key_cache,
                                     const void* value_cache, int layout,
                                     const int32_t* block_tables, int max_blocks_per_seq,

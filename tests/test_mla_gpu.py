@@ -1,0 +1,102 @@
+"""GPU parity of the MLA causal paged prefill against the float64 oracle.
+
+Tolerances (as for every bf16 output here): |out - ref| <= 2e-2 + 1e-2 |ref| elementwise,
+|lse - ref| <= 1e-3 (base-2 LSE), rows that see no key exactly 0 / -inf.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_gqa_table_amd as pkv
+from paged_kv_gqa_table_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+ABS, REL, LSE_TOL = 2e-2, 1e-2, 1e-3
+FIELDS = ("q_nope", "q_pe", "ckv_cache", "kpe_cache", "qo_indptr", "kv_indptr", "kv_indices")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(case):
+    t = [getattr(case, k).to("cuda") for k in FIELDS]
+    out = torch.full_like(t[0], float("nan"))
+    lse = torch.full(t[0].shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+    pkv.mla_paged_prefill(*t, case.sm_scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out.cpu().to(torch.float64).numpy(), lse.cpu().to(torch.float64).numpy()
+
+
+def run_oracle(case):
+    return oracle.mla_prefill(*(getattr(case, k) for k in FIELDS), case.sm_scale)
+
+
+def check(o, l, ro, rl, what):
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
+    err = np.abs(o - ro)
+    bad = err > ABS + REL * np.abs(ro)
+    assert not bad.any(), f"{what}: {bad.sum()} out of tolerance, max abs {err.max()}"
+    both = np.isneginf(l) & np.isneginf(rl)
+    lerr = np.where(both, 0.0, np.abs(l - rl))
+    assert np.all(np.isfinite(lerr)) and lerr.max(initial=0) <= LSE_TOL, f"{what}: lse err {lerr.max()}"
+    return float(err.max(initial=0)), float(lerr.max(initial=0))
+
+
+def test_mla_prefill_b8_full():
+    case = inputs.mla_prefill_b8()
+    say(f"mla_prefill_b8: total_q={case.total_q} pages={case.num_pages}")
+    o, l = run_gpu(case)
+    ro, rl = run_oracle(case)
+    e, le = check(o, l, ro, rl, "mla_prefill_b8")
+    say(f"  max abs err {e:.3e}, lse err {le:.3e}")
+
+
+@pytest.mark.parametrize("q_lens,prefixes", [
+    ([1], [0]),
+    ([1, 2, 3, 4, 5], [0, 1, 31, 32, 33]),
+    ([4, 33, 64, 65], [100, 0, 7, 31]),
+    ([130, 9], [2, 500]),
+])
+def test_mla_edge_lengths(q_lens, prefixes):
+    say(f"mla edge q_lens={q_lens} prefixes={prefixes}")
+    case = inputs.make_mla(q_lens, prefixes, seed=sum(q_lens) + len(prefixes), extra_pages=5)
+    o, l = run_gpu(case)
+    ro, rl = run_oracle(case)
+    check(o, l, ro, rl, "edge")
+
+
+def test_mla_empty_kv_and_canaries():
+    """A batch with rows but no keys gives 0 / -inf; pages nobody references hold NaN."""
+    base = inputs.make_mla([5, 3], [20, 0], seed=9, extra_pages=7)
+    # insert a middle batch with 3 rows and no keys
+    qo = base.qo_indptr.tolist()
+    kv = base.kv_indptr.tolist()
+    qo_new = torch.tensor([0, qo[1], qo[1] + 3, qo[2] + 3], dtype=torch.int32)
+    kv_new = torch.tensor([0, kv[1], kv[1], kv[2]], dtype=torch.int32)
+    pad = lambda t: torch.cat([t[:qo[1]], torch.randn((3,) + t.shape[1:]).to(t.dtype), t[qo[1]:]])
+    case = inputs.MlaCase(name="empty_kv", q_nope=pad(base.q_nope), q_pe=pad(base.q_pe),
+                          ckv_cache=base.ckv_cache.clone(), kpe_cache=base.kpe_cache.clone(),
+                          qo_indptr=qo_new, kv_indptr=kv_new, kv_indices=base.kv_indices, sm_scale=base.sm_scale)
+    used = set(case.kv_indices.tolist())
+    unused = [i for i in range(case.num_pages) if i not in used]
+    assert unused
+    case.ckv_cache[unused] = float("nan")
+    case.kpe_cache[unused] = float("nan")
+    o, l = run_gpu(case)
+    ro, rl = run_oracle(case)
+    check(o, l, ro, rl, "empty kv + canaries")
+    rows = slice(qo[1], qo[1] + 3)
+    assert np.all(o[rows] == 0.0) and np.all(np.isneginf(l[rows]))
+
+
+def test_mla_deterministic():
+    case = inputs.make_mla([40, 7], [300, 12], seed=3)
+    o1, l1 = run_gpu(case)
+    o2, l2 = run_gpu(case)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
