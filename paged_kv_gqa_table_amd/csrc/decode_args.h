@@ -42,4 +42,7 @@ hipError_t launch_decode_mfma_bf16_tm(const DecodePartialArgs& a, int G, int gri
 hipError_t launch_decode_mfma_bf16_xp(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeReduceArgs& a, bool out_bf16, hipStream_t s);
 
+// Workgroup cap of the dense decode launches on the current device (host side).
+int dense_grid_cap();
+
 }  // namespace pkv

@@ -1,11 +1,327 @@
-// Placeholder: groups of 8 go through the vector-ALU kernel until the MFMA kernel lands.
+// Split-K paged decode, phase 1, on the matrix cores (query-head groups 8 <= G <= 16, bf16).
+//
+// Computes the same partials as the vector-ALU kernel (decode_valu.h): for one (sequence,
+// kv head, partition) and each of its G query heads, m = max score, l = sum exp(s - m) and
+// acc = sum exp(s - m) V (PagedAttention V2 Triton page, _partition_attn_kernel; unnormalized
+// accumulator as in the flash-decode post's _flash_decode_partial_kernel, whose Q group
+// tile times the page's K is the dense contraction used here).
+//
+// gfx950 design:
+//  * Same dense work list, workgroup shape (4 waves, pages round-robin) and LDS merge as
+//    the vector-ALU kernel; a wave handles one page (16 tokens) at a time.
+//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A = the page's K (lane: token l%16, 8 dims),
+//    B = Q^T of the group padded to 16 heads (registers, loaded once per item).
+//  * P^T comes straight from the S^T accumulator layout (lane: head l%16, tokens 4*(l/16)+i)
+//    and is the B operand of O^T = V^T P^T on v_mfma_f32_16x16x16_bf16 (k = 16 tokens).
+//    x-packed V ([D][16] per page) gives each lane its 4 tokens of one dim as one 8-byte
+//    load. Token-major V gives a lane 8 dims of one token per 16-byte load; byte permutes
+//    turn the 4 tokens' chunks into 8 A operands (tile n of a 128-dim block holds dims
+//    8 * row + n), so no LDS transpose is needed.
+//  * Per-head running max across the 4 lanes of a head, base-2 exponent, lazy re-basing
+//    behind a wave-uniform branch; the stored m is the exact max in natural-log units.
+#include "common.h"
 #include "decode_args.h"
+#include "worklist.h"
 
 namespace pkv {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr float kMfmaRebase = 8.f;
+
+PKV_DEVICE f32x4_t mfma_k32(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+PKV_DEVICE f32x4_t mfma_k16(uint2 a, uint2 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b),
+                                                   c, 0, 0, 0);
+}
+
+// Element e (0..7) of chunks x and y as a bf16 pair (x[e], y[e]).
+PKV_DEVICE uint32_t pick_pair(const uint4& x, const uint4& y, int e) {
+  const uint32_t xa = e < 2 ? x.x : e < 4 ? x.y : e < 6 ? x.z : x.w;
+  const uint32_t ya = e < 2 ? y.x : e < 4 ? y.y : e < 6 ? y.z : y.w;
+  return (e & 1) ? pair_hi(xa, ya) : pair_lo(xa, ya);
+}
+
+template <int W, int D>
+struct MfmaSmem {
+  float red_acc[W][16][D];
+  float red_m[W][16];
+  float red_mref[W][16];
+  float red_l[W][16];
+};
+
+template <int D, bool XP, int W>
+__device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const int G, const int b, const int kvh,
+                                               const int p, const int len, MfmaSmem<W, D>& sm) {
+  constexpr int BS = 16;
+  constexpr int ROWB = D * 2;
+  constexpr int PAGEB = BS * ROWB;
+  constexpr int KS = D / 32;   // k-steps of S^T
+  constexpr int NT = D / 16;   // O^T tiles
+  constexpr int NB = D / 128;  // 128-dim blocks (token-major V)
+  static_assert(D % 128 == 0 || XP, "token-major V needs whole 128-dim blocks");
+
+  const int lane = threadIdx.x & 63;
+  const int w = uniform((int)(threadIdx.x >> 6));
+  const int g = lane >> 4;
+  const int hl = lane & 15;
+  const int H = a.H;
+
+  const int npages_seq = (len + BS - 1) / BS;
+  const int pg_begin = p * a.ppp;
+  const int pg_end = min(pg_begin + a.ppp, npages_seq);
+  const int n_my = pg_end - pg_begin - w > 0 ? (pg_end - pg_begin - w + W - 1) / W : 0;
+  const int32_t* bt_row = a.bt + (size_t)b * a.mb;
+  int pid_cache = 0;
+  auto load_ids = [&](int i0) {
+    const int i = i0 + lane;
+    int id = (i < n_my) ? bt_row[pg_begin + w + W * i] : 0;
+    id = id < 0 ? 0 : id;
+    pid_cache = id >= a.NB ? a.NB - 1 : id;
+  };
+  load_ids(0);
+
+  // Q^T (B of S^T): lane = (head hl, dims 32 s + 8 g .. +8); heads past G are zero
+  uint4 qb[KS];
+  {
+    const char* qrow = reinterpret_cast<const char*>(a.q) + ((size_t)b * H + (size_t)kvh * G + hl) * ROWB;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qb[s] = hl < G ? ld16(qrow + (s * 32 + g * 8) * 2) : make_uint4(0, 0, 0, 0);
+  }
+
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegInf, m_true = kNegInf, lsum = 0.f;  // head hl
+
+  const size_t block_stride = (size_t)a.KVH * PAGEB;
+  const char* kbase = reinterpret_cast<const char*>(a.kc) + (size_t)kvh * PAGEB;
+  const char* vbase = reinterpret_cast<const char*>(a.vc) + (size_t)kvh * PAGEB;
+  auto page_ptr = [&](const char* base, int i) -> const char* {
+    const int id = __builtin_amdgcn_readlane(pid_cache, i & 63);
+    return base + (size_t)id * block_stride;
+  };
+
+  uint4 kr[KS];
+  uint4 vt[XP ? 1 : 4][XP ? 1 : NB];  // token-major: tokens 4g+i, chunk 16*blk + hl
+  uint2 vx[XP ? NT : 1];              // x-packed: dim 16 t + hl, tokens 4g .. 4g+3
+  auto issue_k = [&](int i) {
+    const char* kp = page_ptr(kbase, i);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if constexpr (XP) kr[s] = ld16(kp + ((s * 4 + g) * BS + hl) * 16);  // chunk (dims 32s+8g), token hl
+      else kr[s] = ld16(kp + hl * ROWB + (s * 32 + g * 8) * 2);
+    }
+  };
+  auto issue_v = [&](int i) {
+    const char* vp = page_ptr(vbase, i);
+    if constexpr (XP) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) vx[t] = *reinterpret_cast<const uint2*>(vp + ((16 * t + hl) * BS + 4 * g) * 2);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int k = 0; k < NB; ++k) vt[j][k] = ld16(vp + (4 * g + j) * ROWB + (16 * k + hl) * 16);
+    }
+  };
+
+  if (n_my > 0) {
+    issue_k(0);
+    issue_v(0);
+  }
+  for (int i = 0; i < n_my; ++i) {
+    const int pg = pg_begin + w + W * i;
+    const int ntok = min(BS, len - pg * BS);
+    const bool more = i + 1 < n_my;
+    if (more && ((i + 1) & 63) == 0) load_ids(i + 1);
+
+    f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) st = mfma_k32(kr[s], qb[s], st);
+    issue_k(more ? i + 1 : i);
+
+    float x[4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = (4 * g + j < ntok) ? st[j] * a.scale_log2 : kNegInf;
+      tmax = fmaxf(tmax, x[j]);
+    }
+    tmax = fmaxf(tmax, xor_lanes(tmax, 16));
+    tmax = fmaxf(tmax, xor_lanes(tmax, 32));
+    m_true = fmaxf(m_true, tmax);
+    const bool rebase = m_true > m_ref + kMfmaRebase;  // true on the first page (m_ref = -inf)
+    if (__builtin_amdgcn_ballot_w64(rebase) != 0) {
+      const float nref = rebase ? m_true : m_ref;
+      const float alpha = fast_exp2(m_ref - nref);
+      m_ref = nref;
+      lsum *= alpha;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+    }
+    float pr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pr[j] = fast_exp2(x[j] - m_ref);
+      lsum += pr[j];
+    }
+    const uint2 pb = make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
+
+    if (ntok < BS) {  // tail page: zero V of invalid tokens (their slots may hold NaN)
+      if constexpr (XP) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int t0 = 4 * g;
+          uint32_t lo = vx[t].x, hi = vx[t].y;
+          lo = (t0 >= ntok) ? 0u : (t0 + 1 >= ntok ? (lo & 0xffffu) : lo);
+          hi = (t0 + 2 >= ntok) ? 0u : (t0 + 3 >= ntok ? (hi & 0xffffu) : hi);
+          vx[t] = make_uint2(lo, hi);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (4 * g + j >= ntok)
+#pragma unroll
+            for (int k = 0; k < NB; ++k) vt[j][k] = make_uint4(0, 0, 0, 0);
+      }
+    }
+
+    if constexpr (XP) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = mfma_k16(vx[t], pb, acc[t]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          const uint2 av = make_uint2(pick_pair(vt[0][k], vt[1][k], n), pick_pair(vt[2][k], vt[3][k], n));
+          acc[k * 8 + n] = mfma_k16(av, pb, acc[k * 8 + n]);
+        }
+    }
+    issue_v(more ? i + 1 : i);
+  }
+
+  // ---- merge: l over the 4 lanes of a head, then waves through LDS
+  lsum += xor_lanes(lsum, 16);
+  lsum += xor_lanes(lsum, 32);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int d;
+      if constexpr (XP) d = 16 * t + 4 * g + j;
+      else d = (t / 8) * 128 + 8 * (4 * g + j) + (t % 8);
+      sm.red_acc[w][hl][d] = acc[t][j];
+    }
+  if (g == 0) {
+    sm.red_m[w][hl] = m_true;
+    sm.red_mref[w][hl] = m_ref;
+    sm.red_l[w][hl] = lsum;
+  }
+  __syncthreads();
+  const size_t stat_base = ((size_t)b * H + (size_t)kvh * G) * a.P + p;
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) {
+    const int h = idx / D;
+    const int d = idx - h * D;
+    float M = sm.red_m[0][h];
+#pragma unroll
+    for (int v = 1; v < W; ++v) M = fmaxf(M, sm.red_m[v][h]);
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
+      const float f = fast_exp2(sm.red_mref[v][h] - M);
+      o = fmaf(f, sm.red_acc[v][h][d], o);
+      L = fmaf(f, sm.red_l[v][h], L);
+    }
+    const size_t si = stat_base + (size_t)h * a.P;
+    a.acc[si * D + d] = o;
+    if (d == 0) {
+      a.m[si] = M * kLn2;
+      a.l[si] = L;
+    }
+  }
+  __syncthreads();
+}
+
+template <int D, bool XP, int W, bool DENSE>
+__global__ __launch_bounds__(64 * W) void decode_partial_mfma_kernel(DecodePartialArgs a, int G, int grid_parts) {
+  __shared__ MfmaSmem<W, D> sm;
+  if constexpr (DENSE) {
+    __shared__ int s_prefix[kMaxDenseSeqs + 1];
+    __shared__ int s_wave[W];
+    const int n_items = build_worklist<64 * W>(a.lens, a.S, a.mb * 16, a.ps, a.KVH, s_prefix, s_wave);
+    write_sentinels(s_prefix, a.S, a.H, a.KVH, grid_parts, a.P, a.m, a.l);
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+      const int b = uniform(find_seq(s_prefix, a.S, item));
+      const int r = item - s_prefix[b];
+      const int nparts = (s_prefix[b + 1] - s_prefix[b]) / a.KVH;
+      const int kvh = uniform(r / nparts);
+      const int p = uniform(r - kvh * nparts);
+      int len = a.lens[b];
+      len = len > a.mb * 16 ? a.mb * 16 : len;
+      mfma_partition<D, XP, W>(a, G, b, kvh, p, uniform(len), sm);
+    }
+  } else {
+    const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    int len = a.lens[b];
+    len = len < 0 ? 0 : (len > a.mb * 16 ? a.mb * 16 : len);
+    if (p * a.ps >= len) {
+      if ((int)threadIdx.x < G) {
+        const size_t si = ((size_t)b * a.H + (size_t)kvh * G + threadIdx.x) * a.P + p;
+        a.m[si] = kNegInf;
+        a.l[si] = 0.f;
+      }
+      return;
+    }
+    mfma_partition<D, XP, W>(a, G, b, kvh, p, len, sm);
+  }
+}
+
+template <int D, bool XP>
+hipError_t launch_mfma_d(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
+  constexpr int W = 4;
+  if (a.S <= kMaxDenseSeqs) {
+    const long upper = (long)a.S * a.KVH * grid_parts;
+    const int grid = (int)(upper < dense_grid_cap() ? upper : dense_grid_cap());
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, true>), dim3(grid), dim3(64 * W), 0, s, a, G,
+                       grid_parts);
+  } else {
+    dim3 grid(grid_parts, a.KVH, a.S);
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, false>), grid, dim3(64 * W), 0, s, a, G, grid_parts);
+  }
+  return hipGetLastError();
+}
+
+template <bool XP>
+hipError_t launch_mfma(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
+  if (G < 8 || G > 16) return hipErrorNotSupported;
+  switch (a.D) {
+    case 64:
+      if constexpr (XP) return launch_mfma_d<64, XP>(a, G, grid_parts, s);
+      else return hipErrorNotSupported;
+    case 128: return launch_mfma_d<128, XP>(a, G, grid_parts, s);
+    case 256: return launch_mfma_d<256, XP>(a, G, grid_parts, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace
+
 hipError_t launch_decode_mfma_bf16_tm(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
-  return G <= 8 ? launch_decode_valu_bf16_tm(a, G, grid_parts, s) : hipErrorNotSupported;
+  // D = 64 token-major rows are 128 bytes: no whole 128-dim V block; the vector-ALU kernel
+  // covers G <= 8 there and larger groups are not compiled.
+  if (a.D == 64) return G <= 8 ? launch_decode_valu_bf16_tm(a, G, grid_parts, s) : hipErrorNotSupported;
+  return launch_mfma<false>(a, G, grid_parts, s);
 }
 hipError_t launch_decode_mfma_bf16_xp(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
-  return G <= 8 ? launch_decode_valu_bf16_xp(a, G, grid_parts, s) : hipErrorNotSupported;
+  return launch_mfma<true>(a, G, grid_parts, s);
 }
+
 }  // namespace pkv

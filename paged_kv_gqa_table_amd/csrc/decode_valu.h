@@ -446,9 +446,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(WPE, 8))
   }
 }
 
-// Upper bound of resident workgroups the dense launch uses (persistent-style cap).
-int dense_grid_cap();
-
 template <bool BF16, bool XP, int D, int G>
 hipError_t launch_valu_one(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
   constexpr int EB = BF16 ? 2 : 4;

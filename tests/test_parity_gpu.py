@@ -201,8 +201,14 @@ EDGE_LENS = [0, 1, 15, 16, 17, 100, 511, 512, 513, 1024, 1500]
     ("bf16", 64, 9, 3, "token_major"),    # G=3
     ("bf16", 256, 10, 2, "token_major"),  # G=5
     ("bf16", 256, 14, 2, "xpacked"),      # G=7
-    ("bf16", 64, 8, 1, "xpacked"),        # G=8, MQA
+    ("bf16", 64, 8, 1, "xpacked"),        # G=8, MQA (matrix cores from here on)
     ("bf16", 128, 16, 2, "xpacked"),      # G=8
+    ("bf16", 128, 16, 2, "token_major"),  # G=8
+    ("bf16", 128, 32, 2, "token_major"),  # G=16
+    ("bf16", 128, 24, 2, "xpacked"),      # G=12
+    ("bf16", 256, 20, 2, "token_major"),  # G=10
+    ("bf16", 256, 48, 4, "xpacked"),      # G=12
+    ("bf16", 64, 6, 1, "token_major"),    # G=6
     ("f32", 64, 4, 4, "xpacked"),
     ("f32", 128, 12, 2, "token_major"),   # G=6
     ("f32", 128, 8, 1, "xpacked"),        # G=8
