@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time to spend")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain elementwise copy of MIB MiB (read MIB, write MIB) a few times, "
+                         "to scale HBM byte counters read under a profiler")
     return ap.parse_args()
 
 
@@ -189,6 +192,21 @@ def cpu_baseline_decode(case, budget_s):
             "seconds": round(dt, 2), "ms_per_step_equiv": dt * 1e3 * (case.kv_bytes() / max(done_bytes, 1))}
 
 
+def calibrate_copy(mib):
+    """A copy kernel of known size: dst = -src over `mib` MiB of float32, five launches.
+    Each launch reads exactly mib MiB and writes exactly mib MiB of HBM (both far larger
+    than the 256 MB Infinity Cache), which fixes the scale of FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib * 2**20 // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4,
+                      "launches": 5}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -199,6 +217,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy > 0:
+        calibrate_copy(args.calibrate_copy)
+        return
     from paged_kv_gqa_table_amd import inputs
     import paged_kv_gqa_table_amd as pkv
     pkv.lib()  # fail loudly if the HIP library is missing

@@ -1,9 +1,9 @@
-// Instances of the vector-ALU decode kernel for one (dtype, layout) pair; split into
-// separate translation units so the build compiles them in parallel.
-#include "decode_valu.h"
+// Instances of the bf16 vector-ALU decode kernel for one layout; one translation unit per
+// (dtype, layout) so the build compiles them in parallel.
+#include "decode_valu_bf16.h"
 
 namespace pkv {
 hipError_t launch_decode_valu_bf16_xp(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
-  return launch_valu<true, true>(a, G, grid_parts, s);
+  return launch_bf16<true>(a, G, grid_parts, s);
 }
 }  // namespace pkv

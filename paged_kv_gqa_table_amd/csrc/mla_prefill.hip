@@ -149,23 +149,37 @@ __global__ __launch_bounds__(256) void mla_prefill_kernel(MlaArgs a, int n_tiles
       for (int s = 0; s < 18; ++s) qb[s] = make_uint4(0, 0, 0, 0);
     }
 
-    // ---- gather of one key tile into LDS buffer `buf`: 2336 chunk slots, 256 threads
-    auto issue_tile = [&](int kt, int buf) {
+    // ---- gather of one key tile into LDS buffer `buf`: 2336 chunk slots over 256 threads.
+    // A wave's DMA instruction j fills slots c0 = 64 * (w + 4 j) .. +63 (lane i -> slot c0 + i).
+    // The page ids a lane needs for tile kt+1 are fetched during tile kt, so issuing a
+    // tile never waits on an id load.
+    constexpr int kDmaPerWave = (kTileAlloc / 64 + 3) / 4;  // 10 (the last one only for some waves)
+    int tok_next[kDmaPerWave];
+    auto load_ids = [&](int kt) {
       const int key0 = kt * kKT;
-      for (int c0 = w * 64; c0 < kTileAlloc; c0 += 256) {
-        const int slot = c0 + lane;  // this lane's chunk slot (the DMA writes slot c0 + lane)
-        int key = slot / kRowStride;
-        int ch = slot - key * kRowStride;
-        int kj = key0 + key;
-        kj = kj < n_keys ? kj : (n_keys > 0 ? n_keys - 1 : 0);  // clamp tail / pad to a valid key
+#pragma unroll
+      for (int j = 0; j < kDmaPerWave; ++j) {
+        const int slot = 64 * (w + 4 * j) + lane;
+        int kj = key0 + slot / kRowStride;
+        kj = kj < n_keys ? kj : (n_keys > 0 ? n_keys - 1 : 0);  // clamp tail / pad rows to a valid key
         int tok = a.kv_indices[k0 + kj];
-        tok = tok < 0 ? 0 : (tok >= a.num_pages ? a.num_pages - 1 : tok);
-        ch = ch < kRowChunks ? ch : 0;  // the pad chunk re-reads chunk 0
-        const char* src = ch < 64 ? reinterpret_cast<const char*>(a.ckv) + (size_t)tok * (kDc * 2) + ch * 16
-                                  : reinterpret_cast<const char*>(a.kpe) + (size_t)tok * (kDp * 2) + (ch - 64) * 16;
-        // lane i of the wave lands in slot c0 + i (slots past the tile fill the pad rows)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)(&s_kv[buf][c0]), 16, 0, 0);
+        tok_next[j] = tok < 0 ? 0 : (tok >= a.num_pages ? a.num_pages - 1 : tok);
+      }
+    };
+    auto issue_tile = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < kDmaPerWave; ++j) {
+        const int c0 = 64 * (w + 4 * j);
+        if (c0 < kTileAlloc) {  // wave-uniform
+          const int slot = c0 + lane;
+          int ch = slot % kRowStride;
+          ch = ch < kRowChunks ? ch : 0;  // the pad chunk re-reads chunk 0
+          const int tok = tok_next[j];
+          const char* src = ch < 64 ? reinterpret_cast<const char*>(a.ckv) + (size_t)tok * (kDc * 2) + ch * 16
+                                    : reinterpret_cast<const char*>(a.kpe) + (size_t)tok * (kDp * 2) + (ch - 64) * 16;
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                           (__attribute__((address_space(3))) void*)(&s_kv[buf][c0]), 16, 0, 0);
+        }
       }
     };
 
@@ -175,12 +189,19 @@ __global__ __launch_bounds__(256) void mla_prefill_kernel(MlaArgs a, int n_tiles
     for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_ref = kNegInf, m_true = kNegInf, lsum = 0.f;  // per head (lane's column)
 
-    if (n_kt > 0) issue_tile(0, 0);
+    if (n_kt > 0) {
+      load_ids(0);
+      issue_tile(0);
+      if (n_kt > 1) load_ids(1);
+    }
     for (int kt = 0; kt < n_kt; ++kt) {
       const int buf = kt & 1;
       vmcnt0();
       __syncthreads();  // tile kt landed in LDS; everyone is done with tile kt-1
-      if (kt + 1 < n_kt) issue_tile(kt + 1, buf ^ 1);
+      if (kt + 1 < n_kt) {
+        issue_tile(buf ^ 1);
+        if (kt + 2 < n_kt) load_ids(kt + 2);
+      }
       const int key0 = kt * kKT;
       if (key0 >= vis) continue;  // uniform: this wave's row sees none of these keys
 
