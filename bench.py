@@ -192,6 +192,35 @@ def cpu_baseline_decode(case, budget_s):
             "seconds": round(dt, 2), "ms_per_step_equiv": dt * 1e3 * (case.kv_bytes() / max(done_bytes, 1))}
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_partial_llama_gqa4_hbm_counters.md")
+
+
+def profiled_traffic(workload):
+    """HBM bytes per phase-1 launch from the committed counter summary (FETCH_SIZE + WRITE_SIZE,
+    scaled by a copy kernel of known size), or None when that summary does not cover this
+    workload or the kernel's sources have changed since the counters were read."""
+    import hashlib
+    if workload != "llama_gqa4" or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_PROFILE):
+        k, sep, v = line.partition(":")
+        if sep and k.strip() in ("traffic_bytes_per_launch", "kernel_sources_sha256", "kernel_sources"):
+            fields[k.strip()] = v.strip()
+    if len(fields) != 3:
+        return None
+    h = hashlib.sha256()
+    for name in fields["kernel_sources"].split():
+        path = os.path.join(ROOT, "paged_kv_gqa_table_amd", "csrc", name)
+        if not os.path.exists(path):
+            return None
+        with open(path, "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != fields["kernel_sources_sha256"]:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def calibrate_copy(mib):
     """A copy kernel of known size: dst = -src over `mib` MiB of float32, five launches.
     Each launch reads exactly mib MiB and writes exactly mib MiB of HBM (both far larger
@@ -260,7 +289,8 @@ def main():
                    "layout": case.layout, "kv_bytes_per_step": kv, "pool_copies_cycled": r["copies"],
                    "seq_len_total": int(case.seq_lens.sum())},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(args.workload),
+                     "algorithmic_bytes_per_launch": kv,
                      "kernel": "paged_decode_partial", "kernel_avg_us": r["partial_avg_ms"] * 1e3,
                      "kernel_median_us": r["partial_median_ms"] * 1e3,
                      "kernel_p10_us": r["partial_p10_ms"] * 1e3, "kernel_p90_us": r["partial_p90_ms"] * 1e3},
