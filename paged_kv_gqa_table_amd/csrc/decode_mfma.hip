@@ -254,16 +254,16 @@ template <int D, bool XP, int W, bool DENSE>
 __global__ __launch_bounds__(64 * W) void decode_partial_mfma_kernel(DecodePartialArgs a, int G, int grid_parts) {
   __shared__ MfmaSmem<W, D> sm;
   if constexpr (DENSE) {
-    __shared__ int s_prefix[kMaxDenseSeqs + 1];
-    __shared__ int s_wave[W];
-    const int n_items = build_worklist<64 * W>(a.lens, a.S, a.mb * 16, a.ps, a.KVH, s_prefix, s_wave);
-    write_sentinels(s_prefix, a.S, a.H, a.KVH, grid_parts, a.P, a.m, a.l);
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-      const int b = uniform(find_seq(s_prefix, a.S, item));
-      const int r = item - s_prefix[b];
-      const int nparts = (s_prefix[b + 1] - s_prefix[b]) / a.KVH;
-      const int kvh = uniform(r / nparts);
-      const int p = uniform(r - kvh * nparts);
+    extern __shared__ int s_worklist[];
+    __shared__ int s_wave[2 * W];
+    const DenseItems it = build_worklist<64 * W>(a.lens, a.S, a.mb * 16, a.ps, a.KVH, s_worklist, s_wave);
+    write_sentinels(it, a.H, grid_parts, a.P, a.m, a.l);
+    for (int item = blockIdx.x; item < it.n_items; item += gridDim.x) {
+      int b, kvh, p;
+      decode_item(it, item, b, kvh, p);
+      b = uniform(b);
+      kvh = uniform(kvh);
+      p = uniform(p);
       int len = a.lens[b];
       len = len > a.mb * 16 ? a.mb * 16 : len;
       mfma_partition<D, XP, W>(a, G, b, kvh, p, uniform(len), sm);
@@ -287,11 +287,11 @@ __global__ __launch_bounds__(64 * W) void decode_partial_mfma_kernel(DecodeParti
 template <int D, bool XP>
 hipError_t launch_mfma_d(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
   constexpr int W = 4;
-  if (a.S <= kMaxDenseSeqs) {
+  if (use_dense_worklist(a.S, a.KVH, grid_parts)) {
     const long upper = (long)a.S * a.KVH * grid_parts;
     const int grid = (int)(upper < dense_grid_cap() ? upper : dense_grid_cap());
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, true>), dim3(grid), dim3(64 * W), 0, s, a, G,
-                       grid_parts);
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, true>), dim3(grid), dim3(64 * W),
+                       worklist_lds_words(a.S) * sizeof(int), s, a, G, grid_parts);
   } else {
     dim3 grid(grid_parts, a.KVH, a.S);
     hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, false>), grid, dim3(64 * W), 0, s, a, G, grid_parts);

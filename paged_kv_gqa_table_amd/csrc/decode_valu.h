@@ -416,16 +416,16 @@ template <bool BF16, int D, int G, bool XP, int LPT, int W, bool DENSE, int WPE>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(WPE, 8))) void decode_partial_valu_kernel(DecodePartialArgs a, int grid_parts) {
   __shared__ ValuSmem<W, G, D, XP> sm;
   if constexpr (DENSE) {
-    __shared__ int s_prefix[kMaxDenseSeqs + 1];
-    __shared__ int s_wave[W];
-    const int n_items = build_worklist<64 * W>(a.lens, a.S, a.mb * 16, a.ps, a.KVH, s_prefix, s_wave);
-    write_sentinels(s_prefix, a.S, a.H, a.KVH, grid_parts, a.P, a.m, a.l);
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-      const int b = uniform(find_seq(s_prefix, a.S, item));
-      const int r = item - s_prefix[b];
-      const int nparts = (s_prefix[b + 1] - s_prefix[b]) / a.KVH;
-      const int kvh = uniform(r / nparts);
-      const int p = uniform(r - kvh * nparts);
+    extern __shared__ int s_worklist[];
+    __shared__ int s_wave[2 * W];
+    const DenseItems it = build_worklist<64 * W>(a.lens, a.S, a.mb * 16, a.ps, a.KVH, s_worklist, s_wave);
+    write_sentinels(it, a.H, grid_parts, a.P, a.m, a.l);
+    for (int item = blockIdx.x; item < it.n_items; item += gridDim.x) {
+      int b, kvh, p;
+      decode_item(it, item, b, kvh, p);
+      b = uniform(b);
+      kvh = uniform(kvh);
+      p = uniform(p);
       int len = a.lens[b];
       len = len > a.mb * 16 ? a.mb * 16 : len;
       valu_partition<BF16, D, G, XP, LPT, W>(a, b, kvh, p, uniform(len), sm);
@@ -459,11 +459,11 @@ hipError_t launch_valu_one(const DecodePartialArgs& a, int grid_parts, hipStream
   constexpr int LPT = (D * EB >= PKV_VALU_ROW_BYTES_LPT16) ? 16 : 8;
   constexpr int W = 4;
   constexpr int WPE = PKV_VALU_WPE;  // target waves per SIMD (4 caps VGPRs at 128)
-  if (a.S <= kMaxDenseSeqs) {
+  if (use_dense_worklist(a.S, a.KVH, grid_parts)) {
     const long upper = (long)a.S * a.KVH * grid_parts;
     const int grid = (int)(upper < dense_grid_cap() ? upper : dense_grid_cap());
     hipLaunchKernelGGL((decode_partial_valu_kernel<BF16, D, G, XP, LPT, W, true, WPE>), dim3(grid), dim3(64 * W),
-                       0, s, a, grid_parts);
+                       worklist_lds_words(a.S) * sizeof(int), s, a, grid_parts);
   } else {
     dim3 grid(grid_parts, a.KVH, a.S);
     hipLaunchKernelGGL((decode_partial_valu_kernel<BF16, D, G, XP, LPT, W, false, WPE>), grid, dim3(64 * W), 0, s,

@@ -391,21 +391,22 @@ __device__ __forceinline__ void bf16_partition(const DecodePartialArgs& a, const
   __syncthreads();
 }
 
+// Waves per SIMD the register allocator must leave room for: 4 where the kernel fits in
+// 128 VGPRs without spilling, else no constraint.
+constexpr int bf16_min_waves(int D, int G) { return (D == 64 && G <= 5) || (D == 128 && G <= 4) ? 4 : 1; }
+
 template <int D, int G, bool XP, int W, bool DENSE>
-__global__ __launch_bounds__(64 * W) void decode_partial_bf16_kernel(DecodePartialArgs a, int grid_parts) {
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(bf16_min_waves(D, G), 8))) void decode_partial_bf16_kernel(DecodePartialArgs a, int grid_parts) {
   __shared__ Bf16Smem<W, G, D> sm;
   if constexpr (DENSE) {
-    __shared__ int s_prefix[kMaxDenseSeqs + 1];
-    __shared__ int s_wave[W];
-    const int n_items = build_worklist<64 * W>(a.lens, a.S, a.mb * 16, a.ps, a.KVH, s_prefix, s_wave);
-    write_sentinels(s_prefix, a.S, a.H, a.KVH, grid_parts, a.P, a.m, a.l);
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-      const int b = uniform(find_seq(s_prefix, a.S, item));
-      const int r = item - s_prefix[b];
-      const int nparts = (s_prefix[b + 1] - s_prefix[b]) / a.KVH;
-      const int kvh = uniform(r / nparts);
-      const int p = uniform(r - kvh * nparts);
-      bf16_partition<D, G, XP, W>(a, b, kvh, p, a.lens[b], sm);
+    extern __shared__ int s_worklist[];
+    __shared__ int s_wave[2 * W];
+    const DenseItems it = build_worklist<64 * W>(a.lens, a.S, a.mb * 16, a.ps, a.KVH, s_worklist, s_wave);
+    write_sentinels(it, a.H, grid_parts, a.P, a.m, a.l);
+    for (int item = blockIdx.x; item < it.n_items; item += gridDim.x) {
+      int b, kvh, p;
+      decode_item(it, item, b, kvh, p);
+      bf16_partition<D, G, XP, W>(a, uniform(b), uniform(kvh), uniform(p), a.lens[b], sm);
     }
   } else {
     // direct map, partition-major: workgroup i handles partition i / (S * KVH) of
@@ -433,10 +434,10 @@ hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream
   // The dense work list costs one extra memory round trip per workgroup but keeps every
   // workgroup busy and balanced; on MI355X it was faster than the plain partition grid even
   // for uniform lengths, so the plain grid (ratio > 0) is kept only for very large batches.
-  if (a.S <= kMaxDenseSeqs && upper > (long)PKV_DENSE_RATIO * dense_grid_cap() / 4) {
+  if (use_dense_worklist(a.S, a.KVH, grid_parts) && upper > (long)PKV_DENSE_RATIO * dense_grid_cap() / 4) {
     const int grid = (int)(upper < dense_grid_cap() ? upper : dense_grid_cap());
-    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, true>), dim3(grid), dim3(64 * W), 0, s, a,
-                       grid_parts);
+    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, true>), dim3(grid), dim3(64 * W),
+                       worklist_lds_words(a.S) * sizeof(int), s, a, grid_parts);
   } else {
     hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, false>), dim3((unsigned)upper), dim3(64 * W), 0, s,
                        a, grid_parts);

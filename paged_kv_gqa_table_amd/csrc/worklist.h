@@ -1,10 +1,18 @@
 // Dense work list for split-K decode, built redundantly by every workgroup from seq_lens.
 //
-// A work item is one (sequence b, kv head, partition p) with p < ceil(len_b / ps). Items of
-// sequence b are numbered prefix[b] .. prefix[b+1]-1 (kv head major, partition minor), so
-// a launch can map blockIdx to real work only: workgroups never spin on empty partitions,
-// however skewed the batch. The prefix sums live in LDS; sequences past kMaxDenseSeqs use
-// the plain (partition, kv head, sequence) grid instead.
+// A work item is one (sequence b, kv head, partition p) with p < ceil(len_b / ps). Only
+// real items are numbered, so a launch maps blockIdx to work without ever visiting an
+// empty partition, however skewed the batch. Items are ordered for a short tail:
+//   1. every full partition (ps tokens) of every sequence, sequence-major, then kv head,
+//      then partition;
+//   2. the partial last partitions (len_b % ps != 0), sequence by sequence, kv head minor.
+// Workgroups take items in blockIdx order, so the items that start last, after the
+// first wave of workgroups drains, are the short ones.
+//
+// LDS (dynamic, worklist_lds_words(S) ints): s_full[S + 1] holds, per sequence, the
+// exclusive prefix of its full items shifted left by one, with bit 0 set when it has a
+// partial partition; s_order[S] lists the sequences with a partial partition in the
+// order their items are numbered.
 #pragma once
 
 #include "common.h"
@@ -12,73 +20,122 @@
 namespace pkv {
 
 constexpr int kMaxDenseSeqs = 4096;
+__host__ __device__ inline int worklist_lds_words(int S) { return 2 * S + 1; }
 
-// Partitions of one sequence, with its length clamped into [0, mb * 16].
-PKV_DEVICE int partitions_of(int len, int mb_tokens, int ps) {
-  len = len < 0 ? 0 : (len > mb_tokens ? mb_tokens : len);
-  return (len + ps - 1) / ps;
+// The list is used when its LDS fits and item counts fit the packed prefix (< 2^30).
+inline bool use_dense_worklist(int S, int KVH, int grid_parts) {
+  return S <= kMaxDenseSeqs && (long)S * KVH * grid_parts < (1L << 30);
 }
 
-// Builds s_prefix[0..S] (exclusive prefix of items per sequence) with all NT threads of
-// the block; returns the total number of items. Ends with a barrier.
+struct DenseItems {
+  const int* full;   // s_full
+  const int* order;  // s_order
+  int S, KVH, n_full, n_items;
+};
+
+// Builds the list with all NT threads of the block (s_wave: 2 * NT / 64 ints). Ends with a
+// barrier. Lengths are clamped into [0, mb_tokens].
 template <int NT>
-__device__ int build_worklist(const int32_t* lens, int S, int mb_tokens, int ps, int KVH, int* s_prefix,
-                              int* s_wave) {
+__device__ DenseItems build_worklist(const int32_t* lens, int S, int mb_tokens, int ps, int KVH, int* lds,
+                                     int* s_wave) {
   constexpr int NW = NT / 64;
+  int* s_full = lds;
+  int* s_order = lds + S + 1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const int per = (S + NT - 1) / NT;
   const int i0 = tid * per;
-  int local = 0;
-  for (int i = i0; i < i0 + per && i < S; ++i) local += partitions_of(lens[i], mb_tokens, ps) * KVH;
-  // inclusive scan of `local` inside the wave
-  int x = local;
+  const int i1 = min(i0 + per, S);
+  int local_f = 0, local_p = 0;
+  for (int i = i0; i < i1; ++i) {
+    int len = lens[i];
+    len = len < 0 ? 0 : (len > mb_tokens ? mb_tokens : len);
+    const int nf = len / ps;
+    const int rem = len - nf * ps;
+    s_full[i] = len;  // this thread's own slots: read back below without a barrier
+    local_f += nf * KVH;
+    local_p += rem > 0;
+  }
+  // inclusive scans of both counts inside the wave
+  int xf = local_f, xp = local_p;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
+    const int yf = __shfl_up(xf, off, 64);
+    const int yp = __shfl_up(xp, off, 64);
+    if (lane >= off) {
+      xf += yf;
+      xp += yp;
+    }
   }
-  if (lane == 63) s_wave[wv] = x;
-  __syncthreads();
-  int base = 0;
-#pragma unroll
-  for (int v = 0; v < NW; ++v) base += (v < wv) ? s_wave[v] : 0;
-  int run = base + x - local;  // exclusive prefix of this thread's first sequence
-  for (int i = i0; i < i0 + per && i < S; ++i) {
-    s_prefix[i] = run;
-    run += partitions_of(lens[i], mb_tokens, ps) * KVH;
+  if (lane == 63) {
+    s_wave[wv] = xf;
+    s_wave[NW + wv] = xp;
   }
-  int total = 0;
-#pragma unroll
-  for (int v = 0; v < NW; ++v) total += s_wave[v];
-  if (tid == 0) s_prefix[S] = total;
   __syncthreads();
-  return total;
+  int base_f = 0, base_p = 0, n_full = 0, n_pseq = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    base_f += (v < wv) ? s_wave[v] : 0;
+    base_p += (v < wv) ? s_wave[NW + v] : 0;
+    n_full += s_wave[v];
+    n_pseq += s_wave[NW + v];
+  }
+  int run_f = base_f + xf - local_f;  // exclusive prefixes at this thread's first sequence
+  int run_p = base_p + xp - local_p;
+  for (int i = i0; i < i1; ++i) {
+    const int len = s_full[i];
+    const int nf = len / ps;
+    const bool has_p = len - nf * ps > 0;
+    s_full[i] = (run_f << 1) | (has_p ? 1 : 0);
+    run_f += nf * KVH;
+    if (has_p) s_order[run_p++] = i;
+  }
+  if (tid == 0) s_full[S] = n_full << 1;
+  __syncthreads();
+  return DenseItems{s_full, s_order, S, KVH, n_full, n_full + n_pseq * KVH};
 }
 
-// Sequence owning `item`: the largest b with s_prefix[b] <= item (uniform search).
-PKV_DEVICE int find_seq(const int* s_prefix, int S, int item) {
-  int lo = 0, hi = S;  // s_prefix[lo] <= item < s_prefix[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_prefix[mid] <= item) lo = mid; else hi = mid;
+PKV_DEVICE int full_prefix(const DenseItems& it, int b) { return it.full[b] >> 1; }
+
+// Number of partitions (full and partial) of sequence b.
+PKV_DEVICE int seq_parts(const DenseItems& it, int b) {
+  return (full_prefix(it, b + 1) - full_prefix(it, b)) / it.KVH + (it.full[b] & 1);
+}
+
+// (b, kv head, p) of `item` (uniform across the workgroup).
+PKV_DEVICE void decode_item(const DenseItems& it, int item, int& b, int& kvh, int& p) {
+  if (item < it.n_full) {
+    int lo = 0, hi = it.S;  // full_prefix(lo) <= item < full_prefix(hi)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (full_prefix(it, mid) <= item) lo = mid; else hi = mid;
+    }
+    const int r = item - full_prefix(it, lo);
+    const int nf = (full_prefix(it, lo + 1) - full_prefix(it, lo)) / it.KVH;
+    b = lo;
+    kvh = r / nf;
+    p = r - kvh * nf;
+  } else {
+    const int r = item - it.n_full;
+    const int j = r / it.KVH;
+    b = it.order[j];
+    b = b < 0 ? 0 : (b >= it.S ? it.S - 1 : b);  // always a valid row, whatever the list holds
+    kvh = r - j * it.KVH;
+    p = (full_prefix(it, b + 1) - full_prefix(it, b)) / it.KVH;  // the partition after the full ones
   }
-  return lo;
 }
 
 // Sentinel m = -inf, l = 0 for every (b, h, p) with ceil(len_b / ps) <= p < grid_parts,
 // spread over the whole grid (one pass, grid-stride).
-PKV_DEVICE void write_sentinels(const int* s_prefix, int S, int H, int KVH, int grid_parts, int P,
-                                float* m, float* l) {
-  const long total = (long)S * H * grid_parts;
+PKV_DEVICE void write_sentinels(const DenseItems& it, int H, int grid_parts, int P, float* m, float* l) {
+  const long total = (long)it.S * H * grid_parts;
   const long stride = (long)gridDim.x * blockDim.x;
   for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
     const int p = (int)(idx % grid_parts);
     const long bh = idx / grid_parts;
     const int b = (int)(bh / H);
-    const int nparts = (s_prefix[b + 1] - s_prefix[b]) / KVH;
-    if (p >= nparts) {
+    if (p >= seq_parts(it, b)) {
       const size_t o = (size_t)bh * P + p;
       m[o] = kNegInf;
       l[o] = 0.f;

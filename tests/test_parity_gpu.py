@@ -243,3 +243,33 @@ def test_nan_canaries_and_permutation(layout):
         "not deterministic"
     ref = oracle_subset(case, list(range(case.num_seqs)))
     check_out(clean["out"], ref["out"], "bf16", "canary case out")
+
+
+@pytest.mark.parametrize("S,dtype,D,H,KVH,layout", [
+    (300, "bf16", 128, 16, 4, "token_major"),   # > 128 sequences: partial items in sequence order
+    (300, "bf16", 128, 32, 2, "xpacked"),       # same, matrix-core kernel (G=16)
+    (300, "f32", 64, 8, 2, "token_major"),
+    (4100, "bf16", 64, 8, 2, "token_major"),    # > 4096 sequences: plain partition grid
+    (4100, "bf16", 128, 24, 2, "xpacked"),      # same, matrix-core kernel (G=12)
+])
+def test_many_sequences(S, dtype, D, H, KVH, layout):
+    say(f"many sequences: S={S} {dtype} D={D} H={H} KVH={KVH} {layout}")
+    rng = np.random.default_rng(S + D + H)
+    lens = rng.integers(0, 200, S)
+    lens[::7] = 0
+    lens[1::11] = 128   # whole partitions only
+    lens[2::13] = 64
+    case = inputs.make_decode(lens, H, KVH, D, dtype=dtype, layout=layout, seed=S + H, partition_size=64)
+    ps = 64
+    g = run_gpu(case, partition_size=ps)
+    seqs = sorted({0, 1, 2, 3, S - 1, *rng.choice(S, 20, replace=False).tolist()})
+    ref = oracle_subset(case, seqs, partition_size=ps, partials=True)
+    check_out(g["out"][seqs], ref["out"], dtype, "out")
+    check_lse(g["lse"][seqs], ref["lse"], dtype, "lse")
+    check_partials(g, ref, seqs, lens, ps, dtype, "partials")
+    for b in range(S):  # every sequence: finite partials where they exist, sentinels after
+        nb = -(-int(lens[b]) // ps)
+        assert np.all(np.isneginf(g["m"][b, :, nb:])) and np.all(g["l"][b, :, nb:] == 0), f"sentinel b={b}"
+        assert np.all(np.isfinite(g["m"][b, :, :nb])) and np.all(g["l"][b, :, :nb] >= 1.0 - 1e-6), f"b={b}"
+        if nb == 0:
+            assert np.all(g["out"][b] == 0.0) and np.all(np.isneginf(g["lse"][b])), f"empty b={b}"
