@@ -44,5 +44,8 @@ hipError_t launch_decode_reduce(const DecodeReduceArgs& a, bool out_bf16, hipStr
 
 // Workgroup cap of the dense decode launches on the current device (host side).
 int dense_grid_cap();
+// Workgroups of `kernel` (block_threads threads, dyn_lds bytes of dynamic LDS) that the
+// current device holds at once; dense_grid_cap() if the runtime cannot tell.
+int resident_grid(const void* kernel, int block_threads, size_t dyn_lds);
 
 }  // namespace pkv

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "decode_args.h"
@@ -48,9 +49,44 @@ int dense_grid_cap() {
   if (cached[dev] == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached[dev] = cus * 16;
+#ifndef PKV_GRID_PER_CU
+#define PKV_GRID_PER_CU 16
+#endif
+    cached[dev] = cus * PKV_GRID_PER_CU;
   }
   return cached[dev];
+}
+
+int resident_grid(const void* kernel, int block_threads, size_t dyn_lds) {
+  struct Entry {
+    const void* kernel;
+    int dev, threads;
+    size_t lds;
+    int grid;
+  };
+  static Entry cache[256];
+  static int n_cache = 0;
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return dense_grid_cap();
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n_cache; ++i)
+      if (cache[i].kernel == kernel && cache[i].dev == dev && cache[i].threads == block_threads &&
+          cache[i].lds == dyn_lds)
+        return cache[i].grid;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, dyn_lds) != hipSuccess ||
+      per_cu <= 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    return dense_grid_cap();
+  }
+  const int grid = per_cu * cus;
+  std::lock_guard<std::mutex> lock(mu);
+  if (n_cache < 256) cache[n_cache++] = Entry{kernel, dev, block_threads, dyn_lds, grid};
+  return grid;
 }
 }  // namespace pkv
 
