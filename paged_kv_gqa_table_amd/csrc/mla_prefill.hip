@@ -14,7 +14,14 @@
 //    batch so the longest causal rows start early.
 //  * Keys come in tiles of 32: the 32 [ckv | kpe] rows (1152 B each) are gathered through
 //    kv_indices straight into LDS with global_load_lds_dwordx4 (no staging registers),
-//    double-buffered so the next tile streams in while this one is used.
+//    double-buffered. Each wave moves 8 keys: one transfer per key for its 1 KiB ckv row
+//    (scalar address, page id from the scalar cache) and 8 lane-masked transfers for the
+//    8 keys' kpe rows, so the gather costs almost no vector instructions. ckv rows sit at
+//    a padded LDS stride; kpe rows are packed.
+//  * The compiler waits for an LDS transfer before the next LDS read (it cannot tell the
+//    two buffers apart), so within a workgroup a tile's gather is not overlapped with the
+//    previous tile's math. Instead the kernel is held to 256 registers so that two
+//    workgroups share a CU and cover each other's gathers.
 //  * S^T = K . Q^T with v_mfma_f32_16x16x32_bf16: A = a K row slice read from LDS, B = the
 //    wave's Q^T kept in registers for the whole key loop (18 k-steps over 576 dims).
 //  * The S^T accumulator layout (lane = head, 4 keys per lane) is exactly the B operand
@@ -37,10 +44,10 @@ constexpr int kDc = 512;        // ckv dims (also V dims)
 constexpr int kDp = 64;         // kpe dims
 constexpr int kQT = 4;          // query tokens per workgroup (one per wave)
 constexpr int kKT = 32;         // keys per tile
-constexpr int kRowChunks = (kDc + kDp) * 2 / 16;  // 72 16-byte chunks of a key row
-constexpr int kRowStride = kRowChunks + 1;        // padded LDS row (chunks): spreads banks
-constexpr int kTileChunks = kKT * kRowStride;     // 2336 slots that hold the tile
-constexpr int kTileAlloc = (kTileChunks + 63) / 64 * 64;  // whole 64-slot DMA rows
+constexpr int kCkvChunks = kDc * 2 / 16;     // 64 16-byte chunks of a ckv row
+constexpr int kKpeChunks = kDp * 2 / 16;     // 8 chunks of a kpe row
+constexpr int kCkvStride = kCkvChunks + 1;   // padded LDS row (chunks): spreads banks
+constexpr int kKeysPerWave = kKT / kQT;      // 8 keys of a tile gathered by each wave
 constexpr int kMaxBatch = 512;
 constexpr float kMlaRebase = 8.f;
 
@@ -54,6 +61,13 @@ PKV_DEVICE f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
 
 PKV_DEVICE void vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// 16 bytes per lane from global memory (scalar base + per-lane offset) straight into LDS
+// (lane i -> lds_base + 16 i; lanes outside the exec mask move nothing).
+PKV_DEVICE void lds_dma16_s(const void* sbase, uint32_t voff, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(reinterpret_cast<const char*>(sbase) + voff),
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
 // Element e (0..7) of two 16-byte bf16 chunks, paired as (x[e], y[e]).
 PKV_DEVICE uint32_t pick_pair(const uint4& x, const uint4& y, int e) {
   const uint32_t xa = e < 2 ? x.x : e < 4 ? x.y : e < 6 ? x.z : x.w;
@@ -63,8 +77,10 @@ PKV_DEVICE uint32_t pick_pair(const uint4& x, const uint4& y, int e) {
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
-  __shared__ __attribute__((aligned(16))) uint4 s_kv[2][kTileAlloc];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))  // 2 workgroups per CU
+void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
+  __shared__ __attribute__((aligned(16))) uint4 s_ckv[2][kKT * kCkvStride];
+  __shared__ __attribute__((aligned(16))) uint4 s_kpe[2][kKT * kKpeChunks];
   __shared__ int s_tiles[kMaxBatch + 1];  // exclusive prefix of query tiles per batch
   __shared__ int s_wave[4];
 
@@ -149,38 +165,34 @@ __global__ __launch_bounds__(256) void mla_prefill_kernel(MlaArgs a, int n_tiles
       for (int s = 0; s < 18; ++s) qb[s] = make_uint4(0, 0, 0, 0);
     }
 
-    // ---- gather of one key tile into LDS buffer `buf`: 2336 chunk slots over 256 threads.
-    // A wave's DMA instruction j fills slots c0 = 64 * (w + 4 j) .. +63 (lane i -> slot c0 + i).
-    // The page ids a lane needs for tile kt+1 are fetched during tile kt, so issuing a
-    // tile never waits on an id load.
-    constexpr int kDmaPerWave = (kTileAlloc / 64 + 3) / 4;  // 10 (the last one only for some waves)
-    int tok_next[kDmaPerWave];
+    // ---- gather of one key tile into LDS buffer `buf`: wave w moves keys 8w .. 8w+7 of the
+    // tile (keys past the workgroup's last one re-read its last key; they are masked). The
+    // page ids of tile kt+1 are read through the scalar cache during tile kt.
+    const __attribute__((address_space(4))) int32_t* ids =
+        (const __attribute__((address_space(4))) int32_t*)(a.kv_indices + k0);
+    int tok_next[kKeysPerWave];
     auto load_ids = [&](int kt) {
-      const int key0 = kt * kKT;
+      const int last = n_keys > 0 ? n_keys - 1 : 0;
 #pragma unroll
-      for (int j = 0; j < kDmaPerWave; ++j) {
-        const int slot = 64 * (w + 4 * j) + lane;
-        int kj = key0 + slot / kRowStride;
-        kj = kj < n_keys ? kj : (n_keys > 0 ? n_keys - 1 : 0);  // clamp tail / pad rows to a valid key
-        int tok = a.kv_indices[k0 + kj];
-        tok_next[j] = tok < 0 ? 0 : (tok >= a.num_pages ? a.num_pages - 1 : tok);
+      for (int k = 0; k < kKeysPerWave; ++k) {
+        const int t = ids[min(kt * kKT + kKeysPerWave * w + k, last)];
+        tok_next[k] = t < 0 ? 0 : (t >= a.num_pages ? a.num_pages - 1 : t);
       }
     };
+    const uint32_t lane16 = (uint32_t)lane * 16;
     auto issue_tile = [&](int buf) {
 #pragma unroll
-      for (int j = 0; j < kDmaPerWave; ++j) {
-        const int c0 = 64 * (w + 4 * j);
-        if (c0 < kTileAlloc) {  // wave-uniform
-          const int slot = c0 + lane;
-          int ch = slot % kRowStride;
-          ch = ch < kRowChunks ? ch : 0;  // the pad chunk re-reads chunk 0
-          const int tok = tok_next[j];
-          const char* src = ch < 64 ? reinterpret_cast<const char*>(a.ckv) + (size_t)tok * (kDc * 2) + ch * 16
-                                    : reinterpret_cast<const char*>(a.kpe) + (size_t)tok * (kDp * 2) + (ch - 64) * 16;
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                           (__attribute__((address_space(3))) void*)(&s_kv[buf][c0]), 16, 0, 0);
-        }
+      for (int k = 0; k < kKeysPerWave; ++k) {
+        const char* row = reinterpret_cast<const char*>(a.ckv) + (size_t)tok_next[k] * (kDc * 2);
+        lds_dma16_s(row, lane16, &s_ckv[buf][(kKeysPerWave * w + k) * kCkvStride]);
       }
+      // kpe rows of the 8 keys: lanes 8k .. 8k+7 move key k (lane i lands in slot i)
+      const uint32_t chunk16 = (uint32_t)(lane & 7) * 16;
+#pragma unroll
+      for (int k = 0; k < kKeysPerWave; ++k)
+        if ((lane >> 3) == k)
+          lds_dma16_s(reinterpret_cast<const char*>(a.kpe) + (size_t)tok_next[k] * (kDp * 2), chunk16,
+                      &s_kpe[buf][kKeysPerWave * w * kKpeChunks]);
     };
 
     // O^T accumulators: tile (dblk, n) holds rows j -> dim dblk*128 + 8*j + n, cols = heads
@@ -207,13 +219,18 @@ __global__ __launch_bounds__(256) void mla_prefill_kernel(MlaArgs a, int n_tiles
 
       // ---- S^T for two 16-key halves
       f32x4_t st[2];
-      const uint4* kv = s_kv[buf];
+      const uint4* ckv = s_ckv[buf];
+      const uint4* kpe = s_kpe[buf];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const uint4* row = kv + (hf * 16 + hq) * kRowStride;  // A: key row (l%16), dims (l/16)*8..
+        // A: key row (l%16), dims (l/16)*8.. of each k-step
+        const uint4* crow = ckv + (hf * 16 + hq) * kCkvStride;
+        const uint4* prow = kpe + (hf * 16 + hq) * kKpeChunks;
 #pragma unroll
-        for (int s = 0; s < 18; ++s) c = mfma16x16x32(row[s * 4 + g], qb[s], c);
+        for (int s = 0; s < 16; ++s) c = mfma16x16x32(crow[s * 4 + g], qb[s], c);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) c = mfma16x16x32(prow[s * 4 + g], qb[16 + s], c);
         st[hf] = c;
       }
       // lane holds keys key0 + hf*16 + 4g + i for head hq
@@ -257,7 +274,7 @@ __global__ __launch_bounds__(256) void mla_prefill_kernel(MlaArgs a, int n_tiles
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int key = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
-          vv[e] = kv[key * kRowStride + dblk * 16 + hq];  // dims dblk*128 + 8*hq .. +8
+          vv[e] = ckv[key * kCkvStride + dblk * 16 + hq];  // dims dblk*128 + 8*hq .. +8
         }
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
