@@ -60,8 +60,8 @@ struct Bf16Smem {
   __attribute__((aligned(16))) uint16_t p_lds[W][G][16];  // bf16 P of the current page
 };
 
-// Processes work items first_item, first_item + gridDim.x, ... (DENSE: numbered by the
-// work list; otherwise the single partition-major item first_item). While an item runs,
+// Processes the workgroup's work items (DENSE: wg_item(.., blockIdx.x, gridDim.x, k) for
+// k = 0, 1, ... of the work list; otherwise the single partition-major item first_item). While an item runs,
 // the page ids and length of the workgroup's next item are fetched, and its query rows go
 // to the other LDS buffer by DMA while the waves merge, so moving to the next item costs no
 // memory round trip before its first K/V pages go out.
@@ -147,7 +147,7 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();  // q of the first item is visible
 
-  int item = first_item;
+  int k_item = 0;
   int slot = 0;
   for (;;) {
     // ---- the prefetched item becomes current
@@ -199,10 +199,11 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
     issue_v(0);
 
     // ---- prefetch of the workgroup's next item
-    item += (int)gridDim.x;
-    const bool has_next = DENSE && item < wl.n_items;
+    ++k_item;
+    const int next_item = DENSE ? wg_item(wl, blockIdx.x, gridDim.x, k_item) : -1;
+    const bool has_next = next_item >= 0;
     if (has_next) {
-      item_of(item, nb, nkvh, np);
+      item_of(next_item, nb, nkvh, np);
       npid = page_ids(nb, np, 0);
       nlen = len_of(nb);
     }
@@ -439,7 +440,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(bf16_min
     __shared__ int s_wave[2 * W];
     const DenseItems wl = build_worklist<64 * W>(a.lens, a.S, a.mb * 16, a.ps, a.KVH, s_worklist, s_wave);
     write_sentinels(wl, a.H, grid_parts, a.P, a.m, a.l);
-    if ((int)blockIdx.x < wl.n_items) bf16_items<D, G, XP, W, true>(a, wl, blockIdx.x, sm);
+    const int first = wg_item(wl, blockIdx.x, gridDim.x, 0);
+    if (first >= 0) bf16_items<D, G, XP, W, true>(a, wl, first, sm);
   } else {
     bf16_items<D, G, XP, W, false>(a, DenseItems{}, blockIdx.x, sm);
   }

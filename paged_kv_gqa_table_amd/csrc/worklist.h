@@ -126,6 +126,18 @@ PKV_DEVICE void decode_item(const DenseItems& it, int item, int& b, int& kvh, in
   }
 }
 
+// The k-th item of workgroup s in a grid of R workgroups, or -1 past its last one. Full
+// items go round-robin (s + k R); the partial items then go first to the workgroups that
+// got one full item fewer, so that no workgroup carries a whole extra item.
+PKV_DEVICE int wg_item(const DenseItems& it, int s, int R, int k) {
+  const int F = it.n_full;
+  const int nf = s < F ? (F - s + R - 1) / R : 0;  // full items of workgroup s
+  if (k < nf) return s + k * R;
+  const int first = F % R;  // the first workgroup with one full item fewer
+  const int item = F + ((s - first) % R + R) % R + (k - nf) * R;
+  return item < it.n_items ? item : -1;
+}
+
 // Sentinel m = -inf, l = 0 for every (b, h, p) with ceil(len_b / ps) <= p < grid_parts,
 // spread over the whole grid (one pass, grid-stride).
 PKV_DEVICE void write_sentinels(const DenseItems& it, int H, int grid_parts, int P, float* m, float* l) {
