@@ -25,9 +25,11 @@
 //  * S^T = K . Q^T with v_mfma_f32_16x16x32_bf16: A = a K row slice read from LDS, B = the
 //    wave's Q^T kept in registers for the whole key loop (18 k-steps over 576 dims).
 //  * The S^T accumulator layout (lane = head, 4 keys per lane) is exactly the B operand
-//    of O^T = V^T . P^T, so P never moves. V^T operands are built from 16-byte LDS reads
-//    of 8 consecutive dims of 8 keys with byte permutes: output tile n of a 128-dim block
-//    holds dims 8 * row + n, which makes each lane's V chunk feed 8 tiles.
+//    of O^T = V^T . P^T, so P never moves. V^T operands (16 consecutive dims x 8 keys per
+//    16-lane group) come straight from the row-major ckv tile through gfx950's transposing
+//    LDS read (ds_read_b64_tr_b16): inside a 16-lane group, source lane 4k + q points at 4
+//    dims (4q .. 4q+3) of key k, and lane j receives dim j of keys 0..3. Two such reads
+//    give a lane its 8 keys, with no permutes in registers.
 //  * Softmax in base 2 (sm_scale * log2 e folded into one multiply), so lse comes out in
 //    base 2 directly. The per-head max is reduced across the 4 lanes of a head with
 //    lane permutes; l and O are re-based lazily (only when the max outgrows the
@@ -61,6 +63,14 @@ PKV_DEVICE f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
 
 PKV_DEVICE void vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+// Transposing 8-byte LDS read (see the header comment for the lane mapping).
+PKV_DEVICE uint2 lds_read_tr16(const void* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(
+      (__attribute__((address_space(3))) void*)p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 // 16 bytes per lane from global memory (scalar base + per-lane offset) straight into LDS
 // (lane i -> lds_base + 16 i; lanes outside the exec mask move nothing).
 PKV_DEVICE void lds_dma16_s(const void* sbase, uint32_t voff, void* lds_base) {
@@ -68,12 +78,6 @@ PKV_DEVICE void lds_dma16_s(const void* sbase, uint32_t voff, void* lds_base) {
                                    (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
-// Element e (0..7) of two 16-byte bf16 chunks, paired as (x[e], y[e]).
-PKV_DEVICE uint32_t pick_pair(const uint4& x, const uint4& y, int e) {
-  const uint32_t xa = e < 2 ? x.x : e < 4 ? x.y : e < 6 ? x.z : x.w;
-  const uint32_t ya = e < 2 ? y.x : e < 4 ? y.y : e < 6 ? y.z : y.w;
-  return (e & 1) ? pair_hi(xa, ya) : pair_lo(xa, ya);
-}
 
 }  // namespace
 
@@ -195,7 +199,7 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
                       &s_kpe[buf][kKeysPerWave * w * kKpeChunks]);
     };
 
-    // O^T accumulators: tile (dblk, n) holds rows j -> dim dblk*128 + 8*j + n, cols = heads
+    // O^T accumulators: tile n holds rows j -> dim 16 n + j, cols = heads
     f32x4_t acc[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -267,21 +271,16 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
       const uint4 pb = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                   pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
 
-      // ---- O^T += V^T P^T over 4 blocks of 128 dims
+      // ---- O^T += V^T P^T over 32 blocks of 16 dims. This lane is source lane 4k + q of
+      // its group: it points at dims 16 n + 4 q .. +3 of keys 4g + k (k-slots 0..3 of the
+      // group) and 16 + 4g + k (k-slots 4..7), the key order of P^T.
+      const char* vrow_lo = reinterpret_cast<const char*>(ckv + (4 * g + (hq >> 2)) * kCkvStride) + (hq & 3) * 8;
+      const char* vrow_hi = reinterpret_cast<const char*>(ckv + (16 + 4 * g + (hq >> 2)) * kCkvStride) + (hq & 3) * 8;
 #pragma unroll
-      for (int dblk = 0; dblk < 4; ++dblk) {
-        uint4 vv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
-          vv[e] = ckv[key * kCkvStride + dblk * 16 + hq];  // dims dblk*128 + 8*hq .. +8
-        }
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const uint4 av = make_uint4(pick_pair(vv[0], vv[1], n), pick_pair(vv[2], vv[3], n),
-                                      pick_pair(vv[4], vv[5], n), pick_pair(vv[6], vv[7], n));
-          acc[dblk * 8 + n] = mfma16x16x32(av, pb, acc[dblk * 8 + n]);
-        }
+      for (int n = 0; n < 32; ++n) {
+        const uint2 lo = lds_read_tr16(vrow_lo + n * 32);
+        const uint2 hi = lds_read_tr16(vrow_hi + n * 32);
+        acc[n] = mfma16x16x32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[n]);
       }
     }
 
@@ -291,19 +290,15 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
     if (has_row) {
       const bool any = lsum > 0.f;
       const float inv = any ? 1.f / lsum : 0.f;
-      // lane: head hq, rows j = 4g + i of every tile -> dims dblk*128 + 8*(4g+i) + n
+      // lane: head hq, rows 4g .. 4g+3 of tile n -> dims 16 n + 4 g .. +3
       uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((size_t)r * kH + hq) * kDc;
 #pragma unroll
-      for (int dblk = 0; dblk < 4; ++dblk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint4 o;
-          o.x = pack_bf16x2(acc[dblk * 8 + 0][i] * inv, acc[dblk * 8 + 1][i] * inv);
-          o.y = pack_bf16x2(acc[dblk * 8 + 2][i] * inv, acc[dblk * 8 + 3][i] * inv);
-          o.z = pack_bf16x2(acc[dblk * 8 + 4][i] * inv, acc[dblk * 8 + 5][i] * inv);
-          o.w = pack_bf16x2(acc[dblk * 8 + 6][i] * inv, acc[dblk * 8 + 7][i] * inv);
-          *reinterpret_cast<uint4*>(orow + dblk * 128 + 8 * (4 * g + i)) = o;
-        }
+      for (int n = 0; n < 32; ++n) {
+        uint2 o;
+        o.x = pack_bf16x2(acc[n][0] * inv, acc[n][1] * inv);
+        o.y = pack_bf16x2(acc[n][2] * inv, acc[n][3] * inv);
+        *reinterpret_cast<uint2*>(orow + 16 * n + 4 * g) = o;
+      }
       if (g == 0) a.lse[(size_t)r * kH + hq] = any ? m_ref + __log2f(lsum) : kNegInf;
     }
     __syncthreads();  // LDS buffers are reused by the next tile of work
