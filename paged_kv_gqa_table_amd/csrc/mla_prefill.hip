@@ -48,18 +48,32 @@ constexpr int kQT = 4;          // query tokens per workgroup (one per wave)
 constexpr int kKT = 32;         // keys per tile
 constexpr int kCkvChunks = kDc * 2 / 16;     // 64 16-byte chunks of a ckv row
 constexpr int kKpeChunks = kDp * 2 / 16;     // 8 chunks of a kpe row
-constexpr int kCkvStride = kCkvChunks + 1;   // padded LDS row (chunks): spreads banks
+constexpr int kCkvStride = kCkvChunks + 2;   // padded LDS row (chunks), see ckv_swz
 constexpr int kKeysPerWave = kKT / kQT;      // 8 keys of a tile gathered by each wave
 constexpr int kMaxBatch = 512;
 constexpr float kMlaRebase = 8.f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int ids8_t __attribute__((ext_vector_type(8), aligned(4)));  // 8 page ids, dword aligned
 
 PKV_DEVICE f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                  c, 0, 0, 0);
 }
+
+// LDS bank spreading. A ckv row r sits at stride kCkvStride (32 B past a multiple of
+// 1 KiB) with 16-byte chunk c at position c ^ ckv_swz(r). The logits read 16 B per lane
+// from 16 consecutive rows at one chunk; the padding puts rows on even chunk offsets and
+// the swizzle moves every other group of 4 rows to the odd ones, so any 8 (or 16) rows
+// land on distinct chunks of a 128-byte (256-byte) bank line. The transposing V reads
+// take 32 B from each of 4 (8) consecutive rows; the padding alone keeps those apart and
+// the swizzle, which only flips chunk bit 0, never splits a 32-byte pair.
+PKV_DEVICE uint32_t ckv_swz(int r) { return (uint32_t)(((r >> 2) ^ (r >> 3)) & 1); }
+// kpe rows are packed (128 B) because one transfer fills 8 of them; chunk c of row r sits
+// at position c ^ kpe_swz(r), which sends the 8 (16) rows of a logits read to distinct
+// chunks of a bank line.
+PKV_DEVICE uint32_t kpe_swz(int r) { return (uint32_t)((r & 7) ^ ((r >> 3) & 1)); }
 
 PKV_DEVICE void vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -72,10 +86,15 @@ PKV_DEVICE uint2 lds_read_tr16(const void* p) {
 }
 
 // 16 bytes per lane from global memory (scalar base + per-lane offset) straight into LDS
-// (lane i -> lds_base + 16 i; lanes outside the exec mask move nothing).
-PKV_DEVICE void lds_dma16_s(const void* sbase, uint32_t voff, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(reinterpret_cast<const char*>(sbase) + voff),
-                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+// (lane i -> lds_base + 16 i; lanes outside the exec mask move nothing). Written as inline
+// assembly so the compiler does not see an LDS write: with the builtin it waits for every
+// outstanding transfer before each later LDS read, which would stall the math on tile kt
+// until tile kt + 1 has landed. The kernel itself waits (vmcnt(0)) and then barriers
+// before any wave reads a buffer that a transfer filled.
+PKV_DEVICE void lds_dma16_s(const void* sbase, uint32_t voff, const void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase) : "m0");
 }
 
 
@@ -168,34 +187,52 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
 #pragma unroll
       for (int s = 0; s < 18; ++s) qb[s] = make_uint4(0, 0, 0, 0);
     }
+    // Q must be in registers before the key loop: the compiler cannot see the tile
+    // transfers, so a wait it placed for Q inside the loop would also wait for them.
+#pragma unroll
+    for (int s = 0; s < 18; ++s) asm volatile("" ::"v"(qb[s].x), "v"(qb[s].y), "v"(qb[s].z), "v"(qb[s].w));
 
     // ---- gather of one key tile into LDS buffer `buf`: wave w moves keys 8w .. 8w+7 of the
     // tile (keys past the workgroup's last one re-read its last key; they are masked). The
-    // page ids of tile kt+1 are read through the scalar cache during tile kt.
+    // page ids of tile kt+2 are read through the scalar cache at the end of tile kt, so the
+    // read completes under the wait for tile kt+1's transfers.
     const __attribute__((address_space(4))) int32_t* ids =
         (const __attribute__((address_space(4))) int32_t*)(a.kv_indices + k0);
     int tok_next[kKeysPerWave];
     auto load_ids = [&](int kt) {
-      const int last = n_keys > 0 ? n_keys - 1 : 0;
+      const int first = kt * kKT + kKeysPerWave * w;
+      int t[kKeysPerWave];
+      if (first + kKeysPerWave <= n_keys) {  // uniform: all 8 ids exist, one 32-byte scalar load
+        const ids8_t v = *reinterpret_cast<const __attribute__((address_space(4))) ids8_t*>(ids + first);
 #pragma unroll
-      for (int k = 0; k < kKeysPerWave; ++k) {
-        const int t = ids[min(kt * kKT + kKeysPerWave * w + k, last)];
-        tok_next[k] = t < 0 ? 0 : (t >= a.num_pages ? a.num_pages - 1 : t);
+        for (int k = 0; k < kKeysPerWave; ++k) t[k] = v[k];
+      } else {  // the workgroup's last tile: keys past its last one re-read that key
+        const int last = n_keys > 0 ? n_keys - 1 : 0;
+#pragma unroll
+        for (int k = 0; k < kKeysPerWave; ++k) t[k] = ids[min(first + k, last)];
       }
+#pragma unroll
+      for (int k = 0; k < kKeysPerWave; ++k) tok_next[k] = t[k];  // clamped when used
     };
-    const uint32_t lane16 = (uint32_t)lane * 16;
+    // LDS position i of a ckv row holds global chunk i ^ ckv_swz(row)
     auto issue_tile = [&](int buf) {
+      int tok[kKeysPerWave];
+#pragma unroll
+      for (int k = 0; k < kKeysPerWave; ++k)
+        tok[k] = tok_next[k] < 0 ? 0 : (tok_next[k] >= a.num_pages ? a.num_pages - 1 : tok_next[k]);
 #pragma unroll
       for (int k = 0; k < kKeysPerWave; ++k) {
-        const char* row = reinterpret_cast<const char*>(a.ckv) + (size_t)tok_next[k] * (kDc * 2);
-        lds_dma16_s(row, lane16, &s_ckv[buf][(kKeysPerWave * w + k) * kCkvStride]);
+        const int row_k = kKeysPerWave * w + k;
+        const char* row = reinterpret_cast<const char*>(a.ckv) + (size_t)tok[k] * (kDc * 2);
+        lds_dma16_s(row, (uint32_t)(lane ^ ckv_swz(row_k)) * 16, &s_ckv[buf][row_k * kCkvStride]);
       }
-      // kpe rows of the 8 keys: lanes 8k .. 8k+7 move key k (lane i lands in slot i)
-      const uint32_t chunk16 = (uint32_t)(lane & 7) * 16;
+      // kpe rows of the 8 keys: lanes 8k .. 8k+7 move key k (lane i lands in slot i, i.e.
+      // position i & 7 of row 8w + k, and loads global chunk (i & 7) ^ kpe_swz(8w + k))
+      const uint32_t chunk16 = (uint32_t)((lane & 7) ^ kpe_swz(kKeysPerWave * w + (lane >> 3))) * 16;
 #pragma unroll
       for (int k = 0; k < kKeysPerWave; ++k)
         if ((lane >> 3) == k)
-          lds_dma16_s(reinterpret_cast<const char*>(a.kpe) + (size_t)tok_next[k] * (kDp * 2), chunk16,
+          lds_dma16_s(reinterpret_cast<const char*>(a.kpe) + (size_t)tok[k] * (kDp * 2), chunk16,
                       &s_kpe[buf][kKeysPerWave * w * kKpeChunks]);
     };
 
@@ -214,74 +251,75 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
       const int buf = kt & 1;
       vmcnt0();
       __syncthreads();  // tile kt landed in LDS; everyone is done with tile kt-1
-      if (kt + 1 < n_kt) {
-        issue_tile(buf ^ 1);
-        if (kt + 2 < n_kt) load_ids(kt + 2);
-      }
+      if (kt + 1 < n_kt) issue_tile(buf ^ 1);
       const int key0 = kt * kKT;
-      if (key0 >= vis) continue;  // uniform: this wave's row sees none of these keys
-
-      // ---- S^T for two 16-key halves
-      f32x4_t st[2];
-      const uint4* ckv = s_ckv[buf];
-      const uint4* kpe = s_kpe[buf];
+      if (key0 < vis) {  // uniform: else this wave's row sees none of these keys
+        // ---- S^T for two 16-key halves
+        f32x4_t st[2];
+        const uint4* ckv = s_ckv[buf];
+        const uint4* kpe = s_kpe[buf];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        // A: key row (l%16), dims (l/16)*8.. of each k-step
-        const uint4* crow = ckv + (hf * 16 + hq) * kCkvStride;
-        const uint4* prow = kpe + (hf * 16 + hq) * kKpeChunks;
+        for (int hf = 0; hf < 2; ++hf) {
+          f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          // A: key row (l%16), dims (l/16)*8.. of each k-step
+          const uint4* crow = ckv + (hf * 16 + hq) * kCkvStride + (g ^ ckv_swz(hq));
+          const uint4* prow = kpe + (hf * 16 + hq) * kKpeChunks;
 #pragma unroll
-        for (int s = 0; s < 16; ++s) c = mfma16x16x32(crow[s * 4 + g], qb[s], c);
+          for (int s = 0; s < 16; ++s) c = mfma16x16x32(crow[s * 4], qb[s], c);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) c = mfma16x16x32(prow[s * 4 + g], qb[16 + s], c);
-        st[hf] = c;
-      }
-      // lane holds keys key0 + hf*16 + 4g + i for head hq
-      float x[8];
-      float tmax = kNegInf;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kj = key0 + hf * 16 + 4 * g + i;
-          const float v = (kj < vis) ? st[hf][i] * a.sm_scale_log2 : kNegInf;
-          x[hf * 4 + i] = v;
-          tmax = fmaxf(tmax, v);
+          for (int s = 0; s < 2; ++s) c = mfma16x16x32(prow[(s * 4 + g) ^ kpe_swz(hq)], qb[16 + s], c);
+          st[hf] = c;
         }
-      tmax = fmaxf(tmax, xor_lanes(tmax, 16));
-      tmax = fmaxf(tmax, xor_lanes(tmax, 32));
-      m_true = fmaxf(m_true, tmax);
-      const bool rebase = m_true > m_ref + kMlaRebase;  // also true on the first tile (m_ref = -inf)
-      if (__builtin_amdgcn_ballot_w64(rebase) != 0) {   // wave-uniform branch
-        const float nref = rebase ? m_true : m_ref;
-        const float alpha = fast_exp2(m_ref - nref);
-        m_ref = nref;
-        lsum *= alpha;
+        // lane holds keys key0 + hf*16 + 4g + i for head hq
+        float x[8];
+        float tmax = kNegInf;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i] *= alpha;
-      }
-      float p[8];
+        for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = fast_exp2(x[e] - m_ref);
-        lsum += p[e];
-      }
-      // P^T as the B operand: k-slot e <-> key (e < 4 ? 4g + e : 16 + 4g + e - 4)
-      const uint4 pb = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                  pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+          for (int i = 0; i < 4; ++i) {
+            const int kj = key0 + hf * 16 + 4 * g + i;
+            const float v = (kj < vis) ? st[hf][i] * a.sm_scale_log2 : kNegInf;
+            x[hf * 4 + i] = v;
+            tmax = fmaxf(tmax, v);
+          }
+        tmax = fmaxf(tmax, xor_lanes(tmax, 16));
+        tmax = fmaxf(tmax, xor_lanes(tmax, 32));
+        m_true = fmaxf(m_true, tmax);
+        const bool rebase = m_true > m_ref + kMlaRebase;  // also true on the first tile (m_ref = -inf)
+        if (__builtin_amdgcn_ballot_w64(rebase) != 0) {   // wave-uniform branch
+          const float nref = rebase ? m_true : m_ref;
+          const float alpha = fast_exp2(m_ref - nref);
+          m_ref = nref;
+          lsum *= alpha;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) acc[i] *= alpha;
+        }
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(x[e] - m_ref);
+          lsum += p[e];
+        }
+        // P^T as the B operand: k-slot e <-> key (e < 4 ? 4g + e : 16 + 4g + e - 4)
+        const uint4 pb = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                    pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
 
-      // ---- O^T += V^T P^T over 32 blocks of 16 dims. This lane is source lane 4k + q of
-      // its group: it points at dims 16 n + 4 q .. +3 of keys 4g + k (k-slots 0..3 of the
-      // group) and 16 + 4g + k (k-slots 4..7), the key order of P^T.
-      const char* vrow_lo = reinterpret_cast<const char*>(ckv + (4 * g + (hq >> 2)) * kCkvStride) + (hq & 3) * 8;
-      const char* vrow_hi = reinterpret_cast<const char*>(ckv + (16 + 4 * g + (hq >> 2)) * kCkvStride) + (hq & 3) * 8;
+        // ---- O^T += V^T P^T over 32 blocks of 16 dims. This lane is source lane 4k + q of
+        // its group: it points at dims 16 n + 4 q .. +3 of keys 4g + k (k-slots 0..3 of the
+        // group) and 16 + 4g + k (k-slots 4..7), the key order of P^T.
+        // (rows r and r + 16 share ckv_swz(r); chunk 2n + ((hq >> 1) & 1) sits at 2n + that ^ swz)
+        const int vr = 4 * g + (hq >> 2);
+        const int vcol = (int)((((uint32_t)hq >> 1) & 1) ^ ckv_swz(vr)) * 16 + (hq & 1) * 8;
+        const char* vrow_lo = reinterpret_cast<const char*>(ckv + vr * kCkvStride) + vcol;
+        const char* vrow_hi = reinterpret_cast<const char*>(ckv + (16 + vr) * kCkvStride) + vcol;
 #pragma unroll
-      for (int n = 0; n < 32; ++n) {
-        const uint2 lo = lds_read_tr16(vrow_lo + n * 32);
-        const uint2 hi = lds_read_tr16(vrow_hi + n * 32);
-        acc[n] = mfma16x16x32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[n]);
+        for (int n = 0; n < 32; ++n) {
+          const uint2 lo = lds_read_tr16(vrow_lo + n * 32);
+          const uint2 hi = lds_read_tr16(vrow_hi + n * 32);
+          acc[n] = mfma16x16x32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[n]);
+        }
       }
+      if (kt + 2 < n_kt) load_ids(kt + 2);
     }
 
     // ---- finish: total l per head over the 4 lanes of the column, normalize, store
