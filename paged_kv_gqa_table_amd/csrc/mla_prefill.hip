@@ -9,19 +9,20 @@
 //
 // gfx950 design (not the page's: it recomputes the 576-wide logits once per 512-dim
 // output slice and runs two passes; here it is one pass with an online softmax):
-//  * A workgroup is 4 waves = 4 consecutive query tokens of one batch; a wave owns the
-//    16 heads of its token (16 MFMA rows). Tiles are handed out last-first inside each
-//    batch so the longest causal rows start early.
+//  * A workgroup is kQT = 8 waves = 8 consecutive query tokens of one batch; a wave owns
+//    the 16 heads of its token (16 MFMA rows). Tiles are handed out last-first inside
+//    each batch so the longest causal rows start early. One workgroup fills a CU (two
+//    waves per SIMD, 256 registers each: 128 hold the wave's O).
 //  * Keys come in tiles of 32: the 32 [ckv | kpe] rows (1152 B each) are gathered through
 //    kv_indices straight into LDS with global_load_lds_dwordx4 (no staging registers),
-//    double-buffered. Each wave moves 8 keys: one transfer per key for its 1 KiB ckv row
-//    (scalar address, page id from the scalar cache) and 8 lane-masked transfers for the
-//    8 keys' kpe rows, so the gather costs almost no vector instructions. ckv rows sit at
-//    a padded LDS stride; kpe rows are packed.
-//  * The compiler waits for an LDS transfer before the next LDS read (it cannot tell the
-//    two buffers apart), so within a workgroup a tile's gather is not overlapped with the
-//    previous tile's math. Instead the kernel is held to 256 registers so that two
-//    workgroups share a CU and cover each other's gathers.
+//    double-buffered. Each wave moves 4 keys: one transfer per key for its 1 KiB ckv row
+//    (scalar address, page ids from one scalar load) and lane-masked transfers for the
+//    keys' kpe rows, so the gather costs almost no vector instructions.
+//  * The gather rate a CU sustains is the limit (more tiles in flight do not help; fewer
+//    bytes per token do), so as many tokens as the register file allows share each
+//    gathered tile. The transfers are issued as inline assembly, invisible to the
+//    compiler's wait insertion, so tile kt+1 lands while tile kt is computed; the kernel
+//    waits for them itself before the barrier that publishes a buffer.
 //  * S^T = K . Q^T with v_mfma_f32_16x16x32_bf16: A = a K row slice read from LDS, B = the
 //    wave's Q^T kept in registers for the whole key loop (18 k-steps over 576 dims).
 //  * The S^T accumulator layout (lane = head, 4 keys per lane) is exactly the B operand
@@ -44,18 +45,27 @@ namespace {
 constexpr int kH = 16;          // heads (MFMA rows / cols)
 constexpr int kDc = 512;        // ckv dims (also V dims)
 constexpr int kDp = 64;         // kpe dims
-constexpr int kQT = 4;          // query tokens per workgroup (one per wave)
+#ifndef MLA_QT
+#define MLA_QT 8
+#endif
+#ifndef MLA_NBUF
+#define MLA_NBUF 2
+#endif
+constexpr int kQT = MLA_QT;     // query tokens per workgroup (one per wave)
+constexpr int kNT = kQT * 64;   // threads per workgroup
+constexpr int kNumBuf = MLA_NBUF;  // LDS key-tile buffers (kNumBuf - 1 tiles in flight)
 constexpr int kKT = 32;         // keys per tile
 constexpr int kCkvChunks = kDc * 2 / 16;     // 64 16-byte chunks of a ckv row
 constexpr int kKpeChunks = kDp * 2 / 16;     // 8 chunks of a kpe row
 constexpr int kCkvStride = kCkvChunks + 2;   // padded LDS row (chunks), see ckv_swz
-constexpr int kKeysPerWave = kKT / kQT;      // 8 keys of a tile gathered by each wave
+constexpr int kKeysPerWave = kKT / kQT;      // keys of a tile gathered by each wave
+static_assert((kNumBuf & (kNumBuf - 1)) == 0 && kNumBuf >= 2 && kKeysPerWave * kQT == kKT, "tile shape");
 constexpr int kMaxBatch = 512;
 constexpr float kMlaRebase = 8.f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef int ids8_t __attribute__((ext_vector_type(8), aligned(4)));  // 8 page ids, dword aligned
+typedef int idsv_t __attribute__((ext_vector_type(kKeysPerWave), aligned(4)));  // a wave's page ids
 
 PKV_DEVICE f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
@@ -76,6 +86,9 @@ PKV_DEVICE uint32_t ckv_swz(int r) { return (uint32_t)(((r >> 2) ^ (r >> 3)) & 1
 PKV_DEVICE uint32_t kpe_swz(int r) { return (uint32_t)((r & 7) ^ ((r >> 3) & 1)); }
 
 PKV_DEVICE void vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits until at most N transfers of this wave are outstanding.
+template <int N>
+PKV_DEVICE void vmcnt_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 // Transposing 8-byte LDS read (see the header comment for the lane mapping).
@@ -100,12 +113,12 @@ PKV_DEVICE void lds_dma16_s(const void* sbase, uint32_t voff, const void* lds_ba
 
 }  // namespace
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))  // 2 workgroups per CU
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2)))  // 2 waves per SIMD
 void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
-  __shared__ __attribute__((aligned(16))) uint4 s_ckv[2][kKT * kCkvStride];
-  __shared__ __attribute__((aligned(16))) uint4 s_kpe[2][kKT * kKpeChunks];
+  __shared__ __attribute__((aligned(16))) uint4 s_ckv[kNumBuf][kKT * kCkvStride];
+  __shared__ __attribute__((aligned(16))) uint4 s_kpe[kNumBuf][kKT * kKpeChunks];
   __shared__ int s_tiles[kMaxBatch + 1];  // exclusive prefix of query tiles per batch
-  __shared__ int s_wave[4];
+  __shared__ int s_wave[kQT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -114,7 +127,7 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
 
   // ---- tile list: tiles of kQT query tokens, per batch
   {
-    const int per = (B + 255) / 256;
+    const int per = (B + kNT - 1) / kNT;
     const int i0 = tid * per;
     int local = 0;
     for (int i = i0; i < i0 + per && i < B; ++i) {
@@ -137,7 +150,11 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
       const int ql = a.qo_indptr[i + 1] - a.qo_indptr[i];
       run += ql > 0 ? (ql + kQT - 1) / kQT : 0;
     }
-    if (tid == 0) s_tiles[B] = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+    if (tid == 0) {
+      int total = 0;
+      for (int v = 0; v < kQT; ++v) total += s_wave[v];
+      s_tiles[B] = total;
+    }
     __syncthreads();
   }
   const int n_tiles = s_tiles[B];
@@ -202,8 +219,8 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
     auto load_ids = [&](int kt) {
       const int first = kt * kKT + kKeysPerWave * w;
       int t[kKeysPerWave];
-      if (first + kKeysPerWave <= n_keys) {  // uniform: all 8 ids exist, one 32-byte scalar load
-        const ids8_t v = *reinterpret_cast<const __attribute__((address_space(4))) ids8_t*>(ids + first);
+      if (first + kKeysPerWave <= n_keys) {  // uniform: all ids exist, one scalar load
+        const idsv_t v = *reinterpret_cast<const __attribute__((address_space(4))) idsv_t*>(ids + first);
 #pragma unroll
         for (int k = 0; k < kKeysPerWave; ++k) t[k] = v[k];
       } else {  // the workgroup's last tile: keys past its last one re-read that key
@@ -242,16 +259,25 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
     for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_ref = kNegInf, m_true = kNegInf, lsum = 0.f;  // per head (lane's column)
 
-    if (n_kt > 0) {
-      load_ids(0);
-      issue_tile(0);
-      if (n_kt > 1) load_ids(1);
-    }
+    // tiles 0 .. kNumBuf-2 in flight before the loop; tile kt + kNumBuf - 1 is issued at
+    // the top of tile kt, into the buffer tile kt - 1 just released
+    constexpr int kPerTile = 2 * kKeysPerWave;  // transfers per wave and tile (ckv + kpe)
+#pragma unroll
+    for (int j = 0; j < kNumBuf - 1; ++j)
+      if (j < n_kt) {
+        load_ids(j);
+        issue_tile(j);
+      }
+    if (kNumBuf - 1 < n_kt) load_ids(kNumBuf - 1);
     for (int kt = 0; kt < n_kt; ++kt) {
-      const int buf = kt & 1;
-      vmcnt0();
+      const int buf = kt & (kNumBuf - 1);
+      // wait for this wave's transfers of tile kt; those of the later tiles may stay in flight
+      const int later = min(kNumBuf - 2, n_kt - 1 - kt);
+      if (kNumBuf >= 4 && later >= 2) vmcnt_le<(kNumBuf >= 4 ? 2 * kPerTile : 0)>();
+      else if (kNumBuf >= 3 && later >= 1) vmcnt_le<(kNumBuf >= 3 ? kPerTile : 0)>();
+      else vmcnt0();
       __syncthreads();  // tile kt landed in LDS; everyone is done with tile kt-1
-      if (kt + 1 < n_kt) issue_tile(buf ^ 1);
+      if (kt + kNumBuf - 1 < n_kt) issue_tile((kt + kNumBuf - 1) & (kNumBuf - 1));
       const int key0 = kt * kKT;
       if (key0 < vis) {  // uniform: else this wave's row sees none of these keys
         // ---- S^T for two 16-key halves
@@ -319,7 +345,7 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
           acc[n] = mfma16x16x32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[n]);
         }
       }
-      if (kt + 2 < n_kt) load_ids(kt + 2);
+      if (kt + kNumBuf < n_kt) load_ids(kt + kNumBuf);
     }
 
     // ---- finish: total l per head over the 4 lanes of the column, normalize, store
@@ -350,7 +376,7 @@ hipError_t launch_mla_prefill(const MlaArgs& a, hipStream_t s) {
   const int cap = dense_grid_cap();
   const int grid = (int)(bound < cap ? bound : cap);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_prefill_kernel, dim3(grid), dim3(256), 0, s, a, (int)bound);
+  hipLaunchKernelGGL(mla_prefill_kernel, dim3(grid), dim3(kNT), 0, s, a, (int)bound);
   return hipGetLastError();
 }
 
