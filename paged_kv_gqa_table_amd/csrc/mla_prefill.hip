@@ -281,20 +281,26 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
       const int key0 = kt * kKT;
       if (key0 < vis) {  // uniform: else this wave's row sees none of these keys
         // ---- S^T for two 16-key halves
-        f32x4_t st[2];
+        f32x4_t st[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
         const uint4* ckv = s_ckv[buf];
         const uint4* kpe = s_kpe[buf];
+        // A: key row (l%16) of each half, dims (l/16)*8.. of each k-step; the two halves'
+        // chains interleave so each LDS read has the other chain's MFMA to hide behind
+        const uint4* crow = ckv + hq * kCkvStride + (g ^ ckv_swz(hq));
+        const uint4* prow = kpe + hq * kKpeChunks;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          // A: key row (l%16), dims (l/16)*8.. of each k-step
-          const uint4* crow = ckv + (hf * 16 + hq) * kCkvStride + (g ^ ckv_swz(hq));
-          const uint4* prow = kpe + (hf * 16 + hq) * kKpeChunks;
+        for (int s = 0; s < 16; ++s) {
+          const uint4 a0 = crow[s * 4];
+          const uint4 a1 = crow[16 * kCkvStride + s * 4];
+          st[0] = mfma16x16x32(a0, qb[s], st[0]);
+          st[1] = mfma16x16x32(a1, qb[s], st[1]);
+        }
 #pragma unroll
-          for (int s = 0; s < 16; ++s) c = mfma16x16x32(crow[s * 4], qb[s], c);
-#pragma unroll
-          for (int s = 0; s < 2; ++s) c = mfma16x16x32(prow[(s * 4 + g) ^ kpe_swz(hq)], qb[16 + s], c);
-          st[hf] = c;
+        for (int s = 0; s < 2; ++s) {
+          const uint4 a0 = prow[(s * 4 + g) ^ kpe_swz(hq)];
+          const uint4 a1 = prow[16 * kKpeChunks + ((s * 4 + g) ^ kpe_swz(hq))];
+          st[0] = mfma16x16x32(a0, qb[16 + s], st[0]);
+          st[1] = mfma16x16x32(a1, qb[16 + s], st[1]);
         }
         // lane holds keys key0 + hf*16 + 4g + i for head hq
         float x[8];
