@@ -211,8 +211,7 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
 
     // ---- gather of one key tile into LDS buffer `buf`: wave w moves keys 8w .. 8w+7 of the
     // tile (keys past the workgroup's last one re-read its last key; they are masked). The
-    // page ids of tile kt+2 are read through the scalar cache at the end of tile kt, so the
-    // read completes under the wait for tile kt+1's transfers.
+    // page ids of tile kt+2 are read through the scalar cache during tile kt.
     const __attribute__((address_space(4))) int32_t* ids =
         (const __attribute__((address_space(4))) int32_t*)(a.kv_indices + k0);
     int tok_next[kKeysPerWave];
@@ -302,6 +301,9 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
           st[0] = mfma16x16x32(a0, qb[16 + s], st[0]);
           st[1] = mfma16x16x32(a1, qb[16 + s], st[1]);
         }
+        // next ids: the scalar load completes under the softmax (any later LDS wait would
+        // also wait for it)
+        if (kt + kNumBuf < n_kt) load_ids(kt + kNumBuf);
         // lane holds keys key0 + hf*16 + 4g + i for head hq
         float x[8];
         float tmax = kNegInf;
@@ -350,8 +352,9 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
           const uint2 hi = lds_read_tr16(vrow_hi + n * 32);
           acc[n] = mfma16x16x32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[n]);
         }
+      } else if (kt + kNumBuf < n_kt) {
+        load_ids(kt + kNumBuf);
       }
-      if (kt + kNumBuf < n_kt) load_ids(kt + kNumBuf);
     }
 
     // ---- finish: total l per head over the 4 lanes of the column, normalize, store
