@@ -10,8 +10,8 @@
 // gfx950 design (not the page's: it recomputes the 576-wide logits once per 512-dim
 // output slice and runs two passes; here it is one pass with an online softmax):
 //  * A workgroup is kQT = 8 waves = 8 consecutive query tokens of one batch; a wave owns
-//    the 16 heads of its token (16 MFMA rows). Tiles are handed out last-first inside
-//    each batch so the longest causal rows start early. One workgroup fills a CU (two
+//    the 16 heads of its token (16 MFMA rows). Tiles are handed out longest first (batches
+//    by KV length, last tile of a batch first). One workgroup fills a CU (two
 //    waves per SIMD, 256 registers each: 128 hold the wave's O).
 //  * Keys come in tiles of 32: the 32 [ckv | kpe] rows (1152 B each) are gathered through
 //    kv_indices straight into LDS with global_load_lds_dwordx4 (no staging registers),
@@ -117,7 +117,9 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2)))  //
 void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
   __shared__ __attribute__((aligned(16))) uint4 s_ckv[kNumBuf][kKT * kCkvStride];
   __shared__ __attribute__((aligned(16))) uint4 s_kpe[kNumBuf][kKT * kKpeChunks];
-  __shared__ int s_tiles[kMaxBatch + 1];  // exclusive prefix of query tiles per batch
+  __shared__ int s_tiles[kMaxBatch + 1];  // exclusive prefix of query tiles, by sorted position
+  __shared__ int s_border[kMaxBatch];     // batch at each sorted position
+  __shared__ int s_kvl[kMaxBatch];        // clamped kv_len per batch
   __shared__ int s_wave[kQT];
 
   const int tid = threadIdx.x;
@@ -125,12 +127,28 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
   const int w = uniform((int)(tid >> 6));
   const int B = a.batch;
 
-  // ---- tile list: tiles of kQT query tokens, per batch
+  // ---- tile list: tiles of kQT query tokens. Batches go longest KV first (ties by index)
+  // and, inside a batch, the last (longest) tile first, so the longest tiles start in the
+  // first wave of workgroups and the short ones fill in behind them.
   {
     const int per = (B + kNT - 1) / kNT;
     const int i0 = tid * per;
-    int local = 0;
     for (int i = i0; i < i0 + per && i < B; ++i) {
+      const int kl = a.kv_indptr[i + 1] - a.kv_indptr[i];
+      s_kvl[i] = kl < 0 ? 0 : kl;
+    }
+    __syncthreads();
+    for (int i = i0; i < i0 + per && i < B; ++i) {
+      const int ki = s_kvl[i];
+      int rank = 0;
+      for (int j = 0; j < B; ++j) rank += (s_kvl[j] > ki) || (s_kvl[j] == ki && j < i);
+      s_border[rank] = i;
+    }
+    __syncthreads();
+    // exclusive prefix of tile counts over the sorted positions
+    int local = 0;
+    for (int k = i0; k < i0 + per && k < B; ++k) {
+      const int i = s_border[k];
       const int ql = a.qo_indptr[i + 1] - a.qo_indptr[i];
       local += ql > 0 ? (ql + kQT - 1) / kQT : 0;
     }
@@ -145,8 +163,9 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
     int base = 0;
     for (int v = 0; v < w; ++v) base += s_wave[v];
     int run = base + x - local;
-    for (int i = i0; i < i0 + per && i < B; ++i) {
-      s_tiles[i] = run;
+    for (int k = i0; k < i0 + per && k < B; ++k) {
+      s_tiles[k] = run;
+      const int i = s_border[k];
       const int ql = a.qo_indptr[i + 1] - a.qo_indptr[i];
       run += ql > 0 ? (ql + kQT - 1) / kQT : 0;
     }
@@ -161,20 +180,21 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
   (void)n_tiles_bound;
 
   for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    // batch of this tile
+    // sorted position (then batch) of this tile
     int lo = 0, hi = B;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (s_tiles[mid] <= tile) lo = mid; else hi = mid;
     }
-    const int b = uniform(lo);
+    const int pos = uniform(lo);
+    const int b = uniform(s_border[pos]);
     const int q0 = a.qo_indptr[b], q1 = a.qo_indptr[b + 1];
     const int k0 = a.kv_indptr[b];
     const int q_len = q1 - q0;
     int kv_len = a.kv_indptr[b + 1] - k0;
     kv_len = kv_len < 0 ? 0 : kv_len;
-    const int nt_b = s_tiles[b + 1] - s_tiles[b];
-    const int t_in_b = uniform(nt_b - 1 - (tile - s_tiles[b]));  // last tile of the batch first
+    const int nt_b = s_tiles[pos + 1] - s_tiles[pos];
+    const int t_in_b = uniform(nt_b - 1 - (tile - s_tiles[pos]));  // last tile of the batch first
     const int i_tok = t_in_b * kQT + w;                             // this wave's query token
     const bool has_row = i_tok < q_len;
     const int r = q0 + i_tok;

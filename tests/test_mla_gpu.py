@@ -71,6 +71,23 @@ def test_mla_edge_lengths(q_lens, prefixes):
     check(o, l, ro, rl, "edge")
 
 
+@pytest.mark.parametrize("n_batch,seed", [(48, 21), (512, 22)])
+def test_mla_many_batches(n_batch, seed):
+    """Many batches, some without query rows, several with equal KV lengths: the tile order
+    (batches by KV length, ties by index) must still cover every row exactly once."""
+    rng = np.random.default_rng(seed)
+    q_lens = rng.integers(0, 20 if n_batch < 100 else 4, n_batch)
+    q_lens[::7] = 0
+    kv_lens = rng.choice([9, 40, 40, 77, 130], n_batch) + q_lens  # repeated lengths -> ties
+    kv_lens[1::5] = kv_lens[0]
+    prefixes = np.maximum(kv_lens - q_lens, 0)
+    say(f"mla many batches: B={n_batch} total_q={int(q_lens.sum())}")
+    case = inputs.make_mla(q_lens.tolist(), prefixes.tolist(), seed=seed, extra_pages=3)
+    o, l = run_gpu(case)
+    ro, rl = run_oracle(case)
+    check(o, l, ro, rl, f"B={n_batch}")
+
+
 def test_mla_empty_kv_and_canaries():
     """A batch with rows but no keys gives 0 / -inf; pages nobody references hold NaN."""
     base = inputs.make_mla([5, 3], [20, 0], seed=9, extra_pages=7)
