@@ -127,6 +127,27 @@ def bench_decode(case, steps, warmup, copies=0):
     )
 
 
+def read_ceiling(nbytes=1 << 30, reps=20):
+    """Median bandwidth of the library's plain streaming read over a buffer 4x the size of
+    the Infinity Cache (GB/s): the reference the paged gathers are compared with."""
+    import torch
+    import paged_kv_gqa_table_amd as pkv
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        pkv.read_bandwidth(buf, sink)
+    evs = [_events(2) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        pkv.read_bandwidth(buf, sink)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    del buf
+    torch.cuda.empty_cache()
+    return nbytes / (ms[len(ms) // 2] * 1e-3) / 1e9
+
+
 def bench_mla(case, steps, warmup):
     import torch
     import paged_kv_gqa_table_amd as pkv
@@ -296,6 +317,14 @@ def main():
                      "kernel_p10_us": r["partial_p10_ms"] * 1e3, "kernel_p90_us": r["partial_p90_ms"] * 1e3},
         "gpu_event_ms_per_step": r["gpu_ms_per_step"],
     }
+    # warm reference: one pool only, so part of the KV stays in the Infinity Cache between steps
+    rw = bench_decode(case, max(20, args.steps // 4), 5, copies=1)
+    result["warm_single_pool"] = {"us_per_step": rw["wall_ms_per_step"] * 1e3,
+                                  "GB_s": kv / (rw["wall_ms_per_step"] * 1e-3) / 1e9,
+                                  "kernel_avg_us": rw["partial_avg_ms"] * 1e3}
+    ceiling = read_ceiling()
+    result["roofline"]["measured_read_ceiling_GB_s"] = ceiling
+    result["roofline"]["frac_of_measured_read_ceiling"] = achieved / ceiling
     if not args.no_extra and args.workload == "llama_gqa4":
         extra = {}
         for name in ("wide_gqa6", "skewed_gqa8"):

@@ -36,6 +36,7 @@
 #ifndef PKV_H_
 #define PKV_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -158,6 +159,17 @@ int mla_paged_prefill(const void* q_nope, const void* q_pe,
                       int batch, int total_q, int max_q_len, int num_pages,
                       int num_heads, int ckv_dim, int kpe_dim, int page_size,
                       float sm_scale, void* out, float* lse, void* stream);
+
+/* Measurement helper, not part of the attention path: reads `bytes` bytes of device memory
+ * at `buf` once, as a plain streaming read (16-byte loads, grid-stride over the buffer), on
+ * `stream`. Timing it gives the read bandwidth the GPU sustains for the simplest access
+ * pattern, the reference point the decode kernels' paged gathers are compared with.
+ *   buf   device memory, 16-byte aligned; bytes a multiple of 16 (0: nothing to do)
+ *   sink  one uint32 of device memory, written only in a case that never arises in
+ *         practice (it keeps the loads from being optimised away); its value is unspecified
+ * PKV_EINVAL: NULL buf or sink with bytes > 0, misaligned buf, bytes not a multiple of 16.
+ * PKV_EHIP: the launch failed. */
+int pkv_read_bandwidth(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 /* Message for the calling thread's last non-OK status ("" if none). Never NULL. */
 const char* pkv_last_error(void);

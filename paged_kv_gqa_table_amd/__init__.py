@@ -11,7 +11,8 @@ Entry points (same names as the C ABI):
   paged_decode_reduce(...)    LSE-weighted combine of the partials
   mla_paged_prefill(...)      MLA causal paged prefill, page_size 1, base-2 LSE
 and the convenience wrapper paged_decode(...) that allocates the partials and runs both
-decode phases on the current stream.
+decode phases on the current stream. read_bandwidth(...) is a measurement helper (a
+plain streaming read of a buffer), not part of the attention path.
 """
 from __future__ import annotations
 
@@ -23,7 +24,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["paged_decode_partial", "paged_decode_reduce", "paged_decode", "mla_paged_prefill",
-           "lib", "library_path", "PkvError", "TOKEN_MAJOR", "XPACKED", "num_partitions"]
+           "read_bandwidth", "lib", "library_path", "PkvError", "TOKEN_MAJOR", "XPACKED", "num_partitions"]
 
 TOKEN_MAJOR = "token_major"
 XPACKED = "xpacked"
@@ -64,6 +65,8 @@ def lib() -> ctypes.CDLL:
     L.mla_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                     f32, vp, vp, vp]
     L.mla_paged_prefill.restype = i32
+    L.pkv_read_bandwidth.argtypes = [vp, ctypes.c_size_t, vp, vp]
+    L.pkv_read_bandwidth.restype = i32
     L.pkv_last_error.argtypes = []
     L.pkv_last_error.restype = ctypes.c_char_p
     L.pkv_version.argtypes = []
@@ -254,3 +257,15 @@ def mla_paged_prefill(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch
                                  _ptr(out), _ptr(lse), _stream(q_nope.device))
     _check(st, "mla_paged_prefill")
     return out, lse
+
+
+def read_bandwidth(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Read all of ``buf`` once on the current stream (plain streaming read; time it with
+    events for the read bandwidth). ``sink`` is a 1-element int32 device tensor the kernel
+    may write; its value is unspecified."""
+    _dev("buf", buf)
+    _dev("sink", sink, torch.int32)
+    if sink.numel() < 1:
+        raise ValueError("sink must hold at least one int32")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().pkv_read_bandwidth(_ptr(buf), nbytes, _ptr(sink), _stream(buf.device)), "pkv_read_bandwidth")

@@ -13,6 +13,7 @@
 
 #include "decode_args.h"
 #include "mla_args.h"
+#include "probe_args.h"
 
 namespace {
 
@@ -211,6 +212,15 @@ extern "C" int mla_paged_prefill(const void* q_nope, const void* q_pe, const voi
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
   a.out = out; a.lse = lse;
   return hip_status(pkv::launch_mla_prefill(a, reinterpret_cast<hipStream_t>(stream)), "mla_paged_prefill launch");
+}
+
+extern "C" int pkv_read_bandwidth(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return PKV_OK;
+  if (!buf || !sink) return fail(PKV_EINVAL, "pkv_read_bandwidth: NULL pointer argument");
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return fail(PKV_EINVAL, "pkv_read_bandwidth: buffer must be 16-byte aligned and a multiple of 16 bytes");
+  return hip_status(pkv::launch_read_probe(buf, bytes, sink, reinterpret_cast<hipStream_t>(stream)),
+                    "pkv_read_bandwidth launch");
 }
 
 extern "C" const char* pkv_last_error(void) { return g_last_error.c_str(); }

@@ -126,6 +126,18 @@ def test_mla_validation(L, kw, code):
     assert _mla(L, **kw) == code
 
 
+@pytest.mark.parametrize("buf,nbytes,sink,code", [
+    (None, 1024, FAKE, EINVAL),
+    (FAKE, 1024, None, EINVAL),
+    (FAKE, 1000, FAKE, EINVAL),        # not a multiple of 16
+    (ctypes.c_void_p(0x1008), 1024, FAKE, EINVAL),  # misaligned
+    (None, 0, None, OK),               # nothing to read
+])
+def test_read_bandwidth_validation(L, buf, nbytes, sink, code):
+    """The measurement helper rejects bad arguments before any HIP call."""
+    assert L.pkv_read_bandwidth(buf, nbytes, sink, None) == code
+
+
 def test_python_layer_maps_statuses(L):
     import torch
     with pytest.raises((ValueError, TypeError)):

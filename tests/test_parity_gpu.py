@@ -273,3 +273,15 @@ def test_many_sequences(S, dtype, D, H, KVH, layout):
         assert np.all(np.isfinite(g["m"][b, :, :nb])) and np.all(g["l"][b, :, :nb] >= 1.0 - 1e-6), f"b={b}"
         if nb == 0:
             assert np.all(g["out"][b] == 0.0) and np.all(np.isneginf(g["lse"][b])), f"empty b={b}"
+
+
+def test_read_bandwidth_helper():
+    """The streaming-read measurement helper runs on odd sizes and leaves the sink alone
+    (the fold of a buffer of ones never equals the kernel's marker value)."""
+    for n in (4, 4 * 1000 + 4, 1 << 22):
+        buf = torch.ones(n, dtype=torch.int32, device="cuda")
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        say(f"read_bandwidth: {n * 4} bytes")
+        pkv.read_bandwidth(buf, sink)
+        torch.cuda.synchronize()
+        assert int(sink.item()) == 0
