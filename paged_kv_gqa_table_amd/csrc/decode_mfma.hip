@@ -115,8 +115,8 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
     const char* kp = page_ptr(kbase, i);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if constexpr (XP) kr[s] = ld16(kp + ((s * 4 + g) * BS + hl) * 16);  // chunk (dims 32s+8g), token hl
-      else kr[s] = ld16(kp + hl * ROWB + (s * 32 + g * 8) * 2);
+      if constexpr (XP) kr[s] = ld16_kv(kp + ((s * 4 + g) * BS + hl) * 16);  // chunk (dims 32s+8g), token hl
+      else kr[s] = ld16_kv(kp + hl * ROWB + (s * 32 + g * 8) * 2);
     }
   };
   auto issue_v = [&](int i) {
@@ -128,7 +128,7 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int k = 0; k < NB; ++k) vt[j][k] = ld16(vp + (4 * g + j) * ROWB + (16 * k + hl) * 16);
+        for (int k = 0; k < NB; ++k) vt[j][k] = ld16_kv(vp + (4 * g + j) * ROWB + (16 * k + hl) * 16);
     }
   };
 

@@ -147,18 +147,18 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
 #pragma unroll
     for (int j = 0; j < TPL; ++j)
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) kr[j][k] = ld16(kp + k_off(tg + TPI * j, c + LPT * k));
+      for (int k = 0; k < CPL; ++k) kr[j][k] = ld16_kv(kp + k_off(tg + TPI * j, c + LPT * k));
   };
   auto issue_v = [&](int i) {
     const char* vp = page_ptr(vbase, i);
     if constexpr (XP) {
 #pragma unroll
-      for (int q = 0; q < NVC; ++q) vr[q] = ld16(vp + (size_t)(64 * q + lane) * 16);
+      for (int q = 0; q < NVC; ++q) vr[q] = ld16_kv(vp + (size_t)(64 * q + lane) * 16);
     } else {
 #pragma unroll
       for (int j = 0; j < TPL; ++j)
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) vr[j * CPL + k] = ld16(vp + k_off(tg + TPI * j, c + LPT * k));
+        for (int k = 0; k < CPL; ++k) vr[j * CPL + k] = ld16_kv(vp + k_off(tg + TPI * j, c + LPT * k));
     }
   };
 

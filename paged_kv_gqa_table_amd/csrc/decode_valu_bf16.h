@@ -179,19 +179,19 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int k = 0; k < KCPL; ++k) kr[j][k] = ld16(kp + k_off(kt + 8 * j, kc + 8 * k));
+        for (int k = 0; k < KCPL; ++k) kr[j][k] = ld16_kv(kp + k_off(kt + 8 * j, kc + 8 * k));
     };
     auto issue_v = [&](int i) {
       const char* vp = page_ptr(vbase, i);
       if constexpr (XP) {
 #pragma unroll
-        for (int q = 0; q < NVC; ++q) vr[q] = ld16(vp + (size_t)(64 * q + lane) * 16);
+        for (int q = 0; q < NVC; ++q) vr[q] = ld16_kv(vp + (size_t)(64 * q + lane) * 16);
       } else {
 #pragma unroll
         for (int j = 0; j < VT; ++j)
 #pragma unroll
           for (int k = 0; k < VCPL; ++k)
-            vr[j * VCPL + k] = ld16(vp + (vt + (64 / LV) * j) * ROWB + (vc + LV * k) * 16);
+            vr[j * VCPL + k] = ld16_kv(vp + (vt + (64 / LV) * j) * ROWB + (vc + LV * k) * 16);
       }
     };
     // first page (a valid page of the pool even when this wave has none in the item)

@@ -8,7 +8,6 @@
 
 namespace pkv {
 
-int dense_grid_cap();
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace pkv
