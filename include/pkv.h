@@ -150,7 +150,8 @@ int paged_decode_reduce(const float* partial_acc, const float* partial_m,
  *   out        [total_q, num_heads, ckv_dim] bf16        lse [total_q, num_heads] float32
  * PKV_EINVAL: NULL pointers with total_q > 0, negative sizes, sm_scale not finite.
  * PKV_EUNSUPPORTED: anything but num_heads = 16, ckv_dim = 512, kpe_dim = 64, page_size = 1
- *   (the shapes [MLA]'s _forward asserts).
+ *   (the shapes [MLA]'s _forward asserts); batch > 512 (the kernel keeps its per-batch tile
+ *   list in LDS).
  */
 int mla_paged_prefill(const void* q_nope, const void* q_pe,
                       const void* ckv_cache, const void* kpe_cache,

@@ -6,6 +6,8 @@
 
 namespace pkv {
 
+constexpr int kMlaMaxBatch = 512;  // batches the kernel's LDS tile list holds
+
 struct MlaArgs {
   const void* q_nope;        // [total_q, 16, 512] bf16
   const void* q_pe;          // [total_q, 16, 64] bf16

@@ -60,7 +60,7 @@ constexpr int kKpeChunks = kDp * 2 / 16;     // 8 chunks of a kpe row
 constexpr int kCkvStride = kCkvChunks + 2;   // padded LDS row (chunks), see ckv_swz
 constexpr int kKeysPerWave = kKT / kQT;      // keys of a tile gathered by each wave
 static_assert((kNumBuf & (kNumBuf - 1)) == 0 && kNumBuf >= 2 && kKeysPerWave * kQT == kKT, "tile shape");
-constexpr int kMaxBatch = 512;
+constexpr int kMaxBatch = kMlaMaxBatch;
 constexpr float kMlaRebase = 8.f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -114,7 +114,7 @@ PKV_DEVICE void lds_dma16_s(const void* sbase, uint32_t voff, const void* lds_ba
 }  // namespace
 
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2)))  // 2 waves per SIMD
-void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
+void mla_prefill_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) uint4 s_ckv[kNumBuf][kKT * kCkvStride];
   __shared__ __attribute__((aligned(16))) uint4 s_kpe[kNumBuf][kKT * kKpeChunks];
   __shared__ int s_tiles[kMaxBatch + 1];  // exclusive prefix of query tiles, by sorted position
@@ -177,7 +177,6 @@ void mla_prefill_kernel(MlaArgs a, int n_tiles_bound) {
     __syncthreads();
   }
   const int n_tiles = s_tiles[B];
-  (void)n_tiles_bound;
 
   for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
     // sorted position (then batch) of this tile
@@ -405,7 +404,7 @@ hipError_t launch_mla_prefill(const MlaArgs& a, hipStream_t s) {
   const int cap = dense_grid_cap();
   const int grid = (int)(bound < cap ? bound : cap);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_prefill_kernel, dim3(grid), dim3(kNT), 0, s, a, (int)bound);
+  hipLaunchKernelGGL(mla_prefill_kernel, dim3(grid), dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 

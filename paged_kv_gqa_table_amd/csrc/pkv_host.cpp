@@ -200,6 +200,9 @@ extern "C" int mla_paged_prefill(const void* q_nope, const void* q_pe, const voi
     return fail(PKV_EUNSUPPORTED,
                 "mla_paged_prefill: compiled for num_heads 16, ckv_dim 512, kpe_dim 64, page_size 1 "
                 "(got %d, %d, %d, %d)", num_heads, ckv_dim, kpe_dim, page_size);
+  if (batch > pkv::kMlaMaxBatch)
+    return fail(PKV_EUNSUPPORTED, "mla_paged_prefill: batch %d exceeds %d (the tile list is held in LDS)", batch,
+                pkv::kMlaMaxBatch);
   if (total_q == 0 || batch == 0) return PKV_OK;
   if (!q_nope || !q_pe || !ckv_cache || !kpe_cache || !qo_indptr || !kv_indptr || !kv_indices || !out || !lse)
     return fail(PKV_EINVAL, "mla_paged_prefill: NULL pointer argument");

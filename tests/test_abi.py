@@ -116,6 +116,7 @@ def _mla(L, **kw):
     (dict(Dc=256), EUNSUP),
     (dict(Dp=32), EUNSUP),
     (dict(ps=16), EUNSUP),
+    (dict(batch=513), EUNSUP),
     (dict(out=None), EINVAL),
     (dict(max_q_len=0), EINVAL),
     (dict(batch=-1), EINVAL),
