@@ -399,7 +399,7 @@ void mla_prefill_kernel(MlaArgs a) {
 
 hipError_t launch_mla_prefill(const MlaArgs& a, hipStream_t s) {
   if (a.batch > kMaxBatch) return hipErrorNotSupported;
-  // upper bound of query tiles: total_q / 4 + one partial tile per batch
+  // upper bound of query tiles: total_q / kQT + one partial tile per batch
   const long bound = (long)a.total_q / kQT + a.batch;
   const int cap = dense_grid_cap();
   const int grid = (int)(bound < cap ? bound : cap);
