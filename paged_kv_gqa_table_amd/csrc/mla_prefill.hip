@@ -18,9 +18,9 @@
 //    double-buffered. Each wave moves 4 keys: one transfer per key for its 1 KiB ckv row
 //    (scalar address, page ids from one scalar load) and lane-masked transfers for the
 //    keys' kpe rows, so the gather costs almost no vector instructions.
-//  * The gather rate a CU sustains is the limit (more tiles in flight do not help; fewer
-//    bytes per token do), so as many tokens as the register file allows share each
-//    gathered tile. The transfers are issued as inline assembly, invisible to the
+//  * The gather rate a CU sustains bounds the kernel (measured: more tiles in flight did
+//    not help, fewer bytes per token did), so as many tokens as the register file allows
+//    share each gathered tile. The transfers are issued as inline assembly, invisible to the
 //    compiler's wait insertion, so tile kt+1 lands while tile kt is computed; the kernel
 //    waits for them itself before the barrier that publishes a buffer.
 //  * S^T = K . Q^T with v_mfma_f32_16x16x32_bf16: A = a K row slice read from LDS, B = the
@@ -45,21 +45,14 @@ namespace {
 constexpr int kH = 16;          // heads (MFMA rows / cols)
 constexpr int kDc = 512;        // ckv dims (also V dims)
 constexpr int kDp = 64;         // kpe dims
-#ifndef MLA_QT
-#define MLA_QT 8
-#endif
-#ifndef MLA_NBUF
-#define MLA_NBUF 2
-#endif
-constexpr int kQT = MLA_QT;     // query tokens per workgroup (one per wave)
+constexpr int kQT = 8;          // query tokens per workgroup (one per wave)
 constexpr int kNT = kQT * 64;   // threads per workgroup
-constexpr int kNumBuf = MLA_NBUF;  // LDS key-tile buffers (kNumBuf - 1 tiles in flight)
 constexpr int kKT = 32;         // keys per tile
 constexpr int kCkvChunks = kDc * 2 / 16;     // 64 16-byte chunks of a ckv row
 constexpr int kKpeChunks = kDp * 2 / 16;     // 8 chunks of a kpe row
 constexpr int kCkvStride = kCkvChunks + 2;   // padded LDS row (chunks), see ckv_swz
 constexpr int kKeysPerWave = kKT / kQT;      // keys of a tile gathered by each wave
-static_assert((kNumBuf & (kNumBuf - 1)) == 0 && kNumBuf >= 2 && kKeysPerWave * kQT == kKT, "tile shape");
+static_assert(kKeysPerWave * kQT == kKT, "tile shape");
 constexpr int kMaxBatch = kMlaMaxBatch;
 constexpr float kMlaRebase = 8.f;
 
@@ -86,9 +79,6 @@ PKV_DEVICE uint32_t ckv_swz(int r) { return (uint32_t)(((r >> 2) ^ (r >> 3)) & 1
 PKV_DEVICE uint32_t kpe_swz(int r) { return (uint32_t)((r & 7) ^ ((r >> 3) & 1)); }
 
 PKV_DEVICE void vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Waits until at most N transfers of this wave are outstanding.
-template <int N>
-PKV_DEVICE void vmcnt_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 // Transposing 8-byte LDS read (see the header comment for the lane mapping).
@@ -115,8 +105,8 @@ PKV_DEVICE void lds_dma16_s(const void* sbase, uint32_t voff, const void* lds_ba
 
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2)))  // 2 waves per SIMD
 void mla_prefill_kernel(MlaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint4 s_ckv[kNumBuf][kKT * kCkvStride];
-  __shared__ __attribute__((aligned(16))) uint4 s_kpe[kNumBuf][kKT * kKpeChunks];
+  __shared__ __attribute__((aligned(16))) uint4 s_ckv[2][kKT * kCkvStride];  // double-buffered key tiles
+  __shared__ __attribute__((aligned(16))) uint4 s_kpe[2][kKT * kKpeChunks];
   __shared__ int s_tiles[kMaxBatch + 1];  // exclusive prefix of query tiles, by sorted position
   __shared__ int s_border[kMaxBatch];     // batch at each sorted position
   __shared__ int s_kvl[kMaxBatch];        // clamped kv_len per batch
@@ -228,9 +218,10 @@ void mla_prefill_kernel(MlaArgs a) {
 #pragma unroll
     for (int s = 0; s < 18; ++s) asm volatile("" ::"v"(qb[s].x), "v"(qb[s].y), "v"(qb[s].z), "v"(qb[s].w));
 
-    // ---- gather of one key tile into LDS buffer `buf`: wave w moves keys 8w .. 8w+7 of the
-    // tile (keys past the workgroup's last one re-read its last key; they are masked). The
-    // page ids of tile kt+2 are read through the scalar cache during tile kt.
+    // ---- gather of one key tile into LDS buffer `buf`: wave w moves keys kKeysPerWave w ..
+    // kKeysPerWave (w + 1) - 1 of the tile (keys past the workgroup's last one re-read its
+    // last key; they are masked). The page ids of tile kt+2 are read through the scalar
+    // cache during tile kt.
     const __attribute__((address_space(4))) int32_t* ids =
         (const __attribute__((address_space(4))) int32_t*)(a.kv_indices + k0);
     int tok_next[kKeysPerWave];
@@ -277,25 +268,17 @@ void mla_prefill_kernel(MlaArgs a) {
     for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_ref = kNegInf, m_true = kNegInf, lsum = 0.f;  // per head (lane's column)
 
-    // tiles 0 .. kNumBuf-2 in flight before the loop; tile kt + kNumBuf - 1 is issued at
-    // the top of tile kt, into the buffer tile kt - 1 just released
-    constexpr int kPerTile = 2 * kKeysPerWave;  // transfers per wave and tile (ckv + kpe)
-#pragma unroll
-    for (int j = 0; j < kNumBuf - 1; ++j)
-      if (j < n_kt) {
-        load_ids(j);
-        issue_tile(j);
-      }
-    if (kNumBuf - 1 < n_kt) load_ids(kNumBuf - 1);
+    // tile kt + 1 is issued at the top of tile kt, into the buffer tile kt - 1 released
+    if (n_kt > 0) {
+      load_ids(0);
+      issue_tile(0);
+      if (n_kt > 1) load_ids(1);
+    }
     for (int kt = 0; kt < n_kt; ++kt) {
-      const int buf = kt & (kNumBuf - 1);
-      // wait for this wave's transfers of tile kt; those of the later tiles may stay in flight
-      const int later = min(kNumBuf - 2, n_kt - 1 - kt);
-      if (kNumBuf >= 4 && later >= 2) vmcnt_le<(kNumBuf >= 4 ? 2 * kPerTile : 0)>();
-      else if (kNumBuf >= 3 && later >= 1) vmcnt_le<(kNumBuf >= 3 ? kPerTile : 0)>();
-      else vmcnt0();
-      __syncthreads();  // tile kt landed in LDS; everyone is done with tile kt-1
-      if (kt + kNumBuf - 1 < n_kt) issue_tile((kt + kNumBuf - 1) & (kNumBuf - 1));
+      const int buf = kt & 1;
+      vmcnt0();          // this wave's transfers of tile kt
+      __syncthreads();   // every wave's transfers of tile kt landed; everyone is done with tile kt-1
+      if (kt + 1 < n_kt) issue_tile(buf ^ 1);
       const int key0 = kt * kKT;
       if (key0 < vis) {  // uniform: else this wave's row sees none of these keys
         // ---- S^T for two 16-key halves
@@ -322,7 +305,7 @@ void mla_prefill_kernel(MlaArgs a) {
         }
         // next ids: the scalar load completes under the softmax (any later LDS wait would
         // also wait for it)
-        if (kt + kNumBuf < n_kt) load_ids(kt + kNumBuf);
+        if (kt + 2 < n_kt) load_ids(kt + 2);
         // lane holds keys key0 + hf*16 + 4g + i for head hq
         float x[8];
         float tmax = kNegInf;
@@ -371,8 +354,8 @@ void mla_prefill_kernel(MlaArgs a) {
           const uint2 hi = lds_read_tr16(vrow_hi + n * 32);
           acc[n] = mfma16x16x32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[n]);
         }
-      } else if (kt + kNumBuf < n_kt) {
-        load_ids(kt + kNumBuf);
+      } else if (kt + 2 < n_kt) {
+        load_ids(kt + 2);
       }
     }
 
