@@ -19,6 +19,8 @@
 //    8 * row + n), so no LDS transpose is needed.
 //  * Per-head running max across the 4 lanes of a head, base-2 exponent, lazy re-basing
 //    behind a wave-uniform branch; the stored m is the exact max in natural-log units.
+#include <type_traits>
+
 #include "common.h"
 #include "decode_args.h"
 #include "worklist.h"
@@ -111,15 +113,22 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
   uint4 kr[KS];
   uint4 vt[XP ? 1 : 4][XP ? 1 : NB];  // token-major: tokens 4g+i, chunk 16*blk + hl
   uint2 vx[XP ? NT : 1];              // x-packed: dim 16 t + hl, tokens 4g .. 4g+3
-  auto issue_k = [&](int i) {
+  // Pages are loaded non-temporally, except each wave's last page: the loop refills the
+  // registers past the end by re-reading that page (so the loads stay unconditional and
+  // need no merge copies), which must then be an L2 hit, not HBM.
+  auto ldkv = [&](auto nt, const char* p) -> uint4 {
+    if constexpr (decltype(nt)::value) return ld16_kv(p);
+    else return ld16(p);
+  };
+  auto issue_k = [&](auto nt, int i) {
     const char* kp = page_ptr(kbase, i);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if constexpr (XP) kr[s] = ld16_kv(kp + ((s * 4 + g) * BS + hl) * 16);  // chunk (dims 32s+8g), token hl
-      else kr[s] = ld16_kv(kp + hl * ROWB + (s * 32 + g * 8) * 2);
+      if constexpr (XP) kr[s] = ldkv(nt, kp + ((s * 4 + g) * BS + hl) * 16);  // chunk (dims 32s+8g), token hl
+      else kr[s] = ldkv(nt, kp + hl * ROWB + (s * 32 + g * 8) * 2);
     }
   };
-  auto issue_v = [&](int i) {
+  auto issue_v = [&](auto nt, int i) {
     const char* vp = page_ptr(vbase, i);
     if constexpr (XP) {
 #pragma unroll
@@ -128,15 +137,21 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int k = 0; k < NB; ++k) vt[j][k] = ld16_kv(vp + (4 * g + j) * ROWB + (16 * k + hl) * 16);
+        for (int k = 0; k < NB; ++k) vt[j][k] = ldkv(nt, vp + (4 * g + j) * ROWB + (16 * k + hl) * 16);
     }
   };
 
-  if (n_my > 0) {
-    issue_k(0);
-    issue_v(0);
+  using Streaming = std::true_type;  // non-temporal loads
+  using Cached = std::false_type;    // ordinary loads (kept in L2)
+  if (n_my > 1) {
+    issue_k(Streaming{}, 0);
+    issue_v(Streaming{}, 0);
+  } else if (n_my == 1) {
+    issue_k(Cached{}, 0);
+    issue_v(Cached{}, 0);
   }
-  for (int i = 0; i < n_my; ++i) {
+  // one page; `nt` is the cache policy of the loads it issues for the next page
+  auto page = [&](auto nt, int i) {
     const int pg = pg_begin + w + W * i;
     const int ntok = min(BS, len - pg * BS);
     const bool more = i + 1 < n_my;
@@ -145,7 +160,7 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
     f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) st = mfma_k32(kr[s], qb[s], st);
-    issue_k(more ? i + 1 : i);
+    issue_k(nt, more ? i + 1 : i);
 
     float x[4];
     float tmax = kNegInf;
@@ -205,8 +220,11 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
           acc[k * 8 + n] = mfma_k16(av, pb, acc[k * 8 + n]);
         }
     }
-    issue_v(more ? i + 1 : i);
-  }
+    issue_v(nt, more ? i + 1 : i);
+  };
+  int i = 0;
+  for (; i + 2 < n_my; ++i) page(Streaming{}, i);    // refills pages 1 .. n_my-2
+  for (; i < n_my; ++i) page(Cached{}, i);  // refills the last page, then re-reads it
 
   // ---- merge: l over the 4 lanes of a head, then waves through LDS
   lsum += xor_lanes(lsum, 16);

@@ -31,6 +31,8 @@
 //    formed, its V loads as soon as P.V is done.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "decode_args.h"
 #include "worklist.h"
@@ -142,32 +144,44 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
     const int id = __builtin_amdgcn_readlane(pid_cache, i & 63);
     return base + (size_t)id * block_stride;
   };
-  auto issue_k = [&](int i) {
+  // Pages are loaded non-temporally, except each wave's last page: the loop refills the
+  // registers past the end by re-reading that page (so the loads stay unconditional and
+  // need no merge copies), which must then be an L2 hit, not HBM.
+  auto ldkv = [&](auto nt, const char* p) -> uint4 {
+    if constexpr (decltype(nt)::value) return ld16_kv(p);
+    else return ld16(p);
+  };
+  auto issue_k = [&](auto nt, int i) {
     const char* kp = page_ptr(kbase, i);
 #pragma unroll
     for (int j = 0; j < TPL; ++j)
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) kr[j][k] = ld16_kv(kp + k_off(tg + TPI * j, c + LPT * k));
+      for (int k = 0; k < CPL; ++k) kr[j][k] = ldkv(nt, kp + k_off(tg + TPI * j, c + LPT * k));
   };
-  auto issue_v = [&](int i) {
+  auto issue_v = [&](auto nt, int i) {
     const char* vp = page_ptr(vbase, i);
     if constexpr (XP) {
 #pragma unroll
-      for (int q = 0; q < NVC; ++q) vr[q] = ld16_kv(vp + (size_t)(64 * q + lane) * 16);
+      for (int q = 0; q < NVC; ++q) vr[q] = ldkv(nt, vp + (size_t)(64 * q + lane) * 16);
     } else {
 #pragma unroll
       for (int j = 0; j < TPL; ++j)
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) vr[j * CPL + k] = ld16_kv(vp + k_off(tg + TPI * j, c + LPT * k));
+        for (int k = 0; k < CPL; ++k) vr[j * CPL + k] = ldkv(nt, vp + k_off(tg + TPI * j, c + LPT * k));
     }
   };
 
-  if (n_my > 0) {
-    issue_k(0);
-    issue_v(0);
+  using Streaming = std::true_type;  // non-temporal loads
+  using Cached = std::false_type;    // ordinary loads (kept in L2)
+  if (n_my > 1) {
+    issue_k(Streaming{}, 0);
+    issue_v(Streaming{}, 0);
+  } else if (n_my == 1) {
+    issue_k(Cached{}, 0);
+    issue_v(Cached{}, 0);
   }
-#pragma unroll 2
-  for (int i = 0; i < n_my; ++i) {
+  // one page; `nt` is the cache policy of the loads it issues for the next page
+  auto page = [&](auto nt, int i) {
     const int pg = pg_begin + w + W * i;
     const int ntok = min(BS, len - pg * BS);  // valid tokens in this page (uniform)
     const bool more = i + 1 < n_my;
@@ -202,10 +216,9 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
         s[g][j] = d0 + d1;
       }
     }
-    // K registers are free again: the next page's loads leave now. The load is issued
-    // unconditionally (the last iteration re-reads its own page, an L2 hit) so the
-    // registers need no merge copy at the loop back edge.
-    issue_k(more ? i + 1 : i);
+    // K registers are free again: the next page's loads leave now (unconditionally: the
+    // last iteration re-reads its own page, see issue_k).
+    issue_k(nt, more ? i + 1 : i);
 
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -346,8 +359,11 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
       }
       wave_lds_fence();  // this page's P reads finish before the next page overwrites it
     }
-    issue_v(more ? i + 1 : i);  // V registers are free again (unconditional, as for K)
-  }
+    issue_v(nt, more ? i + 1 : i);  // V registers are free again (unconditional, as for K)
+  };
+  int i = 0;
+  for (; i + 2 < n_my; ++i) page(Streaming{}, i);    // refills pages 1 .. n_my-2
+  for (; i < n_my; ++i) page(Cached{}, i);  // refills the last page, then re-reads it
 
   // ---- merge this wave's lanes, then the waves, through LDS
 #pragma unroll

@@ -15,6 +15,8 @@
 //    running max with lazy re-basing, base-2 exponent, LDS merge of the waves.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "decode_args.h"
 #include "worklist.h"
@@ -174,29 +176,43 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
     };
     uint4 kr[2][KCPL];
     uint4 vr[NVREG];
-    auto issue_k = [&](int i) {
+    // Pages are loaded non-temporally, except each wave's last page of the item: the loop
+    // refills the registers past the end by re-reading that page (so the loads stay
+    // unconditional and need no merge copies), which must then be an L2 hit, not HBM.
+    auto ldkv = [&](auto nt, const char* p) -> uint4 {
+      if constexpr (decltype(nt)::value) return ld16_kv(p);
+      else return ld16(p);
+    };
+    auto issue_k = [&](auto nt, int i) {
       const char* kp = page_ptr(kbase, i);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int k = 0; k < KCPL; ++k) kr[j][k] = ld16_kv(kp + k_off(kt + 8 * j, kc + 8 * k));
+        for (int k = 0; k < KCPL; ++k) kr[j][k] = ldkv(nt, kp + k_off(kt + 8 * j, kc + 8 * k));
     };
-    auto issue_v = [&](int i) {
+    auto issue_v = [&](auto nt, int i) {
       const char* vp = page_ptr(vbase, i);
       if constexpr (XP) {
 #pragma unroll
-        for (int q = 0; q < NVC; ++q) vr[q] = ld16_kv(vp + (size_t)(64 * q + lane) * 16);
+        for (int q = 0; q < NVC; ++q) vr[q] = ldkv(nt, vp + (size_t)(64 * q + lane) * 16);
       } else {
 #pragma unroll
         for (int j = 0; j < VT; ++j)
 #pragma unroll
           for (int k = 0; k < VCPL; ++k)
-            vr[j * VCPL + k] = ld16_kv(vp + (vt + (64 / LV) * j) * ROWB + (vc + LV * k) * 16);
+            vr[j * VCPL + k] = ldkv(nt, vp + (vt + (64 / LV) * j) * ROWB + (vc + LV * k) * 16);
       }
     };
+    using Streaming = std::true_type;  // non-temporal loads
+    using Cached = std::false_type;    // ordinary loads (kept in L2)
     // first page (a valid page of the pool even when this wave has none in the item)
-    issue_k(0);
-    issue_v(0);
+    if (n_my > 1) {
+      issue_k(Streaming{}, 0);
+      issue_v(Streaming{}, 0);
+    } else {
+      issue_k(Cached{}, 0);
+      issue_v(Cached{}, 0);
+    }
 
     // ---- prefetch of the workgroup's next item
     ++k_item;
@@ -220,11 +236,11 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
     }
     const uint32_t* q_cur = &sm.q_lds[slot][0][0];
 
-    for (int i = 0; i < n_my; ++i) {
+    // one page; `nt` is the cache policy of the loads it issues for page nx
+    auto page = [&](auto nt, int i) {
       const int pg = pg_begin + w + W * i;
       const int ntok = min(BS, len - pg * BS);
-      // refill target: the next page, or this page again past the end (an L2 hit that keeps
-      // the loads unconditional, so the registers need no merge copies)
+      // refill target: the next page, or the last page again past the end (see issue_k)
       const int nx = i + 1 < n_my ? i + 1 : i;
       ensure_ids(nx);
       // ---- scores of tokens kt and kt + 8, summed over the 8 lanes of a row
@@ -248,7 +264,7 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
           s[g][j] = d0 + d1;
         }
       }
-      issue_k(nx);
+      issue_k(nt, nx);
 
 #pragma unroll
       for (int g = 0; g < G; ++g)
@@ -357,8 +373,11 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
           }
       }
       wave_lds_fence();  // this page's P reads finish before the next page overwrites it
-      issue_v(nx);
-    }
+      issue_v(nt, nx);
+    };
+    int i = 0;
+    for (; i + 2 < n_my; ++i) page(Streaming{}, i);   // refills pages 1 .. n_my-2
+    for (; i < n_my; ++i) page(Cached{}, i); // refills the last page, then re-reads it
     // the next item's q goes to the other LDS buffer while the waves meet (an LDS DMA in
     // flight during the page loop would make every LDS read there wait for all loads)
     if (has_next) fetch_q(nb, nkvh, slot ^ 1);
