@@ -97,7 +97,8 @@ PKV_DEVICE uint2 lds_read_tr16(const void* p) {
 PKV_DEVICE void lds_dma16_s(const void* sbase, uint32_t voff, const void* lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase) : "m0");
+  // M0 (the LDS destination) is an input operand, so the compiler writes it and knows its value
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0));
 }
 
 
