@@ -6,6 +6,8 @@
  *                         grouped-query heads: per-partition online-softmax partials
  *   paged_decode_reduce   log-sum-exp weighted combine of those partials
  *   mla_paged_prefill     MLA causal paged prefill (page_size 1), base-2 LSE
+ * and a measurement helper, pkv_read_bandwidth (a plain streaming read of a buffer),
+ * that no part of the attention path uses.
  *
  * Conventions shared by every entry point:
  *   - Every pointer argument is a DEVICE pointer (HIP global memory) owned by the
