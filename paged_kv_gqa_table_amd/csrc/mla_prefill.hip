@@ -16,8 +16,9 @@
 //  * Keys come in tiles of 32: the 32 [ckv | kpe] rows (1152 B each) are gathered through
 //    kv_indices straight into LDS with global_load_lds_dwordx4 (no staging registers),
 //    double-buffered. Each wave moves 4 keys: one transfer per key for its 1 KiB ckv row
-//    (scalar address, page ids from one scalar load) and lane-masked transfers for the
-//    keys' kpe rows, so the gather costs almost no vector instructions.
+//    (scalar address, page ids from one scalar load) and one 32-lane transfer for the
+//    four keys' kpe rows (scalar base, per-lane offsets), so the gather costs almost no
+//    vector instructions.
 //  * The gather rate a CU sustains bounds the kernel (measured: more tiles in flight did
 //    not help, fewer bytes per token did), so as many tokens as the register file allows
 //    share each gathered tile. The transfers are issued as inline assembly, invisible to the
@@ -253,14 +254,24 @@ void mla_prefill_kernel(MlaArgs a) {
         const char* row = reinterpret_cast<const char*>(a.ckv) + (size_t)tok[k] * (kDc * 2);
         lds_dma16_s(row, (uint32_t)(lane ^ ckv_swz(row_k)) * 16, &s_ckv[buf][row_k * kCkvStride]);
       }
-      // kpe rows of the 8 keys: lanes 8k .. 8k+7 move key k (lane i lands in slot i, i.e.
-      // position i & 7 of row 8w + k, and loads global chunk (i & 7) ^ kpe_swz(8w + k))
-      const uint32_t chunk16 = (uint32_t)((lane & 7) ^ kpe_swz(kKeysPerWave * w + (lane >> 3))) * 16;
+      // kpe rows of the wave's keys: lanes 8k .. 8k+7 move key k (lane i lands in slot i,
+      // i.e. position i & 7 of row kKeysPerWave w + k, and loads global chunk
+      // (i & 7) ^ kpe_swz(row)). One transfer from the kpe array with a per-lane 32-bit
+      // offset while page * 128 fits in 32 bits; else one transfer per key.
+      const int kl = lane >> 3;
+      const uint32_t chunk16 = (uint32_t)((lane & 7) ^ kpe_swz(kKeysPerWave * w + kl)) * 16;
+      void* kpe_dst = &s_kpe[buf][kKeysPerWave * w * kKpeChunks];
+      if (a.num_pages <= (1 << 25)) {  // uniform
+        int tk = tok[0];
 #pragma unroll
-      for (int k = 0; k < kKeysPerWave; ++k)
-        if ((lane >> 3) == k)
-          lds_dma16_s(reinterpret_cast<const char*>(a.kpe) + (size_t)tok[k] * (kDp * 2), chunk16,
-                      &s_kpe[buf][kKeysPerWave * w * kKpeChunks]);
+        for (int k = 1; k < kKeysPerWave; ++k) tk = kl == k ? tok[k] : tk;
+        if (kl < kKeysPerWave) lds_dma16_s(a.kpe, (uint32_t)tk * (kDp * 2) + chunk16, kpe_dst);
+      } else {
+#pragma unroll
+        for (int k = 0; k < kKeysPerWave; ++k)
+          if (kl == k)
+            lds_dma16_s(reinterpret_cast<const char*>(a.kpe) + (size_t)tok[k] * (kDp * 2), chunk16, kpe_dst);
+      }
     };
 
     // O^T accumulators: tile n holds rows j -> dim 16 n + j, cols = heads
