@@ -14,8 +14,8 @@ values it does not compute itself (dense brute force through library
 softmax / logsumexp / SDPA, closed forms, invariants, hand-worked fixtures).
 """
 from .decode import (TOKEN_MAJOR, XPACKED, decode, decode_partials, gather_sequence,
-                     reduce_partials)
+                     partition_ranges, reduce_partials)
 from .mla import mla_prefill
 
 __all__ = ["TOKEN_MAJOR", "XPACKED", "decode", "decode_partials", "gather_sequence",
-           "reduce_partials", "mla_prefill"]
+           "partition_ranges", "reduce_partials", "mla_prefill"]

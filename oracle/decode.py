@@ -15,7 +15,8 @@ Sources (the pages this restates; no code is taken from them):
     out = sum f * acc_s / sum f * l_s; zeros for an empty context).
 
 Readings taken where the pages differ or are silent (each listed in the design doc):
-  partial acc is unnormalized; partial m is in natural-log units of the scaled
+  partial acc is unnormalized (normalized on request, for the PagedAttention V2
+  interface); partial m is in natural-log units of the scaled
   score; partitions are token ranges [p*ps, min((p+1)*ps, len)); an empty
   sequence gives out = 0 and lse = -inf; query head h reads kv head h // G.
 """
@@ -143,16 +144,44 @@ def decode(query, key_cache, value_cache, layout: str, block_tables, seq_lens, s
     return out, lse
 
 
+def partition_ranges(n: int, block_size: int, partition_size: int, num_splits: int = 0):
+    """Token ranges [t0, t1) of the non-empty partitions of one n-token sequence.
+
+    Fixed partitions (num_splits = 0; PagedAttention V2 page, ``_partition_attn_kernel``):
+    partition p covers [p*ps, min((p+1)*ps, n)) for p < ceil(n / ps).
+
+    NUM_SPLITS policy (num_splits = NS > 0; flash-decode post,
+    ``_flash_decode_partial_kernel``): the sequence's nb = ceil(n / bs) pages are cut
+    into runs of bps = ceil(nb / NS) whole pages, so split s covers pages
+    [s*bps, min((s+1)*bps, nb)), i.e. tokens [s*bps*bs, min((s+1)*bps*bs, n)). Splits
+    that start at or past page nb are empty (only ceil(nb / bps) <= NS are real).
+    An empty sequence has no partitions.
+    """
+    if n <= 0:
+        return []
+    if num_splits > 0:
+        nb = -(-n // block_size)
+        bps = -(-nb // num_splits)
+        span = bps * block_size
+    else:
+        span = partition_size
+    count = -(-n // span)
+    return [(p * span, min((p + 1) * span, n)) for p in range(count)]
+
+
 def decode_partials(query, key_cache, value_cache, layout: str, block_tables, seq_lens,
                     scale: float, num_kv_heads: int, block_size: int, partition_size: int,
-                    max_num_partitions: int):
+                    max_num_partitions: int, num_splits: int = 0, normalized: bool = False):
     """Split-K partials per (b, h, p): (acc [S,H,P,D], m [S,H,P], l [S,H,P]) in float64.
 
-    Partition p of sequence b covers tokens [p*ps, min((p+1)*ps, len_b)). For each
-    non-empty one, m = max_t s_t, l = sum_t exp(s_t - m) and acc = sum_t exp(s_t - m) v_t
-    (unnormalized, as the flash-decode post's partial kernel keeps it). Partitions with
-    p*ps >= len_b carry the sentinel m = -inf, l = 0 (PagedAttention V2 page, unused-
-    partition branch); their acc is left 0 here and is not part of the contract.
+    Partition p of sequence b covers the token range ``partition_ranges`` gives (fixed
+    ps-token partitions, or the NUM_SPLITS page-aligned policy when num_splits > 0). For
+    each non-empty one, m = max_t s_t, l = sum_t exp(s_t - m) and
+    acc = sum_t exp(s_t - m) v_t (unnormalized, as the flash-decode post's partial kernel
+    keeps it), or acc / l when ``normalized`` (the PagedAttention V2 page's tmp_output,
+    with l its exp_sums and m its max_logits). Partitions past the sequence's last one
+    carry the sentinel m = -inf, l = 0 (PagedAttention V2 page, unused-partition branch);
+    their acc is left 0 here and is not part of the contract.
     """
     q = _as_f64(query)
     bt = _as_int(block_tables)
@@ -161,41 +190,46 @@ def decode_partials(query, key_cache, value_cache, layout: str, block_tables, se
     G = H // num_kv_heads
     P = int(max_num_partitions)
     ps = int(partition_size)
-    if ps < 1:
+    if ps < 1 and num_splits <= 0:
         raise ValueError("partition_size must be >= 1")
     acc = np.zeros((S, H, P, D))
     m = np.full((S, H, P), -np.inf)
     l = np.zeros((S, H, P))
     for b in range(S):
         n = int(lens[b])
-        if n == 0:
+        ranges = partition_ranges(n, block_size, ps, num_splits)
+        if not ranges:
             continue
-        nparts = -(-n // ps)
-        if nparts > P:
+        if len(ranges) > P:
             raise ValueError("max_num_partitions too small for this sequence")
         K, V = gather_sequence(key_cache, value_cache, layout, bt[b], n, block_size)
         for h in range(H):
             kh = _kv_head(h, G)
             s = _scores(q[b, h], K[kh], scale)
-            for p in range(nparts):
-                t0, t1 = p * ps, min((p + 1) * ps, n)
+            for p, (t0, t1) in enumerate(ranges):
                 sp = s[t0:t1]
                 mp = sp.max()
                 e = np.exp(sp - mp)
                 m[b, h, p] = mp
                 l[b, h, p] = e.sum()
                 acc[b, h, p] = e @ V[kh][t0:t1]
+                if normalized:
+                    acc[b, h, p] = acc[b, h, p] / l[b, h, p]
     return acc, m, l
 
 
-def reduce_partials(partial_acc, partial_m, partial_l, seq_lens, partition_size: int):
+def reduce_partials(partial_acc, partial_m, partial_l, seq_lens, partition_size: int,
+                    num_splits: int = 0, block_size: int = 16, normalized: bool = False):
     """Cross-partition combine. Returns (out [S,H,D], lse [S,H]) in float64.
 
-    Over the P_b = ceil(len_b / ps) partitions of sequence b: M = max_p m_p,
-    w_p = exp(m_p - M), out = sum_p w_p acc_p / sum_p w_p l_p and
-    lse = M + log(sum_p w_p l_p) (flash-decode post, combine kernel; the partition
-    count per sequence follows the PagedAttention V2 page's reduce kernel).
-    Partitions p >= P_b are never read. len_b = 0 gives zeros and -inf.
+    Over the P_b non-empty partitions of sequence b (``partition_ranges``; for fixed
+    partitions P_b = ceil(len_b / ps) as in the PagedAttention V2 page's reduce kernel):
+    M = max_p m_p, w_p = exp(m_p - M), out = sum_p w_p acc_p / sum_p w_p l_p and
+    lse = M + log(sum_p w_p l_p) (flash-decode post, combine kernel). With
+    ``normalized`` partials (acc_p already divided by l_p) every partition weighs
+    w_p l_p instead: out = sum_p w_p l_p acc_p / sum_p w_p l_p (PagedAttention V2 page,
+    ``_reduce_partitions_kernel``). Partitions p >= P_b are never read. len_b = 0 gives
+    zeros and -inf.
     """
     acc = _as_f64(partial_acc)
     m = _as_f64(partial_m)
@@ -206,14 +240,17 @@ def reduce_partials(partial_acc, partial_m, partial_l, seq_lens, partition_size:
     lse = np.full((S, H), -np.inf)
     for b in range(S):
         n = int(lens[b])
-        if n == 0:
+        nparts = len(partition_ranges(n, block_size, int(partition_size), num_splits))
+        if nparts == 0:
             continue
-        nparts = -(-n // int(partition_size))
         for h in range(H):
             mp = m[b, h, :nparts]
             M = mp.max()
             w = np.exp(mp - M)
             Z = w @ l[b, h, :nparts]
-            out[b, h] = (w @ acc[b, h, :nparts]) / Z
+            if normalized:
+                out[b, h] = ((w * l[b, h, :nparts]) @ acc[b, h, :nparts]) / Z
+            else:
+                out[b, h] = (w @ acc[b, h, :nparts]) / Z
             lse[b, h] = M + np.log(Z)
     return out, lse

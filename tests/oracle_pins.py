@@ -298,6 +298,100 @@ def pin_empty_sequence(orc):
     assert np.all(o2[0] == 0.0) and np.all(s2[0] == -np.inf)
 
 
+# NUM_SPLITS policy of the flash-decode post's partial kernel, worked by hand for a
+# 37-token sequence in 4-token pages (nb = ceil(37 / 4) = 10 pages):
+#   NS = 1  -> bps = 10 pages -> one range of all 37 tokens
+#   NS = 3  -> bps = ceil(10 / 3) = 4 pages = 16 tokens -> [0,16) [16,32) [32,37)
+#   NS = 4  -> bps = 3 pages = 12 tokens -> [0,12) [12,24) [24,36) [36,37)
+#   NS = 6  -> bps = 2 pages = 8 tokens -> five ranges, split 5 starts at page 10: empty
+#   NS = 16 -> bps = 1 page -> ten 4-token ranges (the last [36,37)), splits 10..15 empty
+# and for a 5-token sequence (nb = 2): NS = 4 -> bps = 1 -> [0,4) [4,5), splits 2, 3 empty.
+SPLIT_POLICY_CASES = {
+    (37, 1): [(0, 37)],
+    (37, 3): [(0, 16), (16, 32), (32, 37)],
+    (37, 4): [(0, 12), (12, 24), (24, 36), (36, 37)],
+    (37, 6): [(0, 8), (8, 16), (16, 24), (24, 32), (32, 37)],
+    (37, 16): [(4 * i, min(4 * i + 4, 37)) for i in range(10)],
+    (5, 4): [(0, 4), (4, 5)],
+}
+
+
+def _check_partition_stats(acc, m, l, b, h, s_all, Ve_h, ranges, P, normalized, what):
+    for p in range(P):
+        if p >= len(ranges):
+            assert m[b, h, p] == -np.inf and l[b, h, p] == 0.0, f"{what}: sentinel at p={p}"
+            continue
+        t0, t1 = ranges[p]
+        sp = s_all[t0:t1]
+        _close(m[b, h, p], sp.max(), 1e-12, what=f"{what}: partition max")
+        _close(m[b, h, p] + math.log(l[b, h, p]), sps.logsumexp(sp), 1e-12, what=f"{what}: partition lse")
+        avg = acc[b, h, p] if normalized else acc[b, h, p] / l[b, h, p]
+        _close(avg, sps.softmax(sp) @ Ve_h[t0:t1], 1e-12, what=f"{what}: partition average")
+
+
+def pin_split_policy(orc):
+    """NUM_SPLITS page-aligned splits: the hand-worked ranges above, their sentinels, and the
+    reduce against dense brute force for every split count."""
+    H, KVH, D, bs, scale = 4, 2, 8, 4, 0.6
+    for (n, ns), ranges in SPLIT_POLICY_CASES.items():
+        assert [tuple(r) for r in orc.partition_ranges(n, bs, 0, ns)] == ranges, f"ranges n={n} NS={ns}"
+    for layout in ("token_major", "xpacked"):
+        q, kc, vc, bt, lens_a, K, V = _tiny_case(29, [37, 5, 0], H, KVH, D, bs, layout)
+        ref_out, ref_lse = _brute_decode(q, K, V, lens_a, scale, H // KVH)
+        for ns in (1, 2, 3, 4, 6, 7, 10, 16):
+            acc, m, l = orc.decode_partials(q, kc, vc, layout, bt, lens_a, scale, KVH, bs, 0, ns,
+                                            num_splits=ns)
+            for b, n in enumerate((37, 5)):
+                ranges = SPLIT_POLICY_CASES.get((n, ns))
+                if ranges is None:
+                    continue
+                Ke = torch.repeat_interleave(torch.from_numpy(K[b]), H // KVH, dim=0).numpy()
+                Ve = torch.repeat_interleave(torch.from_numpy(V[b]), H // KVH, dim=0).numpy()
+                for h in range(H):
+                    s_all = scale * np.einsum("td,d->t", Ke[h], q[b, h])
+                    _check_partition_stats(acc, m, l, b, h, s_all, Ve[h], ranges, ns, False,
+                                           f"{layout} NS={ns} b={b}")
+            assert np.all(m[2] == -np.inf) and np.all(l[2] == 0.0), "empty sequence: all sentinels"
+            o2, s2 = orc.reduce_partials(acc, m, l, lens_a, 0, num_splits=ns, block_size=bs)
+            _close(o2, ref_out, 1e-12, what=f"{layout} NS={ns} reduce")
+            _close(s2, ref_lse, 1e-12, what=f"{layout} NS={ns} reduce lse")
+
+
+def pin_normalized_partials(orc):
+    """PagedAttention V2 form: tmp_output = softmax over the partition's own scores times its
+    V rows; exp_sums and max_logits as before; its reduce against dense brute force, with
+    NaN in every never-read row."""
+    lens = [45, 9, 0, 16]
+    H, KVH, D, bs, ps, scale = 6, 2, 8, 4, 16, 0.8
+    for layout in ("xpacked", "token_major"):
+        q, kc, vc, bt, lens_a, K, V = _tiny_case(31, lens, H, KVH, D, bs, layout)
+        acc, m, l = orc.decode_partials(q, kc, vc, layout, bt, lens_a, scale, KVH, bs, ps, 5, normalized=True)
+        G = H // KVH
+        for b, n in enumerate(lens):
+            if n == 0:
+                assert np.all(m[b] == -np.inf) and np.all(l[b] == 0.0)
+                continue
+            Ke = torch.repeat_interleave(torch.from_numpy(K[b]), G, dim=0).numpy()
+            Ve = torch.repeat_interleave(torch.from_numpy(V[b]), G, dim=0).numpy()
+            ranges = [(t0, min(t0 + ps, n)) for t0 in range(0, n, ps)]
+            for h in range(H):
+                s_all = scale * np.einsum("td,d->t", Ke[h], q[b, h])
+                _check_partition_stats(acc, m, l, b, h, s_all, Ve[h], ranges, 5, True, f"{layout} normalized")
+        ref_out, ref_lse = _brute_decode(q, K, V, lens_a, scale, G)
+        acc = acc.copy()
+        for b, n in enumerate(lens):
+            acc[b, :, -(-n // ps):] = np.nan
+        o2, s2 = orc.reduce_partials(acc, m, l, lens_a, ps, normalized=True)
+        _close(o2, ref_out, 1e-12, what=f"{layout} normalized reduce")
+        _close(s2, ref_lse, 1e-12, what=f"{layout} normalized reduce lse")
+        # NUM_SPLITS and normalized together
+        acc, m, l = orc.decode_partials(q, kc, vc, layout, bt, lens_a, scale, KVH, bs, 0, 3,
+                                        num_splits=3, normalized=True)
+        o3, s3 = orc.reduce_partials(acc, m, l, lens_a, 0, num_splits=3, block_size=bs, normalized=True)
+        _close(o3, ref_out, 1e-12, what=f"{layout} normalized NS=3 reduce")
+        _close(s3, ref_lse, 1e-12, what=f"{layout} normalized NS=3 reduce lse")
+
+
 # ----------------------------------------------------------------------------------------
 # MLA pins
 # ----------------------------------------------------------------------------------------
@@ -401,7 +495,8 @@ def pin_mla_special_cases(orc):
 
 DECODE_PINS = [pin_decode_worked_example, pin_reduce_worked_example, pin_decode_brute_force,
                pin_decode_special_cases, pin_split_invariance, pin_partition_stats,
-               pin_sentinel_padding, pin_page_permutation, pin_empty_sequence]
+               pin_sentinel_padding, pin_page_permutation, pin_empty_sequence, pin_split_policy,
+               pin_normalized_partials]
 MLA_PINS = [pin_mla_worked_example, pin_mla_sdpa, pin_mla_causal_perturbation,
             pin_mla_special_cases]
 ALL_PINS = DECODE_PINS + MLA_PINS

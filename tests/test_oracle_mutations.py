@@ -33,14 +33,21 @@ MUTATIONS = [
     ("decode.py", "lse[b, h] = M + np.log(Z)", "lse[b, h] = np.log(Z)", 0, "max term dropped from lse"),
     ("decode.py", "acc[b, h, p] = e @ V[kh][t0:t1]", "acc[b, h, p] = (e @ V[kh][t0:t1]) / e.sum()", 0,
      "normalized partial acc"),
-    ("decode.py", "t0, t1 = p * ps, min((p + 1) * ps, n)", "t0, t1 = p * ps, min((p + 1) * ps, n - 1)", 0,
+    ("decode.py", "return [(p * span, min((p + 1) * span, n)) for p in range(count)]",
+     "return [(p * span, min((p + 1) * span, n - 1)) for p in range(count)]", 0,
      "last token dropped from partition"),
     ("decode.py", "m[b, h, p] = mp", "m[b, h, p] = mp * np.log2(np.e)", 0, "partial m in base 2"),
     ("decode.py", "w = np.exp(mp - M)", "w = np.exp(M - mp)", 0, "combine weight sign"),
     ("decode.py", "Z = w @ l[b, h, :nparts]", "Z = w.sum()", 0, "exp-sums dropped from combine"),
     ("decode.py", "lse[b, h] = M + np.log(Z)", "lse[b, h] = np.log(Z)", 1, "max term dropped from reduce lse"),
-    ("decode.py", "nparts = -(-n // int(partition_size))", "nparts = max(1, n // int(partition_size))", 0,
-     "floor partition count in reduce"),
+    ("decode.py", "count = -(-n // span)", "count = max(1, n // span)", 0, "floor partition count"),
+    ("decode.py", "bps = -(-nb // num_splits)", "bps = max(1, nb // num_splits)", 0, "floor pages per split"),
+    ("decode.py", "span = bps * block_size", "span = bps * block_size - 1", 0, "split span one token short"),
+    ("decode.py", "nb = -(-n // block_size)", "nb = max(1, n // block_size)", 0, "floor page count of a split"),
+    ("decode.py", "acc[b, h, p] = acc[b, h, p] / l[b, h, p]", "acc[b, h, p] = acc[b, h, p] * 1.0", 0,
+     "normalized partial not divided by l"),
+    ("decode.py", "out[b, h] = ((w * l[b, h, :nparts]) @ acc[b, h, :nparts]) / Z",
+     "out[b, h] = (w @ acc[b, h, :nparts]) / Z", 0, "normalized reduce without exp-sums weight"),
     ("mla.py", "vis = min(prefix + i + 1, kv_len)", "vis = min(prefix + i, kv_len)", 0, "causal off by one"),
     ("mla.py", "return sm_scale * (qn_row @ Kc.T + qp_row @ Kp.T)", "return sm_scale * (qn_row @ Kc.T)", 0,
      "kpe term dropped"),
