@@ -56,8 +56,11 @@ def _events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
-def bench_decode(case, steps, warmup, copies=0):
-    """Time `steps` decode steps; returns a dict of measurements."""
+def bench_decode(case, steps, warmup, copies=0, one_launch=False):
+    """Time `steps` decode steps; returns a dict of measurements. A step is the two phases
+    (paged_decode_partial + paged_decode_reduce), or with `one_launch` the single-launch
+    paged_decode (phase 1 with the combine done by the last workgroup of each (sequence,
+    kv head)); the timed kernel is then that one launch."""
     import torch
     import paged_kv_gqa_table_amd as pkv
 
@@ -79,11 +82,18 @@ def bench_decode(case, steps, warmup, copies=0):
     m = torch.empty((S, H, P), dtype=torch.float32, device=dev)
     l = torch.empty((S, H, P), dtype=torch.float32, device=dev)
     out = torch.empty((S, H, D), dtype=case.query.dtype, device=dev)
+    counters = torch.zeros((S * case.num_kv_heads,), dtype=torch.int32, device=dev)
 
     def step(i, ev=None):
         kc, vc = pools[i % copies]
         if ev is not None:
             ev[0].record()
+        if one_launch:
+            pkv.paged_decode_into(q, kc, vc, bt, lens, case.scale, case.num_kv_heads, ps, 0, max_len, out, None,
+                                  acc, m, l, counters, layout=case.layout)
+            if ev is not None:
+                ev[1].record()
+            return
         pkv.paged_decode_partial(q, kc, vc, bt, lens, case.scale, case.num_kv_heads, ps, max_len,
                                  acc, m, l, layout=case.layout)
         if ev is not None:
@@ -327,6 +337,10 @@ def main():
     result["roofline"]["frac_of_measured_read_ceiling"] = achieved / ceiling
     if not args.no_extra and args.workload == "llama_gqa4":
         extra = {}
+        ro = bench_decode(case, max(20, args.steps // 2), 5, one_launch=True)
+        extra["llama_gqa4_one_launch"] = {"us_per_step": ro["wall_ms_per_step"] * 1e3,
+                                          "GB_s": kv / (ro["wall_ms_per_step"] * 1e-3) / 1e9,
+                                          "kernel_avg_us": ro["partial_avg_ms"] * 1e3}
         for name in ("wide_gqa6", "skewed_gqa8"):
             _log(f"secondary workload {name}")
             c2 = inputs.decode_workload(name)
@@ -336,6 +350,9 @@ def main():
                            "partial_GB_s": c2.kv_bytes() / (r2["partial_avg_ms"] * 1e-3) / 1e9,
                            "layout": c2.layout}
             extra[name]["pct_of_peak"] = 100.0 * extra[name]["GB_s"] / HBM_PEAK_GBS
+            r3 = bench_decode(c2, max(10, args.steps // 4), 5, one_launch=True)
+            extra[name]["one_launch_us_per_step"] = r3["wall_ms_per_step"] * 1e3
+            extra[name]["one_launch_GB_s"] = c2.kv_bytes() / (r3["wall_ms_per_step"] * 1e-3) / 1e9
             del c2
             torch.cuda.empty_cache()
         try:

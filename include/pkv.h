@@ -1,10 +1,16 @@
 /*
  * pkv.h -- C ABI of the paged-KV attention library for AMD Instinct MI355X (gfx950).
  *
- * Three operations:
+ * Operations:
  *   paged_decode_partial  split-K single-token decode over a paged KV cache with
  *                         grouped-query heads: per-partition online-softmax partials
  *   paged_decode_reduce   log-sum-exp weighted combine of those partials
+ *   paged_decode_split_partial, paged_decode_split_reduce
+ *                         the same two phases with [FD]'s NUM_SPLITS page-aligned splits
+ *   paged_decode          the whole decode in one launch (single pass when every
+ *                         sequence fits one partition)
+ *   paged_attention_v2    [PAv2]'s launcher: x-packed cache, 512-token partitions,
+ *                         normalized partials (tmp_output, exp_sums, max_logits)
  *   mla_paged_prefill     MLA causal paged prefill (page_size 1), base-2 LSE
  * and a measurement helper, pkv_read_bandwidth (a plain streaming read of a buffer),
  * that no part of the attention path uses.
@@ -97,6 +103,8 @@ typedef enum {
  *   for head_dim 64 token-major) run on the matrix cores, padded to 16 heads.
  * num_seqs == 0 or max_seq_len == 0 launches nothing except the sentinel writes that
  *   the length rule above asks for.
+ * A length above max_seq_len (a broken contract) is cut to max_num_partitions partitions,
+ *   so no write lands outside the partial arrays.
  */
 int paged_decode_partial(const void* query, int dtype,
                          const void* key_cache, const void* value_cache, int layout,
@@ -132,6 +140,101 @@ int paged_decode_reduce(const float* partial_acc, const float* partial_m,
                         int num_seqs, int num_heads, int head_dim,
                         int partition_size, int max_num_partitions,
                         void* out, int out_dtype, float* lse, void* stream);
+
+/*
+ * paged_decode_split_partial / paged_decode_split_reduce -- the two phases with [FD]'s
+ * split policy (_flash_decode_partial_kernel: NUM_SPLITS splits per sequence, each a run
+ * of whole pages).
+ *
+ * Sequence b's nb = ceil(len_b / block_size) pages are cut into runs of
+ * bps = ceil(nb / num_splits) pages; split s covers tokens
+ * [s*bps*block_size, min((s+1)*bps*block_size, len_b)). Splits starting at or past page nb
+ * are empty (m = -inf, l = 0, acc row not written). Everything else is as in
+ * paged_decode_partial / paged_decode_reduce, with num_splits in place of
+ * max_num_partitions: partial_acc is [num_seqs, num_heads, num_splits, head_dim] and
+ * partial_m, partial_l are [num_seqs, num_heads, num_splits]. The reduce reads the
+ * ceil(nb / bps) non-empty splits of each sequence.
+ * PKV_EINVAL: num_splits <= 0, and the conditions of the fixed-partition entry points.
+ * PKV_EUNSUPPORTED: as paged_decode_partial, and more than 4096 sequences (the work list
+ *   the split map needs is held in LDS).
+ */
+int paged_decode_split_partial(const void* query, int dtype,
+                               const void* key_cache, const void* value_cache, int layout,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* seq_lens,
+                               int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                               int block_size, int num_blocks, float scale, int num_splits,
+                               int max_seq_len,
+                               float* partial_acc, float* partial_m, float* partial_l,
+                               void* stream);
+int paged_decode_split_reduce(const float* partial_acc, const float* partial_m,
+                              const float* partial_l, const int32_t* seq_lens,
+                              int num_seqs, int num_heads, int head_dim,
+                              int block_size, int num_splits,
+                              void* out, int out_dtype, float* lse, void* stream);
+
+/*
+ * paged_decode -- the whole decode step in ONE launch ([FD] Decode_Paged_GQAAttention_Kernel
+ * when a sequence has one partition; otherwise its split-K kernels with the combine run by
+ * the last workgroup to finish a (sequence, kv head)).
+ *
+ * Computes what paged_decode_partial followed by paged_decode_reduce computes (or the
+ * _split_ pair when num_splits > 0; partition_size is then ignored), writing
+ *   out[b,h,:] (element type `dtype`, RNE) and lse[b,h] (natural log; lse may be NULL).
+ * A sequence with a single partition is written straight from its workgroup. For longer
+ * ones the partial arrays are scratch space owned by the caller (same shapes as for
+ * paged_decode_partial, max_num_partitions >= num_splits under the split policy), and
+ *   counters   [num_seqs * num_kv_heads] int32 of device memory, all ZERO on entry; the
+ *              launch leaves them zero again, so one zeroed buffer serves every later
+ *              call on the same stream. Calls that overlap in time need separate counters
+ *              and partial arrays.
+ * max_num_partitions == 1 is the single-pass form: every sequence is one partition whatever
+ * its length (partition_size and num_splits are then ignored) and partial_acc, partial_m,
+ * partial_l and counters may be NULL.
+ * len_b == 0 gives out = 0 and lse = -inf.
+ * PKV_EINVAL: as paged_decode_partial; NULL out; NULL partial arrays or counters when
+ *   max_num_partitions > 1.
+ * PKV_EUNSUPPORTED: as paged_decode_partial, and more than 4096 sequences.
+ */
+int paged_decode(const void* query, int dtype,
+                 const void* key_cache, const void* value_cache, int layout,
+                 const int32_t* block_tables, int max_blocks_per_seq,
+                 const int32_t* seq_lens,
+                 int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                 int block_size, int num_blocks, float scale,
+                 int partition_size, int num_splits, int max_num_partitions, int max_seq_len,
+                 float* partial_acc, float* partial_m, float* partial_l, int32_t* counters,
+                 void* out, float* lse, void* stream);
+
+/*
+ * paged_attention_v2 -- [PAv2]'s paged_attention_v2_triton launcher as a C call: both
+ * phases on `stream` with its fixed 512-token partitions and its x-packed cache layout
+ * (PKV_KV_XPACKED), keeping its normalized partial form:
+ *   max_logits[b,h,p]   = max_t s_t                      (natural-log units)
+ *   exp_sums[b,h,p]     = sum_t exp(s_t - max_logits)
+ *   tmp_output[b,h,p,:] = sum_t exp(s_t - max_logits) V_t / exp_sums   (float32)
+ *   out[b,h,:] = sum_p exp(m_p - M) exp_sums_p tmp_output_p / sum_p exp(m_p - M) exp_sums_p
+ * over the ceil(len_b / 512) partitions of sequence b (M = max_p m_p); `dtype` is the type
+ * of query, caches and out. Empty partitions get max_logits = -inf, exp_sums = 0.
+ *   out         [num_seqs, num_heads, head_size]
+ *   exp_sums, max_logits  [num_seqs, num_heads, max_num_partitions] float32
+ *   tmp_output  [num_seqs, num_heads, max_num_partitions, head_size] float32
+ *   query [num_seqs, num_heads, head_size]; key_cache [num_blocks, num_kv_heads,
+ *   head_size / x, block_size, x]; value_cache [num_blocks, num_kv_heads, head_size, block_size]
+ * [PAv2]'s launcher accepts alibi_slopes, kv_cache_dtype, k_scale and v_scale but never
+ * uses them; here alibi_slopes must be NULL (PKV_EUNSUPPORTED otherwise), and the other
+ * three have no argument (the cache is read in `dtype`, unscaled).
+ * PKV_EINVAL / PKV_EUNSUPPORTED: as paged_decode_partial with partition_size = 512.
+ */
+int paged_attention_v2(void* out, float* exp_sums, float* max_logits, float* tmp_output,
+                       const void* query, int dtype,
+                       const void* key_cache, const void* value_cache,
+                       int num_kv_heads, float scale,
+                       const int32_t* block_tables, int max_blocks_per_seq,
+                       const int32_t* seq_lens,
+                       int num_seqs, int num_heads, int head_size, int block_size,
+                       int num_blocks, int max_seq_len, int max_num_partitions,
+                       const float* alibi_slopes, void* stream);
 
 /*
  * mla_paged_prefill -- MLA causal paged prefill, page_size 1 ([MLA]).

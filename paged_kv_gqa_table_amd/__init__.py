@@ -9,10 +9,16 @@ point raises.
 Entry points (same names as the C ABI):
   paged_decode_partial(...)   split-K partials (acc, m, l) per (seq, head, partition)
   paged_decode_reduce(...)    LSE-weighted combine of the partials
+  paged_decode_split_partial(...), paged_decode_split_reduce(...)
+                              the same with NUM_SPLITS page-aligned splits per sequence
+  paged_decode(...)           the whole decode: allocates the scratch it needs and runs the
+                              one-launch C entry point (or, with one_launch=False, the two
+                              phases)
+  paged_attention_v2(...)     the PagedAttention V2 launcher (x-packed cache, 512-token
+                              partitions, normalized tmp_output / exp_sums / max_logits)
   mla_paged_prefill(...)      MLA causal paged prefill, page_size 1, base-2 LSE
-and the convenience wrapper paged_decode(...) that allocates the partials and runs both
-decode phases on the current stream. read_bandwidth(...) is a measurement helper (a
-plain streaming read of a buffer), not part of the attention path.
+read_bandwidth(...) is a measurement helper (a plain streaming read of a buffer), not part
+of the attention path.
 """
 from __future__ import annotations
 
@@ -23,8 +29,10 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["paged_decode_partial", "paged_decode_reduce", "paged_decode", "mla_paged_prefill",
-           "read_bandwidth", "lib", "library_path", "PkvError", "TOKEN_MAJOR", "XPACKED", "num_partitions"]
+__all__ = ["paged_decode_partial", "paged_decode_reduce", "paged_decode_split_partial",
+           "paged_decode_split_reduce", "paged_decode", "paged_decode_into", "paged_attention_v2",
+           "mla_paged_prefill", "read_bandwidth", "lib", "library_path", "PkvError", "TOKEN_MAJOR",
+           "XPACKED", "num_partitions"]
 
 TOKEN_MAJOR = "token_major"
 XPACKED = "xpacked"
@@ -62,6 +70,17 @@ def lib() -> ctypes.CDLL:
     L.paged_decode_partial.restype = i32
     L.paged_decode_reduce.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp, vp]
     L.paged_decode_reduce.restype = i32
+    L.paged_decode_split_partial.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                             f32, i32, i32, vp, vp, vp, vp]
+    L.paged_decode_split_partial.restype = i32
+    L.paged_decode_split_reduce.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp, vp]
+    L.paged_decode_split_reduce.restype = i32
+    L.paged_decode.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32,
+                               i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.paged_decode.restype = i32
+    L.paged_attention_v2.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, i32, vp, i32, i32, i32, i32,
+                                     i32, i32, i32, vp, vp]
+    L.paged_attention_v2.restype = i32
     L.mla_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                     f32, vp, vp, vp]
     L.mla_paged_prefill.restype = i32
@@ -124,12 +143,8 @@ def _pool_geometry(key_cache: torch.Tensor, layout: str) -> Tuple[int, int, int]
     raise ValueError(f"unknown layout {layout!r}")
 
 
-def paged_decode_partial(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
-                         block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
-                         num_kv_heads: int, partition_size: int, max_seq_len: int,
-                         partial_acc: torch.Tensor, partial_m: torch.Tensor, partial_l: torch.Tensor,
-                         layout: str = TOKEN_MAJOR) -> None:
-    """Phase 1 of split-K decode into caller-allocated partials (asynchronous)."""
+def _check_decode_inputs(query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, layout):
+    """Common checks of the decode inputs; returns (S, H, D, num_blocks, block_size)."""
     if query.dtype not in _DTYPE:
         raise ValueError(f"query dtype {query.dtype} not supported")
     _dev("query", query, ndim=3)
@@ -137,9 +152,6 @@ def paged_decode_partial(query: torch.Tensor, key_cache: torch.Tensor, value_cac
     _dev("value_cache", value_cache, query.dtype)
     _dev("block_tables", block_tables, torch.int32, 2)
     _dev("seq_lens", seq_lens, torch.int32, 1)
-    _dev("partial_acc", partial_acc, torch.float32, 4)
-    _dev("partial_m", partial_m, torch.float32, 3)
-    _dev("partial_l", partial_l, torch.float32, 3)
     S, H, D = query.shape
     nb, bs, kd = _pool_geometry(key_cache, layout)
     if kd != D:
@@ -154,18 +166,55 @@ def paged_decode_partial(query: torch.Tensor, key_cache: torch.Tensor, value_cac
         v_shape = (nb, num_kv_heads, bs, D)
     if tuple(value_cache.shape) != v_shape:
         raise ValueError(f"value_cache must be {v_shape}, got {tuple(value_cache.shape)}")
+    if seq_lens.shape[0] != S or block_tables.shape[0] != S:
+        raise ValueError("seq_lens / block_tables do not match the batch")
+    return S, H, D, nb, bs
+
+
+def _check_partials(partial_acc, partial_m, partial_l, S, H, D):
+    _dev("partial_acc", partial_acc, torch.float32, 4)
+    _dev("partial_m", partial_m, torch.float32, 3)
+    _dev("partial_l", partial_l, torch.float32, 3)
     P = partial_m.shape[2]
     if tuple(partial_acc.shape) != (S, H, P, D) or tuple(partial_m.shape) != (S, H, P) \
             or tuple(partial_l.shape) != (S, H, P):
         raise ValueError("partials must be [S, H, P, D] and [S, H, P]")
-    if seq_lens.shape[0] != S or block_tables.shape[0] != S:
-        raise ValueError("seq_lens / block_tables do not match the batch")
+    return P
+
+
+def paged_decode_partial(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                         block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                         num_kv_heads: int, partition_size: int, max_seq_len: int,
+                         partial_acc: torch.Tensor, partial_m: torch.Tensor, partial_l: torch.Tensor,
+                         layout: str = TOKEN_MAJOR) -> None:
+    """Phase 1 of split-K decode into caller-allocated partials (asynchronous)."""
+    S, H, D, nb, bs = _check_decode_inputs(query, key_cache, value_cache, block_tables, seq_lens,
+                                           num_kv_heads, layout)
+    P = _check_partials(partial_acc, partial_m, partial_l, S, H, D)
     st = lib().paged_decode_partial(
         _ptr(query), _DTYPE[query.dtype], _ptr(key_cache), _ptr(value_cache), _LAYOUT[layout],
         _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, H, num_kv_heads, D, bs, nb,
         float(scale), int(partition_size), P, int(max_seq_len), _ptr(partial_acc), _ptr(partial_m),
         _ptr(partial_l), _stream(query.device))
     _check(st, "paged_decode_partial")
+
+
+def paged_decode_split_partial(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                               block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                               num_kv_heads: int, max_seq_len: int, partial_acc: torch.Tensor,
+                               partial_m: torch.Tensor, partial_l: torch.Tensor,
+                               layout: str = TOKEN_MAJOR) -> None:
+    """Phase 1 with NUM_SPLITS page-aligned splits per sequence; num_splits is the partition
+    axis of the partials (asynchronous)."""
+    S, H, D, nb, bs = _check_decode_inputs(query, key_cache, value_cache, block_tables, seq_lens,
+                                           num_kv_heads, layout)
+    ns = _check_partials(partial_acc, partial_m, partial_l, S, H, D)
+    st = lib().paged_decode_split_partial(
+        _ptr(query), _DTYPE[query.dtype], _ptr(key_cache), _ptr(value_cache), _LAYOUT[layout],
+        _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, H, num_kv_heads, D, bs, nb,
+        float(scale), ns, int(max_seq_len), _ptr(partial_acc), _ptr(partial_m), _ptr(partial_l),
+        _stream(query.device))
+    _check(st, "paged_decode_split_partial")
 
 
 def paged_decode_reduce(partial_acc: torch.Tensor, partial_m: torch.Tensor, partial_l: torch.Tensor,
@@ -192,30 +241,146 @@ def paged_decode_reduce(partial_acc: torch.Tensor, partial_m: torch.Tensor, part
     _check(st, "paged_decode_reduce")
 
 
+def paged_decode_split_reduce(partial_acc: torch.Tensor, partial_m: torch.Tensor, partial_l: torch.Tensor,
+                              seq_lens: torch.Tensor, block_size: int, out: torch.Tensor,
+                              lse: Optional[torch.Tensor] = None) -> None:
+    """Phase 2 for NUM_SPLITS partials (num_splits = their partition axis) (asynchronous)."""
+    _dev("partial_acc", partial_acc, torch.float32, 4)
+    _dev("partial_m", partial_m, torch.float32, 3)
+    _dev("partial_l", partial_l, torch.float32, 3)
+    _dev("seq_lens", seq_lens, torch.int32, 1)
+    if out.dtype not in _DTYPE:
+        raise ValueError(f"out dtype {out.dtype} not supported")
+    _dev("out", out, ndim=3)
+    S, H, P, D = partial_acc.shape
+    if tuple(out.shape) != (S, H, D):
+        raise ValueError("out must be [S, H, D]")
+    if lse is not None:
+        _dev("lse", lse, torch.float32, 2)
+        if tuple(lse.shape) != (S, H):
+            raise ValueError("lse must be [S, H]")
+    st = lib().paged_decode_split_reduce(_ptr(partial_acc), _ptr(partial_m), _ptr(partial_l), _ptr(seq_lens),
+                                         S, H, D, int(block_size), P, _ptr(out), _DTYPE[out.dtype], _ptr(lse),
+                                         _stream(out.device))
+    _check(st, "paged_decode_split_reduce")
+
+
+def paged_decode_into(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                      block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float, num_kv_heads: int,
+                      partition_size: int, num_splits: int, max_seq_len: int, out: torch.Tensor,
+                      lse: Optional[torch.Tensor] = None, partial_acc: Optional[torch.Tensor] = None,
+                      partial_m: Optional[torch.Tensor] = None, partial_l: Optional[torch.Tensor] = None,
+                      counters: Optional[torch.Tensor] = None, layout: str = TOKEN_MAJOR) -> None:
+    """The one-launch C ``paged_decode`` into caller-allocated buffers (asynchronous).
+
+    With partials of one partition (or none) it is the single pass; otherwise ``counters``
+    ([S * num_kv_heads] int32) must be zero and is left zero."""
+    S, H, D, nb, bs = _check_decode_inputs(query, key_cache, value_cache, block_tables, seq_lens,
+                                           num_kv_heads, layout)
+    _dev("out", out, query.dtype, 3)
+    if tuple(out.shape) != (S, H, D):
+        raise ValueError("out must be [S, H, D]")
+    if lse is not None:
+        _dev("lse", lse, torch.float32, 2)
+        if tuple(lse.shape) != (S, H):
+            raise ValueError("lse must be [S, H]")
+    if partial_m is None:
+        P = 1
+    else:
+        P = _check_partials(partial_acc, partial_m, partial_l, S, H, D)
+    if counters is not None:
+        _dev("counters", counters, torch.int32, 1)
+        if counters.numel() < S * num_kv_heads:
+            raise ValueError("counters must hold num_seqs * num_kv_heads int32")
+    st = lib().paged_decode(
+        _ptr(query), _DTYPE[query.dtype], _ptr(key_cache), _ptr(value_cache), _LAYOUT[layout],
+        _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, H, num_kv_heads, D, bs, nb,
+        float(scale), int(partition_size), int(num_splits), P, int(max_seq_len), _ptr(partial_acc),
+        _ptr(partial_m), _ptr(partial_l), _ptr(counters), _ptr(out), _ptr(lse), _stream(query.device))
+    _check(st, "paged_decode")
+
+
 def paged_decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
                  block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float, num_kv_heads: int,
                  partition_size: int = 512, layout: str = TOKEN_MAJOR,
                  max_seq_len: Optional[int] = None, return_lse: bool = False,
-                 max_num_partitions: Optional[int] = None):
-    """Split-K decode: allocates the partials, runs both phases on the current stream.
+                 max_num_partitions: Optional[int] = None, num_splits: int = 0,
+                 one_launch: Optional[bool] = None):
+    """Decode attention for one new token per sequence; returns ``out`` [S, H, D] in the
+    query dtype, or ``(out, lse)``.
 
+    Partitions are ``partition_size`` tokens, or ``num_splits`` page-aligned splits per
+    sequence when num_splits > 0. ``one_launch`` runs the C ``paged_decode`` (one kernel;
+    partials and zeroed counters are allocated here as its scratch); otherwise the two
+    phases run as separate launches. By default (None) one launch is used only when every
+    sequence fits one partition (the single pass): with several partitions the launch's
+    cross-workgroup combine costs more on MI355X than the second launch it saves.
     ``max_seq_len`` defaults to ``seq_lens.max()`` (one device-to-host read).
-    Returns ``out`` [S, H, D] in the query dtype, or ``(out, lse)``.
     """
     if max_seq_len is None:
         max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0
     S, H, D = query.shape
-    P = max_num_partitions or num_partitions(max_seq_len, partition_size)
+    if num_splits > 0:
+        P = max(int(num_splits), int(max_num_partitions or 0))
+    else:
+        P = max_num_partitions or num_partitions(max_seq_len, partition_size)
+    if one_launch is None:
+        one_launch = P == 1
     dev = query.device
-    acc = torch.empty((S, H, P, D), dtype=torch.float32, device=dev)
-    m = torch.empty((S, H, P), dtype=torch.float32, device=dev)
-    l = torch.empty((S, H, P), dtype=torch.float32, device=dev)
     out = torch.empty((S, H, D), dtype=query.dtype, device=dev)
     lse = torch.empty((S, H), dtype=torch.float32, device=dev) if return_lse else None
-    paged_decode_partial(query, key_cache, value_cache, block_tables, seq_lens, scale, num_kv_heads,
-                         partition_size, max_seq_len, acc, m, l, layout=layout)
-    paged_decode_reduce(acc, m, l, seq_lens, partition_size, out, lse)
+    acc = m = l = counters = None
+    if P > 1 or not one_launch:
+        acc = torch.empty((S, H, P, D), dtype=torch.float32, device=dev)
+        m = torch.empty((S, H, P), dtype=torch.float32, device=dev)
+        l = torch.empty((S, H, P), dtype=torch.float32, device=dev)
+    if one_launch:
+        if P > 1:
+            counters = torch.zeros((S * num_kv_heads,), dtype=torch.int32, device=dev)
+        paged_decode_into(query, key_cache, value_cache, block_tables, seq_lens, scale, num_kv_heads,
+                          partition_size, num_splits, max_seq_len, out, lse, acc, m, l, counters, layout)
+    elif num_splits > 0:
+        paged_decode_split_partial(query, key_cache, value_cache, block_tables, seq_lens, scale, num_kv_heads,
+                                   max_seq_len, acc, m, l, layout=layout)
+        paged_decode_split_reduce(acc, m, l, seq_lens, _pool_geometry(key_cache, layout)[1], out, lse)
+    else:
+        paged_decode_partial(query, key_cache, value_cache, block_tables, seq_lens, scale, num_kv_heads,
+                             partition_size, max_seq_len, acc, m, l, layout=layout)
+        paged_decode_reduce(acc, m, l, seq_lens, partition_size, out, lse)
     return (out, lse) if return_lse else out
+
+
+def paged_attention_v2(out: torch.Tensor, exp_sums: torch.Tensor, max_logits: torch.Tensor,
+                       tmp_output: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                       value_cache: torch.Tensor, num_kv_heads: int, scale: float,
+                       block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
+                       max_seq_len: int, alibi_slopes: Optional[torch.Tensor] = None,
+                       kv_cache_dtype: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0,
+                       **kwargs) -> None:
+    """The PagedAttention V2 launcher's call, argument for argument (asynchronous).
+
+    x-packed caches, 512-token partitions; tmp_output holds each partition's normalized
+    average, exp_sums its l and max_logits its m. ALiBi, fp8 caches and K/V scales are
+    accepted by that launcher but unused there, and are refused here unless absent.
+    """
+    if alibi_slopes is not None:
+        raise NotImplementedError("paged_attention_v2: alibi_slopes are not supported")
+    if kv_cache_dtype != "auto" or float(k_scale) != 1.0 or float(v_scale) != 1.0:
+        raise NotImplementedError("paged_attention_v2: only kv_cache_dtype='auto' with unit k/v scales")
+    S, H, D, nb, bs = _check_decode_inputs(query, key_cache, value_cache, block_tables, seq_lens,
+                                           num_kv_heads, XPACKED)
+    if bs != int(block_size):
+        raise ValueError(f"block_size {block_size} does not match the cache ({bs})")
+    P = _check_partials(tmp_output, max_logits, exp_sums, S, H, D)
+    _dev("out", out, query.dtype, 3)
+    if tuple(out.shape) != (S, H, D):
+        raise ValueError("out must be [S, H, D]")
+    st = lib().paged_attention_v2(
+        _ptr(out), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_output), _ptr(query), _DTYPE[query.dtype],
+        _ptr(key_cache), _ptr(value_cache), int(num_kv_heads), float(scale), _ptr(block_tables),
+        block_tables.shape[1], _ptr(seq_lens), S, H, D, bs, nb, int(max_seq_len), P, None,
+        _stream(query.device))
+    _check(st, "paged_attention_v2")
 
 
 def mla_paged_prefill(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.Tensor,

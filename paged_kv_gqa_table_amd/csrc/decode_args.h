@@ -13,15 +13,36 @@ struct DecodePartialArgs {
   const int32_t* bt;      // [S, mb]
   const int32_t* lens;    // [S]
   int mb;                 // max_blocks_per_seq
+  int len_cap;            // lengths are clamped to this many tokens: min(mb * 16, P * ps), or
+                          // mb * 16 under NUM_SPLITS, so no partition index reaches P
   int S, H, KVH, D, NB;   // sizes; NB = pool blocks
   float scale_log2;       // scale * log2(e): scores are kept in base-2 units inside
-  int ps;                 // partition size in tokens (multiple of 16)
-  int ppp;                // pages per partition = ps / 16
+  int ps;                 // partition size in tokens (multiple of 16); unused when nsplit > 0
+  int ppp;                // pages per partition = ps / 16; unused when nsplit > 0
+  int nsplit;             // > 0: NUM_SPLITS policy, ceil(pages_b / nsplit) pages per partition
+  int normalize;          // != 0: store acc / l instead of acc
   int P;                  // max_num_partitions: stride of the partial arrays
-  float* acc;             // [S, H, P, D]
+  float* acc;             // [S, H, P, D]; may be null in final mode when P == 1
   float* m;               // [S, H, P]
   float* l;               // [S, H, P]
+  // Final mode (out != null): one launch computes the output. A (sequence, kv head) with a
+  // single partition writes out / lse directly; otherwise its partials are written and the
+  // last workgroup to finish one of its partitions (counted in counters[b * KVH + kvh],
+  // which it resets to 0) combines them.
+  void* out;              // [S, H, D], the query dtype
+  float* lse;             // [S, H] natural log, may be null
+  int* counters;          // [S * KVH], zero on entry and on exit; null when P == 1
 };
+
+// Tokens per partition of a sequence of len tokens: the fixed partition size, or under the
+// NUM_SPLITS policy (flash-decode post, split-K partial kernel) ceil(ceil(len / bs) / nsplit)
+// whole pages of bs tokens (at least one page, so that an empty sequence has no partitions).
+__host__ __device__ inline int part_tokens(int len, int ps, int nsplit, int bs) {
+  if (nsplit <= 0) return ps;
+  const int pages = (len + bs - 1) / bs;
+  const int ppp = (pages + nsplit - 1) / nsplit;
+  return (ppp > 0 ? ppp : 1) * bs;
+}
 
 struct DecodeReduceArgs {
   const float* acc;
@@ -29,6 +50,8 @@ struct DecodeReduceArgs {
   const float* l;
   const int32_t* lens;
   int S, H, D, ps, P;
+  int nsplit, bs;         // NUM_SPLITS policy when nsplit > 0 (see part_tokens)
+  int normalized;         // != 0: acc rows hold acc / l
   void* out;
   float* lse;             // may be null
 };

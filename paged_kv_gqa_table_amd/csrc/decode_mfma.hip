@@ -23,6 +23,7 @@
 
 #include "common.h"
 #include "decode_args.h"
+#include "decode_epilogue.h"
 #include "worklist.h"
 
 namespace pkv {
@@ -58,7 +59,7 @@ struct MfmaSmem {
   float red_l[W][16];
 };
 
-template <int D, bool XP, int W>
+template <int D, bool XP, int W, bool FINAL>
 __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const int G, const int b, const int kvh,
                                                const int p, const int len, MfmaSmem<W, D>& sm) {
   constexpr int BS = 16;
@@ -76,8 +77,9 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
   const int H = a.H;
 
   const int npages_seq = (len + BS - 1) / BS;
-  const int pg_begin = p * a.ppp;
-  const int pg_end = min(pg_begin + a.ppp, npages_seq);
+  const int ppp = uniform(part_tokens(len, a.ps, a.nsplit, BS) / BS);
+  const int pg_begin = p * ppp;
+  const int pg_end = min(pg_begin + ppp, npages_seq);
   const int n_my = pg_end - pg_begin - w > 0 ? (pg_end - pg_begin - w + W - 1) / W : 0;
   const int32_t* bt_row = a.bt + (size_t)b * a.mb;
   int pid_cache = 0;
@@ -244,7 +246,9 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
     sm.red_l[w][hl] = lsum;
   }
   __syncthreads();
-  const size_t stat_base = ((size_t)b * H + (size_t)kvh * G) * a.P + p;
+  const int nparts = FINAL ? item_parts(a, len) : 0;
+  const bool single = FINAL && nparts == 1;  // final output straight from the merge
+  const size_t bh0 = (size_t)b * H + (size_t)kvh * G;
   for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) {
     const int h = idx / D;
     const int d = idx - h * D;
@@ -258,24 +262,22 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
       o = fmaf(f, sm.red_acc[v][h][d], o);
       L = fmaf(f, sm.red_l[v][h], L);
     }
-    const size_t si = stat_base + (size_t)h * a.P;
-    a.acc[si * D + d] = o;
-    if (d == 0) {
-      a.m[si] = M * kLn2;
-      a.l[si] = L;
-    }
+    store_item_value<D, true>(a, bh0 + h, p, d, o, M, L, single);
   }
   __syncthreads();
+  if constexpr (FINAL)
+    if (nparts > 1) finish_item_fused<D, true, W>(a, b, kvh, G, nparts);
 }
 
-template <int D, bool XP, int W, bool DENSE>
+template <int D, bool XP, int W, bool DENSE, bool FINAL>
 __global__ __launch_bounds__(64 * W) void decode_partial_mfma_kernel(DecodePartialArgs a, int G, int grid_parts) {
   __shared__ MfmaSmem<W, D> sm;
   if constexpr (DENSE) {
     extern __shared__ int s_worklist[];
     __shared__ int s_wave[2 * W];
-    const DenseItems it = build_worklist<64 * W>(a.lens, a.S, a.mb * 16, a.ps, a.KVH, s_worklist, s_wave);
+    const DenseItems it = build_worklist<64 * W>(a.lens, a.S, a.len_cap, a.ps, a.nsplit, a.KVH, s_worklist, s_wave);
     write_sentinels(it, a.H, grid_parts, a.P, a.m, a.l);
+    if constexpr (FINAL) write_empty_outputs<D, true>(it, a);
     for (int item = blockIdx.x; item < it.n_items; item += gridDim.x) {
       int b, kvh, p;
       decode_item(it, item, b, kvh, p);
@@ -283,38 +285,47 @@ __global__ __launch_bounds__(64 * W) void decode_partial_mfma_kernel(DecodeParti
       kvh = uniform(kvh);
       p = uniform(p);
       int len = a.lens[b];
-      len = len > a.mb * 16 ? a.mb * 16 : len;
-      mfma_partition<D, XP, W>(a, G, b, kvh, p, uniform(len), sm);
+      len = len > a.len_cap ? a.len_cap : len;
+      mfma_partition<D, XP, W, FINAL>(a, G, b, kvh, p, uniform(len), sm);
     }
   } else {
     const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     int len = a.lens[b];
-    len = len < 0 ? 0 : (len > a.mb * 16 ? a.mb * 16 : len);
-    if (p * a.ps >= len) {
-      if ((int)threadIdx.x < G) {
+    len = len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
+    if (p * part_tokens(len, a.ps, a.nsplit, 16) >= len) {
+      if ((int)threadIdx.x < G && a.m != nullptr) {
         const size_t si = ((size_t)b * a.H + (size_t)kvh * G + threadIdx.x) * a.P + p;
         a.m[si] = kNegInf;
         a.l[si] = 0.f;
       }
+      if constexpr (FINAL)
+        if (p == 0) write_empty_rows<D, true>(a, b, kvh, G);
       return;
     }
-    mfma_partition<D, XP, W>(a, G, b, kvh, p, len, sm);
+    mfma_partition<D, XP, W, FINAL>(a, G, b, kvh, p, len, sm);
   }
 }
 
-template <int D, bool XP>
-hipError_t launch_mfma_d(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
+template <int D, bool XP, bool FINAL>
+hipError_t launch_mfma_f(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
   constexpr int W = 4;
   if (use_dense_worklist(a.S, a.KVH, grid_parts)) {
     const long upper = (long)a.S * a.KVH * grid_parts;
     const int grid = (int)(upper < dense_grid_cap() ? upper : dense_grid_cap());
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, true>), dim3(grid), dim3(64 * W),
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, true, FINAL>), dim3(grid), dim3(64 * W),
                        worklist_lds_words(a.S) * sizeof(int), s, a, G, grid_parts);
   } else {
     dim3 grid(grid_parts, a.KVH, a.S);
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, false>), grid, dim3(64 * W), 0, s, a, G, grid_parts);
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, false, FINAL>), grid, dim3(64 * W), 0, s, a, G,
+                       grid_parts);
   }
   return hipGetLastError();
+}
+
+template <int D, bool XP>
+hipError_t launch_mfma_d(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
+  return a.out != nullptr ? launch_mfma_f<D, XP, true>(a, G, grid_parts, s)
+                          : launch_mfma_f<D, XP, false>(a, G, grid_parts, s);
 }
 
 template <bool XP>

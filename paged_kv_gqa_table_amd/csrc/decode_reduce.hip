@@ -3,12 +3,14 @@
 // Computes what the flash-decode post's _flash_decode_combine_kernel computes
 // (M = max m_p, w_p = exp(m_p - M), out = sum w_p acc_p / sum w_p l_p, zeros for an
 // empty sequence), over ceil(len / ps) partitions per sequence as in the PagedAttention
-// V2 Triton page's _reduce_partitions_kernel. The optional natural-log LSE
-// M + ln(sum w_p l_p) is written as well.
+// V2 Triton page's _reduce_partitions_kernel (or the sequence's non-empty NUM_SPLITS
+// splits). The optional natural-log LSE M + ln(sum w_p l_p) is written as well. With
+// normalized partials (acc_p = acc / l, that page's tmp_output) each row weighs w_p l_p.
 //
 // Two forms, chosen by the caller's partition bound P:
-//  * P <= 16: one wave per (sequence, head); each lane owns D / 64 contiguous output dims,
-//    so every partition row of acc is one coalesced 256 B - 1 KiB read, 8 rows in flight.
+//  * P <= 16: one wave per (sequence, head) (reduce_row_wave in decode_epilogue.h, shared
+//    with the one-launch decode); each lane owns D / 64 contiguous output dims, so every
+//    partition row of acc is one coalesced 256 B - 1 KiB read, 8 rows in flight.
 //  * P > 16: one workgroup of 4 waves per (sequence, head); wave w combines its quarter of
 //    the partitions the same way (16 rows in flight), then the four waves' (max, sum,
 //    accumulator) merge through LDS with the same weighting, so a sequence of 128
@@ -19,86 +21,25 @@
 
 #include "common.h"
 #include "decode_args.h"
+#include "decode_epilogue.h"
 
 namespace pkv {
 
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeReduceArgs a) {
-  constexpr int DPL = D / 64;  // output dims per lane
-  constexpr int CH = 8;        // partition rows of acc in flight per lane
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);  // b * H + h
-  if (row >= a.S * a.H) return;
-  const int b = row / a.H;
+// Partitions of sequence b under the launch's partition map (capped at P).
+PKV_DEVICE int reduce_parts(const DecodeReduceArgs& a, int b) {
   int len = a.lens[b];
   len = len < 0 ? 0 : len;
-  int np = (len + a.ps - 1) / a.ps;
-  np = uniform(np > a.P ? a.P : np);
+  const int pt = part_tokens(len, a.ps, a.nsplit, a.bs);
+  const int np = (len + pt - 1) / pt;
+  return uniform(np > a.P ? a.P : np);
+}
 
-  float o[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) o[i] = 0.f;
-  float M = kNegInf, Z = 0.f;
-
-  if (np > 0) {
-    const float* mrow = a.m + (size_t)row * a.P;
-    const float* lrow = a.l + (size_t)row * a.P;
-    const float* arow = a.acc + (size_t)row * a.P * D + lane * DPL;
-    using VecT = typename std::conditional<DPL == 4, float4, typename std::conditional<DPL == 2, float2, float>::type>::type;
-    // m, l of the first 64 partitions (one per lane) and the first CH acc rows all go out
-    // before anything waits on them: one memory round trip for the common case.
-    const float m0 = lane < np ? mrow[lane] : kNegInf;  // partition `lane`
-    const float l0 = lane < np ? lrow[lane] : 0.f;
-    VecT buf[CH];
-#pragma unroll
-    for (int u = 0; u < CH; ++u)
-      if (u < np) buf[u] = *reinterpret_cast<const VecT*>(arow + (size_t)u * D);
-    float mv = m0;
-    for (int i = lane + 64; i < np; i += 64) mv = fmaxf(mv, mrow[i]);  // more than 64 partitions
-    M = uniform(strided_max<1>(mv));
-    const float wl = __expf(m0 - M);  // weight of partition `lane` (0 past np)
-    float zl = wl * l0;
-    for (int i = lane + 64; i < np; i += 64) zl += __expf(mrow[i] - M) * lrow[i];
-    Z = strided_sum<1>(zl);
-    for (int c0 = 0; c0 < np; c0 += CH) {
-      if (c0 > 0) {
-#pragma unroll
-        for (int u = 0; u < CH; ++u)
-          if (c0 + u < np) buf[u] = *reinterpret_cast<const VecT*>(arow + (size_t)(c0 + u) * D);
-      }
-#pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        const int pidx = c0 + u;
-        if (pidx < np) {
-          const float wgt = pidx < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), pidx))
-                                      : __expf(mrow[pidx] - M);
-          const float* f = reinterpret_cast<const float*>(&buf[u]);
-#pragma unroll
-          for (int i = 0; i < DPL; ++i) o[i] = fmaf(wgt, f[i], o[i]);
-        }
-      }
-    }
-    const float inv = 1.f / Z;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) o[i] *= inv;
-  }
-
-  const size_t ob = (size_t)row * D + lane * DPL;
-  if constexpr (OUT_BF16) {
-    uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ob;
-    if constexpr (DPL == 4) {
-      *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-    } else if constexpr (DPL == 2) {
-      *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(o[0], o[1]);
-    } else {
-      dst[0] = (uint16_t)f32_to_bf16_bits(o[0]);
-    }
-  } else {
-    float* dst = reinterpret_cast<float*>(a.out) + ob;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) dst[i] = o[i];
-  }
-  if (a.lse != nullptr && lane == 0) a.lse[row] = (np > 0) ? M + __logf(Z) : kNegInf;
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeReduceArgs a) {
+  const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);  // b * H + h
+  if (row >= a.S * a.H) return;
+  const int np = reduce_parts(a, row / a.H);
+  reduce_row_wave<D, OUT_BF16>(a.acc, a.m, a.l, a.P, np, a.normalized != 0, (size_t)row, a.out, a.lse);
 }
 
 constexpr int kReduceWaves = 4;
@@ -114,11 +55,7 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_split_kernel(
   const int w = uniform((int)(threadIdx.x >> 6));
   const int row = blockIdx.x;  // b * H + h
   if (row >= a.S * a.H) return;  // uniform over the workgroup
-  const int b = row / a.H;
-  int len = a.lens[b];
-  len = len < 0 ? 0 : len;
-  int np = (len + a.ps - 1) / a.ps;
-  np = uniform(np > a.P ? a.P : np);
+  const int np = reduce_parts(a, row / a.H);
   // this wave's partitions [p0, p1)
   const int per = (np + kReduceWaves - 1) / kReduceWaves;
   const int p0 = min(np, w * per), p1 = min(np, p0 + per);
@@ -146,6 +83,7 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_split_kernel(
     for (int i = lane + 64; i < nw; i += 64) mv = fmaxf(mv, mrow[i]);  // more than 64 partitions
     M = uniform(strided_max<1>(mv));
     const float wl = __expf(m0 - M);  // weight of partition p0 + lane (0 past the range)
+    const float cl = a.normalized ? wl * l0 : wl;  // coefficient of acc row p0 + lane
     float zl = wl * l0;
     for (int i = lane + 64; i < nw; i += 64) zl += __expf(mrow[i] - M) * lrow[i];
     Z = strided_sum<1>(zl);
@@ -159,8 +97,13 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_split_kernel(
       for (int u = 0; u < CH; ++u) {
         const int pidx = c0 + u;
         if (pidx < nw) {
-          const float wgt = pidx < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), pidx))
-                                      : __expf(mrow[pidx] - M);
+          float wgt;
+          if (pidx < 64) {
+            wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), pidx));
+          } else {
+            wgt = __expf(mrow[pidx] - M);
+            if (a.normalized) wgt *= lrow[pidx];
+          }
           const float* f = reinterpret_cast<const float*>(&buf[u]);
 #pragma unroll
           for (int i = 0; i < DPL; ++i) o[i] = fmaf(wgt, f[i], o[i]);

@@ -35,6 +35,7 @@
 
 #include "common.h"
 #include "decode_args.h"
+#include "decode_epilogue.h"
 #include "worklist.h"
 
 namespace pkv {
@@ -73,7 +74,7 @@ struct ValuSmem {
 };
 
 // One work item: partials of (b, kvh, p) for the G heads of kv head kvh.
-template <bool BF16, int D, int G, bool XP, int LPT, int W>
+template <bool BF16, int D, int G, bool XP, int LPT, int W, bool FINAL>
 __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const int b, const int kvh,
                                                const int p, const int len, ValuSmem<W, G, D, XP>& sm) {
   using C = ValuCfg<BF16, D, G, XP, LPT, W>;
@@ -87,8 +88,9 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
   const int H = a.H;
 
   const int npages_seq = (len + BS - 1) / BS;
-  const int pg_begin = p * a.ppp;
-  const int pg_end = min(pg_begin + a.ppp, npages_seq);
+  const int ppp = uniform(part_tokens(len, a.ps, a.nsplit, BS) / BS);
+  const int pg_begin = p * ppp;
+  const int pg_end = min(pg_begin + ppp, npages_seq);
   // pages of this wave: pg_begin + w + W * i, i < n_my
   const int n_my = pg_end - pg_begin - w > 0 ? (pg_end - pg_begin - w + W - 1) / W : 0;
   const int32_t* bt_row = a.bt + (size_t)b * a.mb;
@@ -404,7 +406,9 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
   }
   __syncthreads();
 
-  const size_t stat_base = ((size_t)b * H + (size_t)kvh * G) * a.P + p;  // + g * P
+  const int nparts = FINAL ? item_parts(a, len) : 0;
+  const bool single = FINAL && nparts == 1;  // final output straight from the merge
+  const size_t bh0 = (size_t)b * H + (size_t)kvh * G;
   for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) {
     const int g = idx / D;
     const int d = idx - g * D;
@@ -418,24 +422,22 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
       o = fmaf(f, sm.red_acc[v][g][d], o);
       L = fmaf(f, sm.red_l[v][g], L);
     }
-    const size_t si = stat_base + (size_t)g * a.P;
-    a.acc[si * D + d] = o;
-    if (d == 0) {
-      a.m[si] = M * kLn2;
-      a.l[si] = L;
-    }
+    store_item_value<D, BF16>(a, bh0 + g, p, d, o, M, L, single);
   }
   __syncthreads();  // LDS is reused by the next item
+  if constexpr (FINAL)
+    if (nparts > 1) finish_item_fused<D, BF16, W>(a, b, kvh, G, nparts);
 }
 
-template <bool BF16, int D, int G, bool XP, int LPT, int W, bool DENSE, int WPE>
+template <bool BF16, int D, int G, bool XP, int LPT, int W, bool DENSE, int WPE, bool FINAL>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(WPE, 8))) void decode_partial_valu_kernel(DecodePartialArgs a, int grid_parts) {
   __shared__ ValuSmem<W, G, D, XP> sm;
   if constexpr (DENSE) {
     extern __shared__ int s_worklist[];
     __shared__ int s_wave[2 * W];
-    const DenseItems it = build_worklist<64 * W>(a.lens, a.S, a.mb * 16, a.ps, a.KVH, s_worklist, s_wave);
+    const DenseItems it = build_worklist<64 * W>(a.lens, a.S, a.len_cap, a.ps, a.nsplit, a.KVH, s_worklist, s_wave);
     write_sentinels(it, a.H, grid_parts, a.P, a.m, a.l);
+    if constexpr (FINAL) write_empty_outputs<D, BF16>(it, a);
     for (int item = blockIdx.x; item < it.n_items; item += gridDim.x) {
       int b, kvh, p;
       decode_item(it, item, b, kvh, p);
@@ -443,27 +445,30 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(WPE, 8))
       kvh = uniform(kvh);
       p = uniform(p);
       int len = a.lens[b];
-      len = len > a.mb * 16 ? a.mb * 16 : len;
-      valu_partition<BF16, D, G, XP, LPT, W>(a, b, kvh, p, uniform(len), sm);
+      len = len > a.len_cap ? a.len_cap : len;
+      valu_partition<BF16, D, G, XP, LPT, W, FINAL>(a, b, kvh, p, uniform(len), sm);
     }
   } else {
     const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     int len = a.lens[b];
-    len = len < 0 ? 0 : (len > a.mb * 16 ? a.mb * 16 : len);
-    if (p * a.ps >= len) {  // empty partition: sentinel (PagedAttention V2, unused-partition branch)
-      if (threadIdx.x < G) {
+    len = len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
+    if (p * part_tokens(len, a.ps, a.nsplit, 16) >= len) {
+      // empty partition: sentinel (PagedAttention V2, unused-partition branch)
+      if (threadIdx.x < G && a.m != nullptr) {
         const size_t si = ((size_t)b * a.H + (size_t)kvh * G + threadIdx.x) * a.P + p;
         a.m[si] = kNegInf;
         a.l[si] = 0.f;
       }
+      if constexpr (FINAL)
+        if (p == 0) write_empty_rows<D, BF16>(a, b, kvh, G);
       return;
     }
-    valu_partition<BF16, D, G, XP, LPT, W>(a, b, kvh, p, len, sm);
+    valu_partition<BF16, D, G, XP, LPT, W, FINAL>(a, b, kvh, p, len, sm);
   }
 }
 
-template <bool BF16, bool XP, int D, int G>
-hipError_t launch_valu_one(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
+template <bool BF16, bool XP, int D, int G, bool FINAL>
+hipError_t launch_valu_fin(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
   constexpr int EB = BF16 ? 2 : 4;
 #ifndef PKV_VALU_ROW_BYTES_LPT16
 #define PKV_VALU_ROW_BYTES_LPT16 256
@@ -478,14 +483,20 @@ hipError_t launch_valu_one(const DecodePartialArgs& a, int grid_parts, hipStream
   if (use_dense_worklist(a.S, a.KVH, grid_parts)) {
     const long upper = (long)a.S * a.KVH * grid_parts;
     const int grid = (int)(upper < dense_grid_cap() ? upper : dense_grid_cap());
-    hipLaunchKernelGGL((decode_partial_valu_kernel<BF16, D, G, XP, LPT, W, true, WPE>), dim3(grid), dim3(64 * W),
+    hipLaunchKernelGGL((decode_partial_valu_kernel<BF16, D, G, XP, LPT, W, true, WPE, FINAL>), dim3(grid), dim3(64 * W),
                        worklist_lds_words(a.S) * sizeof(int), s, a, grid_parts);
   } else {
     dim3 grid(grid_parts, a.KVH, a.S);
-    hipLaunchKernelGGL((decode_partial_valu_kernel<BF16, D, G, XP, LPT, W, false, WPE>), grid, dim3(64 * W), 0, s,
-                       a, grid_parts);
+    hipLaunchKernelGGL((decode_partial_valu_kernel<BF16, D, G, XP, LPT, W, false, WPE, FINAL>), grid, dim3(64 * W), 0,
+                       s, a, grid_parts);
   }
   return hipGetLastError();
+}
+
+template <bool BF16, bool XP, int D, int G>
+hipError_t launch_valu_one(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
+  return a.out != nullptr ? launch_valu_fin<BF16, XP, D, G, true>(a, grid_parts, s)
+                          : launch_valu_fin<BF16, XP, D, G, false>(a, grid_parts, s);
 }
 
 template <bool BF16, bool XP, int D>

@@ -19,6 +19,7 @@
 
 #include "common.h"
 #include "decode_args.h"
+#include "decode_epilogue.h"
 #include "worklist.h"
 
 namespace pkv {
@@ -66,8 +67,12 @@ struct Bf16Smem {
 // k = 0, 1, ... of the work list; otherwise the single partition-major item first_item). While an item runs,
 // the page ids and length of the workgroup's next item are fetched, and its query rows go
 // to the other LDS buffer by DMA while the waves merge, so moving to the next item costs no
-// memory round trip before its first K/V pages go out.
-template <int D, int G, bool XP, int W, bool DENSE>
+// memory round trip before its first K/V pages go out. SPLIT: partitions follow the
+// NUM_SPLITS policy, so an item's first page depends on its sequence's length and the
+// page ids of the next item are fetched after its length (one more round trip per item).
+// FINAL: the launch produces the output (final mode of DecodePartialArgs); compiled
+// separately so that the plain partial kernel carries none of its code.
+template <int D, int G, bool XP, int W, bool DENSE, bool SPLIT, bool FINAL>
 __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const DenseItems& wl, int first_item,
                                            Bf16Smem<W, G, D>& sm) {
   using C = Bf16Cfg<D, XP>;
@@ -103,15 +108,20 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
   // is unconditional (a page past the partition or the table row reads the row's last
   // entry of the partition instead) and the value is clamped into the pool only when a
   // page address is formed, so nothing waits for it until it is used.
-  auto page_ids = [&](int b, int p, int i0) -> int {
-    const int pg_begin = p * a.ppp;
-    const int pg_last = min(a.mb, pg_begin + a.ppp) - 1;
+  auto page_ids = [&](int b, int p, int ppp, int i0) -> int {
+    const int pg_begin = p * ppp;
+    const int pg_last = min(a.mb, pg_begin + ppp) - 1;
     const int pg = min(pg_begin + w + W * (i0 + lane), pg_last);
     return a.bt[(size_t)b * a.mb + pg];
   };
   auto clamp_len = [&](int len) {
-    len = len < 0 ? 0 : (len > a.mb * BS ? a.mb * BS : len);
+    len = len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
     return uniform(len);
+  };
+  // pages per partition of a sequence of (clamped) length len
+  auto ppp_of = [&](int len) -> int {
+    if constexpr (SPLIT) return uniform(part_tokens(len, a.ps, a.nsplit, BS) / BS);
+    else return a.ppp;
   };
   // sequence length through the scalar cache: only the use waits for it
   auto len_of = [&](int b) { return ((const __attribute__((address_space(4))) int32_t*)a.lens)[b]; };
@@ -134,15 +144,25 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
   // ---- the first item: ids, length and q in one memory round trip
   int nb, nkvh, np;
   item_of(first_item, nb, nkvh, np);
-  int npid = page_ids(nb, np, 0);
+  int npid;
+  int nlen;
+  if constexpr (SPLIT) {
+    nlen = len_of(nb);
+    npid = page_ids(nb, np, ppp_of(clamp_len(nlen)), 0);
+  } else {
+    npid = page_ids(nb, np, a.ppp, 0);
+  }
   fetch_q(nb, nkvh, 0);
-  int nlen = len_of(nb);
-  if (!DENSE && np * a.ps >= clamp_len(nlen)) {  // empty partition (PagedAttention V2 page, unused-partition branch)
-    if ((int)threadIdx.x < G) {
+  if constexpr (!SPLIT) nlen = len_of(nb);
+  if (!DENSE && np * ppp_of(clamp_len(nlen)) * BS >= clamp_len(nlen)) {
+    // empty partition (PagedAttention V2 page, unused-partition branch)
+    if ((int)threadIdx.x < G && a.m != nullptr) {
       const size_t si = ((size_t)nb * H + (size_t)nkvh * G + threadIdx.x) * a.P + np;
       a.m[si] = kNegInf;
       a.l[si] = 0.f;
     }
+    if constexpr (FINAL)
+      if (np == 0) write_empty_rows<D, true>(a, nb, nkvh, G);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA may outlive the workgroup
     return;  // uniform across the workgroup
   }
@@ -155,8 +175,9 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
     // ---- the prefetched item becomes current
     const int b = nb, kvh = nkvh, p = np, len = clamp_len(nlen);
     int pid_cache = npid;
-    const int pg_begin = p * a.ppp;
-    const int pg_end = min(pg_begin + a.ppp, (len + BS - 1) / BS);
+    const int ppp = ppp_of(len);
+    const int pg_begin = p * ppp;
+    const int pg_end = min(pg_begin + ppp, (len + BS - 1) / BS);
     const int n_my = pg_end - pg_begin - w > 0 ? (pg_end - pg_begin - w + W - 1) / W : 0;
     const char* kbase = reinterpret_cast<const char*>(a.kc) + (size_t)kvh * PAGEB;
     const char* vbase = reinterpret_cast<const char*>(a.vc) + (size_t)kvh * PAGEB;
@@ -170,7 +191,7 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
       if (i >= cache_base + 64) {
         cache_base = i & ~63;
         // used at once (the clamp), so the wait for it stays inside this rare branch
-        const int id = page_ids(b, p, cache_base);
+        const int id = page_ids(b, p, ppp, cache_base);
         pid_cache = id < 0 ? 0 : (id >= a.NB ? a.NB - 1 : id);
       }
     };
@@ -220,8 +241,13 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
     const bool has_next = next_item >= 0;
     if (has_next) {
       item_of(next_item, nb, nkvh, np);
-      npid = page_ids(nb, np, 0);
-      nlen = len_of(nb);
+      if constexpr (SPLIT) {
+        nlen = len_of(nb);
+        npid = page_ids(nb, np, ppp_of(clamp_len(nlen)), 0);
+      } else {
+        npid = page_ids(nb, np, a.ppp, 0);
+        nlen = len_of(nb);
+      }
     }
 
     float acc[G][NACC];
@@ -420,7 +446,9 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
     __syncthreads();
     if (has_next) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // q landed; published by the barrier below
 
-    const size_t stat_base = ((size_t)b * H + (size_t)kvh * G) * a.P + p;
+    const int nparts = FINAL ? item_parts(a, len) : 0;
+    const bool single = FINAL && nparts == 1;  // final output straight from the merge
+    const size_t bh0 = (size_t)b * H + (size_t)kvh * G;
     for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) {
       const int g = idx / D;
       const int d = idx - g * D;
@@ -434,14 +462,11 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
         o = fmaf(f, sm.red_acc[v][g][d], o);
         L = fmaf(f, sm.red_l[v][g], L);
       }
-      const size_t si = stat_base + (size_t)g * a.P;
-      a.acc[si * D + d] = o;
-      if (d == 0) {
-        a.m[si] = M * kLn2;
-        a.l[si] = L;
-      }
+      store_item_value<D, true>(a, bh0 + g, p, d, o, M, L, single);
     }
     __syncthreads();
+    if constexpr (FINAL)
+      if (nparts > 1) finish_item_fused<D, true, W>(a, b, kvh, G, nparts);
     if (!has_next) break;
     slot ^= 1;
   }
@@ -451,18 +476,20 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
 // 128 VGPRs without spilling, else no constraint.
 constexpr int bf16_min_waves(int D, int G) { return (D == 64 && G <= 5) || (D == 128 && G <= 4) ? 4 : 1; }
 
-template <int D, int G, bool XP, int W, bool DENSE>
+template <int D, int G, bool XP, int W, bool DENSE, bool SPLIT, bool FINAL>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(bf16_min_waves(D, G), 8))) void decode_partial_bf16_kernel(DecodePartialArgs a, int grid_parts) {
   __shared__ Bf16Smem<W, G, D> sm;
   if constexpr (DENSE) {
     extern __shared__ int s_worklist[];
     __shared__ int s_wave[2 * W];
-    const DenseItems wl = build_worklist<64 * W>(a.lens, a.S, a.mb * 16, a.ps, a.KVH, s_worklist, s_wave);
+    const DenseItems wl = build_worklist<64 * W>(a.lens, a.S, a.len_cap, a.ps, SPLIT ? a.nsplit : 0, a.KVH,
+                                                 s_worklist, s_wave);
     write_sentinels(wl, a.H, grid_parts, a.P, a.m, a.l);
+    if constexpr (FINAL) write_empty_outputs<D, true>(wl, a);
     const int first = wg_item(wl, blockIdx.x, gridDim.x, 0);
-    if (first >= 0) bf16_items<D, G, XP, W, true>(a, wl, first, sm);
+    if (first >= 0) bf16_items<D, G, XP, W, true, SPLIT, FINAL>(a, wl, first, sm);
   } else {
-    bf16_items<D, G, XP, W, false>(a, DenseItems{}, blockIdx.x, sm);
+    bf16_items<D, G, XP, W, false, SPLIT, FINAL>(a, DenseItems{}, blockIdx.x, sm);
   }
 }
 
@@ -473,7 +500,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(bf16_min
 #ifndef PKV_DENSE_RATIO
 #define PKV_DENSE_RATIO 0
 #endif
-template <bool XP, int D, int G>
+template <bool XP, int D, int G, bool SPLIT, bool FINAL>
 hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
   constexpr int W = PKV_BF16_WAVES;
   const long upper = (long)a.S * a.KVH * grid_parts;
@@ -488,30 +515,42 @@ hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream
 #ifndef PKV_RESIDENT_RATIO
 #define PKV_RESIDENT_RATIO 4
 #endif
-    int cap = resident_grid(reinterpret_cast<const void*>(&decode_partial_bf16_kernel<D, G, XP, W, true>), 64 * W,
-                            lds);
+    int cap = resident_grid(reinterpret_cast<const void*>(&decode_partial_bf16_kernel<D, G, XP, W, true, SPLIT, FINAL>),
+                            64 * W, lds);
     if (upper > (long)PKV_RESIDENT_RATIO * cap) cap = dense_grid_cap();
     const int grid = (int)(upper < cap ? upper : cap);
-    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, true>), dim3(grid), dim3(64 * W), lds, s, a,
-                       grid_parts);
+    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, true, SPLIT, FINAL>), dim3(grid), dim3(64 * W), lds,
+                       s, a, grid_parts);
+  } else if constexpr (!SPLIT && !FINAL) {
+    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, false, false, false>), dim3((unsigned)upper),
+                       dim3(64 * W), 0, s, a, grid_parts);
   } else {
-    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, false>), dim3((unsigned)upper), dim3(64 * W), 0, s,
-                       a, grid_parts);
+    return hipErrorNotSupported;  // NUM_SPLITS and one-launch decode use the work list (kMaxDenseSeqs sequences)
   }
   return hipGetLastError();
+}
+
+template <bool XP, int D, int G>
+hipError_t launch_bf16_g(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
+  const bool fin = a.out != nullptr;
+  if (a.nsplit > 0)
+    return fin ? launch_bf16_one<XP, D, G, true, true>(a, grid_parts, s)
+               : launch_bf16_one<XP, D, G, true, false>(a, grid_parts, s);
+  return fin ? launch_bf16_one<XP, D, G, false, true>(a, grid_parts, s)
+             : launch_bf16_one<XP, D, G, false, false>(a, grid_parts, s);
 }
 
 template <bool XP, int D>
 hipError_t launch_bf16_d(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
   switch (G) {
-    case 1: return launch_bf16_one<XP, D, 1>(a, grid_parts, s);
-    case 2: return launch_bf16_one<XP, D, 2>(a, grid_parts, s);
-    case 3: return launch_bf16_one<XP, D, 3>(a, grid_parts, s);
-    case 4: return launch_bf16_one<XP, D, 4>(a, grid_parts, s);
-    case 5: return launch_bf16_one<XP, D, 5>(a, grid_parts, s);
-    case 6: return launch_bf16_one<XP, D, 6>(a, grid_parts, s);
-    case 7: return launch_bf16_one<XP, D, 7>(a, grid_parts, s);
-    case 8: return launch_bf16_one<XP, D, 8>(a, grid_parts, s);
+    case 1: return launch_bf16_g<XP, D, 1>(a, grid_parts, s);
+    case 2: return launch_bf16_g<XP, D, 2>(a, grid_parts, s);
+    case 3: return launch_bf16_g<XP, D, 3>(a, grid_parts, s);
+    case 4: return launch_bf16_g<XP, D, 4>(a, grid_parts, s);
+    case 5: return launch_bf16_g<XP, D, 5>(a, grid_parts, s);
+    case 6: return launch_bf16_g<XP, D, 6>(a, grid_parts, s);
+    case 7: return launch_bf16_g<XP, D, 7>(a, grid_parts, s);
+    case 8: return launch_bf16_g<XP, D, 8>(a, grid_parts, s);
     default: return hipErrorNotSupported;
   }
 }

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
+#include <algorithm>
 #include <cstdio>
 #include <mutex>
 #include <string>
@@ -36,6 +37,7 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 constexpr int kMaxGridYZ = 65535;
+constexpr int kPagedAttentionV2Partition = 512;  // the PagedAttention V2 launcher's fixed PARTITION_SIZE
 
 }  // namespace
 
@@ -91,58 +93,95 @@ int resident_grid(const void* kernel, int block_threads, size_t dyn_lds) {
 }
 }  // namespace pkv
 
-extern "C" int paged_decode_partial(const void* query, int dtype, const void* key_cache,
-                                    const void* value_cache, int layout,
-                                    const int32_t* block_tables, int max_blocks_per_seq,
-                                    const int32_t* seq_lens, int num_seqs, int num_heads,
-                                    int num_kv_heads, int head_dim, int block_size, int num_blocks,
-                                    float scale, int partition_size, int max_num_partitions,
-                                    int max_seq_len, float* partial_acc, float* partial_m,
-                                    float* partial_l, void* stream) {
-  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_EINVAL, "paged_decode_partial: unknown dtype %d", dtype);
+namespace {
+
+// Partition map and outputs of one phase-1 launch (see DecodePartialArgs).
+struct Phase1Mode {
+  int partition_size;   // tokens per partition (ignored when num_splits > 0)
+  int num_splits;       // > 0: NUM_SPLITS page-aligned policy
+  int normalize;        // store acc / l
+  void* out;            // final mode when not null
+  float* lse;
+  int* counters;
+};
+
+// Validation and dispatch shared by every decode entry point. `who` names the entry point
+// in error messages.
+int decode_phase1(const char* who, const void* query, int dtype, const void* key_cache, const void* value_cache,
+                  int layout, const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_lens,
+                  int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                  float scale, int max_num_partitions, int max_seq_len, float* partial_acc, float* partial_m,
+                  float* partial_l, const Phase1Mode& mode, void* stream) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_EINVAL, "%s: unknown dtype %d", who, dtype);
   if (layout != PKV_KV_TOKEN_MAJOR && layout != PKV_KV_XPACKED)
-    return fail(PKV_EINVAL, "paged_decode_partial: unknown layout %d", layout);
-  if (num_seqs < 0) return fail(PKV_EINVAL, "paged_decode_partial: num_seqs < 0");
+    return fail(PKV_EINVAL, "%s: unknown layout %d", who, layout);
+  if (num_seqs < 0) return fail(PKV_EINVAL, "%s: num_seqs < 0", who);
   if (num_seqs == 0) return PKV_OK;
-  if (!query || !key_cache || !value_cache || !block_tables || !seq_lens || !partial_acc ||
-      !partial_m || !partial_l)
-    return fail(PKV_EINVAL, "paged_decode_partial: NULL pointer argument");
+  const bool final_mode = mode.out != nullptr;
+  // a one-launch decode with one partition per sequence keeps no partials
+  const bool keeps_partials = !final_mode || max_num_partitions > 1;
+  if (!query || !key_cache || !value_cache || !block_tables || !seq_lens ||
+      (keeps_partials && (!partial_acc || !partial_m || !partial_l)))
+    return fail(PKV_EINVAL, "%s: NULL pointer argument", who);
+  if (final_mode && max_num_partitions > 1 && !mode.counters)
+    return fail(PKV_EINVAL, "%s: counters must not be NULL when max_num_partitions > 1", who);
   if (num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || max_num_partitions <= 0 || max_seq_len < 0)
-    return fail(PKV_EINVAL, "paged_decode_partial: sizes must be positive (max_seq_len >= 0)");
+    return fail(PKV_EINVAL, "%s: sizes must be positive (max_seq_len >= 0)", who);
   if (num_heads % num_kv_heads != 0)
-    return fail(PKV_EINVAL, "paged_decode_partial: num_heads %d is not a multiple of num_kv_heads %d",
-                num_heads, num_kv_heads);
-  if (partition_size <= 0 || partition_size % block_size != 0)
-    return fail(PKV_EINVAL, "paged_decode_partial: partition_size %d is not a positive multiple of block_size %d",
-                partition_size, block_size);
+    return fail(PKV_EINVAL, "%s: num_heads %d is not a multiple of num_kv_heads %d", who, num_heads, num_kv_heads);
+  if (mode.num_splits < 0) return fail(PKV_EINVAL, "%s: num_splits < 0", who);
+  if (mode.num_splits == 0 && keeps_partials && (mode.partition_size <= 0 || mode.partition_size % block_size != 0))
+    return fail(PKV_EINVAL, "%s: partition_size %d is not a positive multiple of block_size %d", who,
+                mode.partition_size, block_size);
   if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size)
-    return fail(PKV_EINVAL, "paged_decode_partial: max_seq_len %d exceeds max_blocks_per_seq * block_size",
-                max_seq_len);
-  const int grid_parts = (int)(((int64_t)max_seq_len + partition_size - 1) / partition_size);
-  if (grid_parts > max_num_partitions)
-    return fail(PKV_EINVAL, "paged_decode_partial: max_num_partitions %d < ceil(max_seq_len / partition_size) = %d",
-                max_num_partitions, grid_parts);
-  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "paged_decode_partial: scale is not finite");
-  if (block_size != 16)
-    return fail(PKV_EUNSUPPORTED, "paged_decode_partial: block_size %d (compiled for 16)", block_size);
+    return fail(PKV_EINVAL, "%s: max_seq_len %d exceeds max_blocks_per_seq * block_size", who, max_seq_len);
+  int grid_parts;
+  if (final_mode && !keeps_partials) {
+    grid_parts = 1;  // single pass: one partition per sequence, the partition map is not used
+  } else if (mode.num_splits > 0) {
+    grid_parts = mode.num_splits;
+    if (max_num_partitions < mode.num_splits)
+      return fail(PKV_EINVAL, "%s: max_num_partitions %d < num_splits %d", who, max_num_partitions,
+                  mode.num_splits);
+  } else {
+    grid_parts = (int)(((int64_t)max_seq_len + mode.partition_size - 1) / mode.partition_size);
+    if (grid_parts > max_num_partitions)
+      return fail(PKV_EINVAL, "%s: max_num_partitions %d < ceil(max_seq_len / partition_size) = %d", who,
+                  max_num_partitions, grid_parts);
+  }
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale is not finite", who);
+  if (block_size != 16) return fail(PKV_EUNSUPPORTED, "%s: block_size %d (compiled for 16)", who, block_size);
   const bool bf16 = dtype == PKV_BF16;
   if (!(head_dim == 64 || head_dim == 128 || (bf16 && head_dim == 256)))
-    return fail(PKV_EUNSUPPORTED, "paged_decode_partial: head_dim %d for %s", head_dim, bf16 ? "bf16" : "f32");
+    return fail(PKV_EUNSUPPORTED, "%s: head_dim %d for %s", who, head_dim, bf16 ? "bf16" : "f32");
   const int G = num_heads / num_kv_heads;
-  if (G > (bf16 ? 16 : 8))
-    return fail(PKV_EUNSUPPORTED, "paged_decode_partial: %d query heads per kv head", G);
-  if (num_kv_heads > kMaxGridYZ || num_seqs > kMaxGridYZ)
-    return fail(PKV_EUNSUPPORTED, "paged_decode_partial: grid too large");
-  if (grid_parts == 0) return PKV_OK;  // every sequence is empty: nothing is touched
+  if (G > (bf16 ? 16 : 8)) return fail(PKV_EUNSUPPORTED, "%s: %d query heads per kv head", who, G);
+  if (num_kv_heads > kMaxGridYZ || num_seqs > kMaxGridYZ) return fail(PKV_EUNSUPPORTED, "%s: grid too large", who);
+  if (grid_parts == 0 && !final_mode) return PKV_OK;  // every sequence is empty: nothing is touched
+  if (grid_parts == 0) grid_parts = 1;  // final mode still writes the empty sequences' zeros
 
   pkv::DecodePartialArgs a;
   a.q = query; a.kc = key_cache; a.vc = value_cache;
   a.bt = block_tables; a.lens = seq_lens; a.mb = max_blocks_per_seq;
   a.S = num_seqs; a.H = num_heads; a.KVH = num_kv_heads; a.D = head_dim; a.NB = num_blocks;
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.ps = partition_size; a.ppp = partition_size / block_size; a.P = max_num_partitions;
+  const int64_t table_tokens = (int64_t)max_blocks_per_seq * block_size;
+  if (final_mode && !keeps_partials) {
+    // one partition per sequence whatever its length: the whole table row
+    a.ps = (int)std::min<int64_t>(table_tokens, INT32_MAX / 2 / block_size * block_size);
+    a.nsplit = 0;
+    grid_parts = 1;
+  } else {
+    a.ps = mode.num_splits > 0 ? block_size : mode.partition_size;
+    a.nsplit = mode.num_splits;
+  }
+  a.ppp = a.ps / block_size;
+  a.len_cap = (int)std::min<int64_t>(table_tokens, a.nsplit > 0 ? table_tokens : (int64_t)max_num_partitions * a.ps);
+  a.normalize = mode.normalize;
+  a.P = max_num_partitions;
   a.acc = partial_acc; a.m = partial_m; a.l = partial_l;
+  a.out = mode.out; a.lse = mode.lse; a.counters = mode.counters;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   hipError_t e;
@@ -157,7 +196,51 @@ extern "C" int paged_decode_partial(const void* query, int dtype, const void* ke
     e = xp ? pkv::launch_decode_valu_f32_xp(a, G, grid_parts, s)
            : pkv::launch_decode_valu_f32_tm(a, G, grid_parts, s);
   }
-  return hip_status(e, "paged_decode_partial launch");
+  std::string what = std::string(who) + " launch";
+  return hip_status(e, what.c_str());
+}
+
+int decode_phase2(const char* who, const float* partial_acc, const float* partial_m, const float* partial_l,
+                  const int32_t* seq_lens, int num_seqs, int num_heads, int head_dim, int partition_size,
+                  int num_splits, int block_size, int normalized, int max_num_partitions, void* out, int out_dtype,
+                  float* lse, void* stream) {
+  if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return fail(PKV_EINVAL, "%s: unknown out_dtype %d", who, out_dtype);
+  if (num_seqs < 0 || num_heads < 0 || head_dim <= 0) return fail(PKV_EINVAL, "%s: bad sizes", who);
+  if (num_seqs == 0 || num_heads == 0) return PKV_OK;
+  if (!partial_acc || !partial_m || !partial_l || !seq_lens || !out)
+    return fail(PKV_EINVAL, "%s: NULL pointer argument", who);
+  if (num_splits < 0 || block_size <= 0 || max_num_partitions <= 0 || (num_splits == 0 && partition_size <= 0))
+    return fail(PKV_EINVAL, "%s: partition_size (or num_splits), block_size and max_num_partitions must be positive",
+                who);
+  if (!(head_dim == 64 || head_dim == 128 || head_dim == 256))
+    return fail(PKV_EUNSUPPORTED, "%s: head_dim %d", who, head_dim);
+  if ((int64_t)num_seqs * num_heads > (int64_t)INT32_MAX / 2) return fail(PKV_EUNSUPPORTED, "%s: too many rows", who);
+  pkv::DecodeReduceArgs a;
+  a.acc = partial_acc; a.m = partial_m; a.l = partial_l; a.lens = seq_lens;
+  a.S = num_seqs; a.H = num_heads; a.D = head_dim; a.P = max_num_partitions;
+  a.ps = num_splits > 0 ? block_size : partition_size;
+  a.nsplit = num_splits; a.bs = block_size; a.normalized = normalized;
+  a.out = out; a.lse = lse;
+  std::string what = std::string(who) + " launch";
+  return hip_status(pkv::launch_decode_reduce(a, out_dtype == PKV_BF16, reinterpret_cast<hipStream_t>(stream)),
+                    what.c_str());
+}
+
+}  // namespace
+
+extern "C" int paged_decode_partial(const void* query, int dtype, const void* key_cache,
+                                    const void* value_cache, int layout,
+                                    const int32_t* block_tables, int max_blocks_per_seq,
+                                    const int32_t* seq_lens, int num_seqs, int num_heads,
+                                    int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                    float scale, int partition_size, int max_num_partitions,
+                                    int max_seq_len, float* partial_acc, float* partial_m,
+                                    float* partial_l, void* stream) {
+  const Phase1Mode mode{partition_size, 0, 0, nullptr, nullptr, nullptr};
+  return decode_phase1("paged_decode_partial", query, dtype, key_cache, value_cache, layout, block_tables,
+                       max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, scale, max_num_partitions, max_seq_len, partial_acc, partial_m, partial_l, mode,
+                       stream);
 }
 
 extern "C" int paged_decode_reduce(const float* partial_acc, const float* partial_m,
@@ -165,25 +248,64 @@ extern "C" int paged_decode_reduce(const float* partial_acc, const float* partia
                                    int num_heads, int head_dim, int partition_size,
                                    int max_num_partitions, void* out, int out_dtype, float* lse,
                                    void* stream) {
-  if (out_dtype != PKV_F32 && out_dtype != PKV_BF16)
-    return fail(PKV_EINVAL, "paged_decode_reduce: unknown out_dtype %d", out_dtype);
-  if (num_seqs < 0 || num_heads < 0 || head_dim <= 0)
-    return fail(PKV_EINVAL, "paged_decode_reduce: bad sizes");
-  if (num_seqs == 0 || num_heads == 0) return PKV_OK;
-  if (!partial_acc || !partial_m || !partial_l || !seq_lens || !out)
-    return fail(PKV_EINVAL, "paged_decode_reduce: NULL pointer argument");
-  if (partition_size <= 0 || max_num_partitions <= 0)
-    return fail(PKV_EINVAL, "paged_decode_reduce: partition_size and max_num_partitions must be positive");
-  if (!(head_dim == 64 || head_dim == 128 || head_dim == 256))
-    return fail(PKV_EUNSUPPORTED, "paged_decode_reduce: head_dim %d", head_dim);
-  if ((int64_t)num_seqs * num_heads > (int64_t)INT32_MAX / 2)
-    return fail(PKV_EUNSUPPORTED, "paged_decode_reduce: too many rows");
-  pkv::DecodeReduceArgs a;
-  a.acc = partial_acc; a.m = partial_m; a.l = partial_l; a.lens = seq_lens;
-  a.S = num_seqs; a.H = num_heads; a.D = head_dim; a.ps = partition_size; a.P = max_num_partitions;
-  a.out = out; a.lse = lse;
-  return hip_status(pkv::launch_decode_reduce(a, out_dtype == PKV_BF16, reinterpret_cast<hipStream_t>(stream)),
-                    "paged_decode_reduce launch");
+  return decode_phase2("paged_decode_reduce", partial_acc, partial_m, partial_l, seq_lens, num_seqs, num_heads,
+                       head_dim, partition_size, 0, 16, 0, max_num_partitions, out, out_dtype, lse, stream);
+}
+
+extern "C" int paged_decode_split_partial(const void* query, int dtype, const void* key_cache,
+                                          const void* value_cache, int layout, const int32_t* block_tables,
+                                          int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs,
+                                          int num_heads, int num_kv_heads, int head_dim, int block_size,
+                                          int num_blocks, float scale, int num_splits, int max_seq_len,
+                                          float* partial_acc, float* partial_m, float* partial_l, void* stream) {
+  if (num_splits <= 0) return fail(PKV_EINVAL, "paged_decode_split_partial: num_splits must be positive");
+  const Phase1Mode mode{0, num_splits, 0, nullptr, nullptr, nullptr};
+  return decode_phase1("paged_decode_split_partial", query, dtype, key_cache, value_cache, layout, block_tables,
+                       max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, scale, num_splits, max_seq_len, partial_acc, partial_m, partial_l, mode, stream);
+}
+
+extern "C" int paged_decode_split_reduce(const float* partial_acc, const float* partial_m, const float* partial_l,
+                                         const int32_t* seq_lens, int num_seqs, int num_heads, int head_dim,
+                                         int block_size, int num_splits, void* out, int out_dtype, float* lse,
+                                         void* stream) {
+  if (num_splits <= 0) return fail(PKV_EINVAL, "paged_decode_split_reduce: num_splits must be positive");
+  return decode_phase2("paged_decode_split_reduce", partial_acc, partial_m, partial_l, seq_lens, num_seqs,
+                       num_heads, head_dim, 0, num_splits, block_size, 0, num_splits, out, out_dtype, lse, stream);
+}
+
+extern "C" int paged_decode(const void* query, int dtype, const void* key_cache, const void* value_cache,
+                            int layout, const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* seq_lens, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                            int block_size, int num_blocks, float scale, int partition_size, int num_splits,
+                            int max_num_partitions, int max_seq_len, float* partial_acc, float* partial_m,
+                            float* partial_l, int32_t* counters, void* out, float* lse, void* stream) {
+  if (!out) return fail(PKV_EINVAL, "paged_decode: NULL pointer argument (out)");
+  const Phase1Mode mode{partition_size, num_splits, 0, out, lse, counters};
+  return decode_phase1("paged_decode", query, dtype, key_cache, value_cache, layout, block_tables,
+                       max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, scale, max_num_partitions, max_seq_len, partial_acc, partial_m, partial_l, mode,
+                       stream);
+}
+
+extern "C" int paged_attention_v2(void* out, float* exp_sums, float* max_logits, float* tmp_output,
+                                  const void* query, int dtype, const void* key_cache, const void* value_cache,
+                                  int num_kv_heads, float scale, const int32_t* block_tables,
+                                  int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_heads,
+                                  int head_size, int block_size, int num_blocks, int max_seq_len,
+                                  int max_num_partitions, const float* alibi_slopes, void* stream) {
+  if (alibi_slopes != nullptr)
+    return fail(PKV_EUNSUPPORTED, "paged_attention_v2: alibi_slopes are not supported (pass NULL)");
+  const Phase1Mode mode{kPagedAttentionV2Partition, 0, 1, nullptr, nullptr, nullptr};
+  int st = decode_phase1("paged_attention_v2", query, dtype, key_cache, value_cache, PKV_KV_XPACKED, block_tables,
+                         max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                         num_blocks, scale, max_num_partitions, max_seq_len, tmp_output, max_logits, exp_sums, mode,
+                         stream);
+  if (st != PKV_OK) return st;
+  if (!out) return fail(PKV_EINVAL, "paged_attention_v2: NULL pointer argument (out)");
+  return decode_phase2("paged_attention_v2", tmp_output, max_logits, exp_sums, seq_lens, num_seqs, num_heads,
+                       head_size, kPagedAttentionV2Partition, 0, block_size, 1, max_num_partitions, out, dtype,
+                       nullptr, stream);
 }
 
 extern "C" int mla_paged_prefill(const void* q_nope, const void* q_pe, const void* ckv_cache,

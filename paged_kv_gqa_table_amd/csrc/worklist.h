@@ -1,6 +1,8 @@
 // Dense work list for split-K decode, built redundantly by every workgroup from seq_lens.
 //
-// A work item is one (sequence b, kv head, partition p) with p < ceil(len_b / ps). Only
+// A work item is one (sequence b, kv head, partition p) with p < ceil(len_b / ps_b), where
+// ps_b is the fixed partition size or, under the NUM_SPLITS policy, the sequence's own
+// page-aligned split size (part_tokens in decode_args.h). Only
 // real items are numbered, so a launch maps blockIdx to work without ever visiting an
 // empty partition, however skewed the batch. Items are ordered for a short tail:
 //   1. every full partition (ps tokens) of every sequence, sequence-major, then kv head,
@@ -16,6 +18,7 @@
 #pragma once
 
 #include "common.h"
+#include "decode_args.h"
 
 namespace pkv {
 
@@ -34,10 +37,11 @@ struct DenseItems {
 };
 
 // Builds the list with all NT threads of the block (s_wave: 2 * NT / 64 ints). Ends with a
-// barrier. Lengths are clamped into [0, mb_tokens].
+// barrier. Lengths are clamped into [0, mb_tokens]; partitions are ps tokens, or split per
+// sequence when nsplit > 0.
 template <int NT>
-__device__ DenseItems build_worklist(const int32_t* lens, int S, int mb_tokens, int ps, int KVH, int* lds,
-                                     int* s_wave) {
+__device__ DenseItems build_worklist(const int32_t* lens, int S, int mb_tokens, int ps, int nsplit, int KVH,
+                                     int* lds, int* s_wave) {
   constexpr int NW = NT / 64;
   int* s_full = lds;
   int* s_order = lds + S + 1;
@@ -51,8 +55,9 @@ __device__ DenseItems build_worklist(const int32_t* lens, int S, int mb_tokens, 
   for (int i = i0; i < i1; ++i) {
     int len = lens[i];
     len = len < 0 ? 0 : (len > mb_tokens ? mb_tokens : len);
-    const int nf = len / ps;
-    const int rem = len - nf * ps;
+    const int psb = part_tokens(len, ps, nsplit, 16);
+    const int nf = len / psb;
+    const int rem = len - nf * psb;
     s_full[i] = len;  // this thread's own slots: read back below without a barrier
     local_f += nf * KVH;
     local_p += rem > 0;
@@ -85,8 +90,9 @@ __device__ DenseItems build_worklist(const int32_t* lens, int S, int mb_tokens, 
   int run_p = base_p + xp - local_p;
   for (int i = i0; i < i1; ++i) {
     const int len = s_full[i];
-    const int nf = len / ps;
-    const bool has_p = len - nf * ps > 0;
+    const int psb = part_tokens(len, ps, nsplit, 16);
+    const int nf = len / psb;
+    const bool has_p = len - nf * psb > 0;
     s_full[i] = (run_f << 1) | (has_p ? 1 : 0);
     run_f += nf * KVH;
     if (has_p) s_order[run_p++] = i;
@@ -138,9 +144,11 @@ PKV_DEVICE int wg_item(const DenseItems& it, int s, int R, int k) {
   return item < it.n_items ? item : -1;
 }
 
-// Sentinel m = -inf, l = 0 for every (b, h, p) with ceil(len_b / ps) <= p < grid_parts,
-// spread over the whole grid (one pass, grid-stride).
+// Sentinel m = -inf, l = 0 for every (b, h, p) with ceil(len_b / ps_b) <= p < grid_parts,
+// spread over the whole grid (one pass, grid-stride). Nothing when m is null (the final
+// mode with a single partition keeps no partials).
 PKV_DEVICE void write_sentinels(const DenseItems& it, int H, int grid_parts, int P, float* m, float* l) {
+  if (m == nullptr) return;
   const long total = (long)it.S * H * grid_parts;
   const long stride = (long)gridDim.x * blockDim.x;
   for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {

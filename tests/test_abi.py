@@ -144,3 +144,58 @@ def test_python_layer_maps_statuses(L):
     with pytest.raises((ValueError, TypeError)):
         pkv.paged_decode_partial(torch.zeros(2, 8, 128), None, None, None, None, 0.1, 2, 512, 128,
                                  None, None, None)
+
+
+def _one_launch(L, **kw):
+    a = dict(query=FAKE, dtype=1, kc=FAKE, vc=FAKE, layout=0, bt=FAKE, mb=8, lens=FAKE, S=2, H=8, KVH=2,
+             D=128, bs=16, nb=64, scale=0.1, ps=64, ns=0, P=2, max_seq_len=128, acc=FAKE, m=FAKE, l=FAKE,
+             ctr=FAKE, out=FAKE, lse=None, stream=None)
+    a.update(kw)
+    return L.paged_decode(a["query"], a["dtype"], a["kc"], a["vc"], a["layout"], a["bt"], a["mb"], a["lens"],
+                          a["S"], a["H"], a["KVH"], a["D"], a["bs"], a["nb"], a["scale"], a["ps"], a["ns"], a["P"],
+                          a["max_seq_len"], a["acc"], a["m"], a["l"], a["ctr"], a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=None), EINVAL),                         # the one-launch decode needs out
+    (dict(ctr=None), EINVAL),                         # more than one partition needs counters
+    (dict(acc=None), EINVAL),                         # ... and the partial arrays
+    (dict(ns=-1), EINVAL),
+    (dict(ns=3, P=2), EINVAL),                        # fewer partitions than splits
+    (dict(P=1, max_seq_len=128, ps=64, acc=None, m=None, l=None, out=None), EINVAL),
+    (dict(bs=8, mb=16, ps=64), EUNSUP),
+    (dict(D=96), EUNSUP),
+    (dict(S=0), OK),                                  # empty batch: nothing to do
+])
+def test_one_launch_decode_validation(L, kw, code):
+    assert _one_launch(L, **kw) == code, L.pkv_last_error()
+
+
+def test_one_launch_single_pass_needs_no_partials(L):
+    # one partition per sequence: NULL partials and counters pass validation; S = 0 keeps
+    # the call from launching anything
+    assert _one_launch(L, P=1, acc=None, m=None, l=None, ctr=None, S=0) == OK
+
+
+def test_split_entry_points_validation(L):
+    args = [FAKE, 1, FAKE, FAKE, 0, FAKE, 8, FAKE, 2, 8, 2, 128, 16, 64, 0.1]
+    assert L.paged_decode_split_partial(*args, 0, 128, FAKE, FAKE, FAKE, None) == EINVAL   # num_splits = 0
+    assert L.paged_decode_split_partial(*args, 4, 200, FAKE, FAKE, FAKE, None) == EINVAL   # max_seq_len > table
+    args[12] = 32
+    assert L.paged_decode_split_partial(*args, 4, 128, FAKE, FAKE, FAKE, None) == EUNSUP   # block_size 32
+    assert L.paged_decode_split_reduce(FAKE, FAKE, FAKE, FAKE, 2, 8, 128, 16, 0, FAKE, 1, None, None) == EINVAL
+    assert L.paged_decode_split_reduce(FAKE, FAKE, FAKE, FAKE, 2, 8, 96, 16, 4, FAKE, 1, None, None) == EUNSUP
+    assert L.paged_decode_split_reduce(FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 16, 4, FAKE, 1, None, None) == OK
+
+
+def test_paged_attention_v2_validation(L):
+    def call(alibi=None, D=128, bs=16, P=1, max_seq_len=512, H=8):
+        return L.paged_attention_v2(FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 2, 0.1, FAKE, 32, FAKE, 2, H, D, bs,
+                                    64, max_seq_len, P, alibi, None)
+    assert call(alibi=FAKE) == EUNSUP        # ALiBi slopes: accepted by the page's launcher, unused there
+    assert call(P=1, max_seq_len=513) == EINVAL  # 512-token partitions: 513 tokens need two
+    assert call(H=7) == EINVAL               # 7 heads over 2 kv heads
+    assert call(D=96) == EUNSUP
+    with pytest.raises(NotImplementedError):
+        pkv.paged_attention_v2(None, None, None, None, None, None, None, 2, 0.1, None, None, 16, 0,
+                               alibi_slopes=object())
