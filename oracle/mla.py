@@ -1,4 +1,5 @@
-"""Oracle for MLA causal paged prefill with page_size 1 and a base-2 LSE.
+"""Oracle for MLA causal paged prefill with a base-2 LSE (page_size 1, and pages of
+several tokens).
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -17,6 +18,12 @@ kernel (``_mla_paged_prefill_causal_h16_ckv512_kpe64_ps1_kernel`` and its
   * kv_len = 0 gives O = 0 and lse = -inf (the page's empty-KV branch). More
     generally any row that sees no key (prefix + i < 0, which only a caller that
     breaks kv_len >= q_len can produce) gets O = 0 and lse = -inf.
+
+Pages of ps > 1 tokens (the page's kernel takes a PAGE_SIZE but its host wrapper
+asserts 1; the plainest reading of its page-counting kv_indptr): batch b owns pages
+kv_indices[kv_indptr[b] .. kv_indptr[b+1]-1] in order, every page holds ps tokens
+except the last, which holds kv_last_page_len[b] (ps when no such array is given);
+key token j sits at slot j % ps of page kv_indices[kv_indptr[b] + j // ps].
 """
 from __future__ import annotations
 
@@ -34,8 +41,10 @@ def _logits(qn_row: np.ndarray, qp_row: np.ndarray, Kc: np.ndarray, Kp: np.ndarr
 
 
 def mla_prefill(q_nope, q_pe, ckv_cache, kpe_cache, qo_indptr, kv_indptr, kv_indices,
-                sm_scale: float):
-    """Returns (O [total_q, H, ckv_dim], lse2 [total_q, H]) in float64."""
+                sm_scale: float, kv_last_page_len=None):
+    """Returns (O [total_q, H, ckv_dim], lse2 [total_q, H]) in float64.
+
+    ckv_cache is [num_pages, ps, ckv_dim] and kpe_cache [num_pages, ps, kpe_dim]."""
     qn = _as_f64(q_nope)
     qp = _as_f64(q_pe)
     ckv = _as_f64(ckv_cache)
@@ -43,8 +52,10 @@ def mla_prefill(q_nope, q_pe, ckv_cache, kpe_cache, qo_indptr, kv_indptr, kv_ind
     qo = _as_int(qo_indptr)
     kvp = _as_int(kv_indptr)
     idx = _as_int(kv_indices)
-    if ckv.shape[1] != 1 or kpe.shape[1] != 1:
-        raise ValueError("page_size must be 1")
+    ps = ckv.shape[1]
+    if kpe.shape[1] != ps:
+        raise ValueError("ckv and kpe pages must hold the same number of tokens")
+    last_len = None if kv_last_page_len is None else _as_int(kv_last_page_len)
     total_q, H, Dc = qn.shape
     O = np.zeros((total_q, H, Dc))
     lse2 = np.full((total_q, H), -np.inf)
@@ -52,12 +63,15 @@ def mla_prefill(q_nope, q_pe, ckv_cache, kpe_cache, qo_indptr, kv_indptr, kv_ind
     for b in range(len(qo) - 1):
         q0, q1 = int(qo[b]), int(qo[b + 1])
         k0, k1 = int(kvp[b]), int(kvp[b + 1])
-        q_len, kv_len = q1 - q0, k1 - k0
+        n_pages = k1 - k0
+        last = ps if last_len is None else int(last_len[b])
+        q_len, kv_len = q1 - q0, (n_pages - 1) * ps + last if n_pages > 0 else 0
         if q_len == 0 or kv_len == 0:
             continue
-        tok = idx[k0:k1]
-        Kc = ckv[tok, 0, :]
-        Kp = kpe[tok, 0, :]
+        pages = idx[k0:k1]
+        j = np.arange(kv_len)
+        Kc = ckv[pages[j // ps], j % ps, :]
+        Kp = kpe[pages[j // ps], j % ps, :]
         prefix = kv_len - q_len
         for i in range(q_len):
             r = q0 + i

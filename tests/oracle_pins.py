@@ -493,10 +493,78 @@ def pin_mla_special_cases(orc):
     assert np.all(O[:2] == 0.0) and np.all(L[:2] == -np.inf)
 
 
+def paged_mla_pool(ckv1, kpe1, kv_lens, starts, ps, rng, extra_pages=2):
+    """Scatter per-batch token rows of a one-token-per-page pool into pages of ps tokens,
+    element by element: batch b's token j (row starts[b] + j of ckv1 / kpe1) goes to slot
+    j % ps of its (j // ps)-th page; pages are handed out by a random permutation and every
+    slot never written stays NaN. Returns (ckv, kpe, kv_indptr in pages, kv_indices,
+    kv_last_page_len)."""
+    Dc, Dp = ckv1.shape[2], kpe1.shape[2]
+    n_pages_b = [-(-int(n) // ps) for n in kv_lens]
+    total = sum(n_pages_b) + extra_pages
+    perm = rng.permutation(total)
+    ckv = np.full((total, ps, Dc), np.nan)
+    kpe = np.full((total, ps, Dp), np.nan)
+    indptr = [0]
+    indices = []
+    last = []
+    cur = 0
+    for b, n in enumerate(kv_lens):
+        pages = perm[cur:cur + n_pages_b[b]]
+        cur += n_pages_b[b]
+        indices.extend(int(x) for x in pages)
+        indptr.append(len(indices))
+        last.append(int(n) - (n_pages_b[b] - 1) * ps if n_pages_b[b] else ps)
+        for j in range(int(n)):
+            for d in range(Dc):
+                ckv[pages[j // ps], j % ps, d] = ckv1[starts[b] + j, 0, d]
+            for d in range(Dp):
+                kpe[pages[j // ps], j % ps, d] = kpe1[starts[b] + j, 0, d]
+    return ckv, kpe, np.asarray(indptr), np.asarray(indices, dtype=np.int64), np.asarray(last)
+
+
+def pin_mla_multi_token_pages(orc):
+    """Pages of 2, 3, 4 and 16 tokens (last pages partly filled, NaN elsewhere) against
+    float64 SDPA over the same tokens laid out one per row."""
+    q_lens, prefixes = [3, 1, 7, 4, 2], [5, 0, 0, 11, 30]
+    kv_lens = [a + b for a, b in zip(q_lens, prefixes)]
+    rng = np.random.default_rng(37)
+    H, Dc, Dp = 3, 8, 4
+    T = sum(q_lens)
+    N = sum(kv_lens)
+    qn = rng.standard_normal((T, H, Dc))
+    qp = rng.standard_normal((T, H, Dp))
+    ckv1 = rng.standard_normal((N, 1, Dc))
+    kpe1 = rng.standard_normal((N, 1, Dp))
+    qo = np.concatenate([[0], np.cumsum(q_lens)])
+    starts = np.concatenate([[0], np.cumsum(kv_lens)])
+    sm = 0.37
+    for ps in (2, 3, 4, 16):
+        ckv, kpe, kvp, idx, last = paged_mla_pool(ckv1, kpe1, kv_lens, starts, ps, rng)
+        O, L = orc.mla_prefill(qn, qp, ckv, kpe, qo, kvp, idx, sm, kv_last_page_len=last)
+        for b in range(len(q_lens)):
+            r0, r1 = qo[b], qo[b + 1]
+            tok = np.arange(starts[b], starts[b + 1])
+            ro, rl = _sdpa_rows(qn[r0:r1], qp[r0:r1], ckv1, kpe1, tok, r1 - r0, sm)
+            _close(O[r0:r1], ro, 1e-12, what=f"mla ps={ps} O b={b}")
+            _close(L[r0:r1], rl, 1e-12, what=f"mla ps={ps} lse b={b}")
+    # full pages: no last-page array needed
+    kv_full = [8, 4]
+    st = np.array([0, 8, 12])
+    ckv, kpe, kvp, idx, last = paged_mla_pool(ckv1, kpe1, kv_full, st, 4, rng)
+    qo2 = np.array([0, 2, 3])
+    O, L = orc.mla_prefill(qn[:3], qp[:3], ckv, kpe, qo2, kvp, idx, sm)
+    for b in range(2):
+        ro, rl = _sdpa_rows(qn[qo2[b]:qo2[b + 1]], qp[qo2[b]:qo2[b + 1]], ckv1, kpe1,
+                            np.arange(st[b], st[b + 1]), qo2[b + 1] - qo2[b], sm)
+        _close(O[qo2[b]:qo2[b + 1]], ro, 1e-12, what="mla full pages O")
+        _close(L[qo2[b]:qo2[b + 1]], rl, 1e-12, what="mla full pages lse")
+
+
 DECODE_PINS = [pin_decode_worked_example, pin_reduce_worked_example, pin_decode_brute_force,
                pin_decode_special_cases, pin_split_invariance, pin_partition_stats,
                pin_sentinel_padding, pin_page_permutation, pin_empty_sequence, pin_split_policy,
                pin_normalized_partials]
 MLA_PINS = [pin_mla_worked_example, pin_mla_sdpa, pin_mla_causal_perturbation,
-            pin_mla_special_cases]
+            pin_mla_special_cases, pin_mla_multi_token_pages]
 ALL_PINS = DECODE_PINS + MLA_PINS

@@ -54,8 +54,15 @@ MUTATIONS = [
     ("mla.py", "lse2[r] = (M[:, 0] + np.log(Z[:, 0])) / ln2", "lse2[r] = (M[:, 0] + np.log(Z[:, 0]))", 0,
      "natural-log lse"),
     ("mla.py", "prefix = kv_len - q_len\n", "prefix = 0\n", 0, "top-left causal alignment"),
-    ("mla.py", "Kc = ckv[tok, 0, :]", "Kc = ckv[np.sort(tok), 0, :]", 0, "kv_indices order ignored"),
-    ("mla.py", "tok = idx[k0:k1]", "tok = idx[q0:q0 + kv_len]", 0, "qo_indptr used for keys"),
+    ("mla.py", "Kc = ckv[pages[j // ps], j % ps, :]", "Kc = ckv[np.sort(pages)[j // ps], j % ps, :]", 0,
+     "kv_indices order ignored"),
+    ("mla.py", "pages = idx[k0:k1]", "pages = idx[q0:q0 + n_pages]", 0, "qo_indptr used for keys"),
+    ("mla.py", "Kc = ckv[pages[j // ps], j % ps, :]", "Kc = ckv[pages[j // ps], (j + 1) % ps, :]", 0,
+     "page slot off by one"),
+    ("mla.py", "Kp = kpe[pages[j // ps], j % ps, :]", "Kp = kpe[pages[j // ps], 0, :]", 0, "kpe from slot 0"),
+    ("mla.py", "(n_pages - 1) * ps + last", "n_pages * ps", 0, "last page length ignored"),
+    ("mla.py", "Kc = ckv[pages[j // ps], j % ps, :]", "Kc = ckv[pages[j % ps], j % ps, :]", 0,
+     "page index from the slot"),
     ("mla.py", "O[r] = (e @ Kc[:vis]) / Z", "O[r] = (e @ Kc[:vis]) / Z.sum()", 0, "normalization across heads"),
 ]
 
