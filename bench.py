@@ -167,8 +167,18 @@ def bench_mla(case, steps, warmup):
     out = torch.empty_like(t["q_nope"])
     lse = torch.empty(t["q_nope"].shape[:2], dtype=torch.float32, device=dev)
     mql = case.max_q_len
+    paged = case.kv_last_page_len is not None
+    if paged:  # pages of several tokens: index scratch allocated once, outside the timing
+        last = case.kv_last_page_len.to(dev)
+        tok_indptr = torch.empty((case.batch + 1,), dtype=torch.int32, device=dev)
+        tok_rows = torch.empty((case.kv_indices.numel() * case.page_size,), dtype=torch.int32, device=dev)
 
     def step():
+        if paged:
+            pkv.mla_paged_prefill_pages(t["q_nope"], t["q_pe"], t["ckv_cache"], t["kpe_cache"], t["qo_indptr"],
+                                        t["kv_indptr"], t["kv_indices"], last, case.sm_scale, mql, tok_indptr,
+                                        tok_rows, out, lse)
+            return
         pkv.mla_paged_prefill(t["q_nope"], t["q_pe"], t["ckv_cache"], t["kpe_cache"], t["qo_indptr"],
                               t["kv_indptr"], t["kv_indices"], case.sm_scale, max_q_len=mql, out=out, lse=lse)
 
@@ -361,6 +371,11 @@ def main():
             rm = bench_mla(mc, 20, 3)
             extra["mla_prefill_b8"] = {"us": rm["ms"] * 1e3, "TFLOP_s": rm["tflops"],
                                        "frac_of_bf16_mfma_peak": rm["tflops"] / BF16_MFMA_PEAK_TFLOPS}
+            del mc
+            mp = inputs.mla_prefill_b8_pages(16)
+            rp = bench_mla(mp, 20, 3)
+            extra["mla_prefill_b8_pages16"] = {"us": rp["ms"] * 1e3, "TFLOP_s": rp["tflops"],
+                                               "frac_of_bf16_mfma_peak": rp["tflops"] / BF16_MFMA_PEAK_TFLOPS}
         except NotImplementedError as e:
             extra["mla_prefill_b8"] = {"error": str(e)}
         result["extra"] = extra

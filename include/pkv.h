@@ -12,6 +12,7 @@
  *   paged_attention_v2    [PAv2]'s launcher: x-packed cache, 512-token partitions,
  *                         normalized partials (tmp_output, exp_sums, max_logits)
  *   mla_paged_prefill     MLA causal paged prefill (page_size 1), base-2 LSE
+ *   mla_paged_prefill_pages  the same over pages of several tokens
  * and a measurement helper, pkv_read_bandwidth (a plain streaming read of a buffer),
  * that no part of the attention path uses.
  *
@@ -265,6 +266,38 @@ int mla_paged_prefill(const void* q_nope, const void* q_pe,
                       int batch, int total_q, int max_q_len, int num_pages,
                       int num_heads, int ckv_dim, int kpe_dim, int page_size,
                       float sm_scale, void* out, float* lse, void* stream);
+
+/*
+ * mla_paged_prefill_pages -- mla_paged_prefill over pages of page_size >= 1 tokens.
+ *
+ * [MLA]'s kernel takes a PAGE_SIZE but its host wrapper asserts 1; this is the plainest
+ * reading of its page-counting kv_indptr: batch b owns pages
+ * kv_indices[kv_indptr[b] .. kv_indptr[b+1]-1] in order, every page holds page_size tokens
+ * except the last, which holds kv_last_page_len[b] (page_size when kv_last_page_len is
+ * NULL), so kv_len = (pages - 1) * page_size + last; key token j is slot j % page_size of
+ * page kv_indices[kv_indptr[b] + j / page_size]. Everything else (causal alignment, logits,
+ * output, base-2 LSE, empty rows) is as in mla_paged_prefill.
+ *   ckv_cache [num_pages, page_size, 512] bf16    kpe_cache [num_pages, page_size, 64] bf16
+ *   kv_indptr [batch + 1] int32 in pages, kv_indptr[batch] = num_kv_indices
+ *   kv_indices [num_kv_indices] int32 page ids in [0, num_pages)
+ *   kv_last_page_len [batch] int32 in [1, page_size], or NULL
+ *   token_indptr [batch + 1] int32, token_rows [num_kv_indices * page_size] int32: device
+ *              scratch owned by the caller; a first small kernel writes the token offsets
+ *              and the pool row (page * page_size + slot) of every token there, then the
+ *              page_size-1 prefill kernel runs on the pool viewed as
+ *              [num_pages * page_size, 1, dim]. Their contents after the call are unspecified.
+ * PKV_EINVAL / PKV_EUNSUPPORTED: as mla_paged_prefill (any page_size >= 1 is accepted), NULL
+ *   scratch, num_pages * page_size or num_kv_indices * page_size of 2^31 or more.
+ */
+int mla_paged_prefill_pages(const void* q_nope, const void* q_pe,
+                            const void* ckv_cache, const void* kpe_cache,
+                            const int32_t* qo_indptr, const int32_t* kv_indptr,
+                            const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                            int batch, int total_q, int max_q_len, int num_pages,
+                            int num_kv_indices, int num_heads, int ckv_dim, int kpe_dim,
+                            int page_size, float sm_scale,
+                            int32_t* token_indptr, int32_t* token_rows,
+                            void* out, float* lse, void* stream);
 
 /* Measurement helper, not part of the attention path: reads `bytes` bytes of device memory
  * at `buf` once, as a plain streaming read (16-byte loads, grid-stride over the buffer), on

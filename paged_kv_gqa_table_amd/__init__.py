@@ -16,7 +16,8 @@ Entry points (same names as the C ABI):
                               phases)
   paged_attention_v2(...)     the PagedAttention V2 launcher (x-packed cache, 512-token
                               partitions, normalized tmp_output / exp_sums / max_logits)
-  mla_paged_prefill(...)      MLA causal paged prefill, page_size 1, base-2 LSE
+  mla_paged_prefill(...)      MLA causal paged prefill, base-2 LSE (page_size 1, or pages of
+                              several tokens through mla_paged_prefill_pages)
 read_bandwidth(...) is a measurement helper (a plain streaming read of a buffer), not part
 of the attention path.
 """
@@ -31,7 +32,7 @@ import torch
 
 __all__ = ["paged_decode_partial", "paged_decode_reduce", "paged_decode_split_partial",
            "paged_decode_split_reduce", "paged_decode", "paged_decode_into", "paged_attention_v2",
-           "mla_paged_prefill", "read_bandwidth", "lib", "library_path", "PkvError", "TOKEN_MAJOR",
+           "mla_paged_prefill", "mla_paged_prefill_pages", "read_bandwidth", "lib", "library_path", "PkvError", "TOKEN_MAJOR",
            "XPACKED", "num_partitions"]
 
 TOKEN_MAJOR = "token_major"
@@ -84,6 +85,9 @@ def lib() -> ctypes.CDLL:
     L.mla_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                     f32, vp, vp, vp]
     L.mla_paged_prefill.restype = i32
+    L.mla_paged_prefill_pages.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                          i32, f32, vp, vp, vp, vp, vp]
+    L.mla_paged_prefill_pages.restype = i32
     L.pkv_read_bandwidth.argtypes = [vp, ctypes.c_size_t, vp, vp]
     L.pkv_read_bandwidth.restype = i32
     L.pkv_last_error.argtypes = []
@@ -386,11 +390,15 @@ def paged_attention_v2(out: torch.Tensor, exp_sums: torch.Tensor, max_logits: to
 def mla_paged_prefill(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.Tensor,
                       kpe_cache: torch.Tensor, qo_indptr: torch.Tensor, kv_indptr: torch.Tensor,
                       kv_indices: torch.Tensor, sm_scale: float, max_q_len: Optional[int] = None,
-                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      kv_last_page_len: Optional[torch.Tensor] = None):
     """MLA causal paged prefill. Returns (out [total_q, H, ckv] bf16, lse [total_q, H] base 2).
 
     Same argument order as the page's ``_forward``. ``max_q_len`` defaults to the largest
     q_len in ``qo_indptr`` (one device-to-host read, as the page's host-side batch map).
+    Caches of ``[num_pages, page_size, dim]`` with page_size > 1 (or a
+    ``kv_last_page_len``) go through ``mla_paged_prefill_pages`` with its index scratch
+    allocated here.
     """
     _dev("q_nope", q_nope, torch.bfloat16, 3)
     _dev("q_pe", q_pe, torch.bfloat16, 3)
@@ -416,12 +424,50 @@ def mla_paged_prefill(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch
         lse = torch.empty((total_q, H), dtype=torch.float32, device=q_nope.device)
     _dev("out", out, torch.bfloat16, 3)
     _dev("lse", lse, torch.float32, 2)
+    if page_size > 1 or kv_last_page_len is not None:
+        n_idx = kv_indices.numel()
+        tok_indptr = torch.empty((batch + 1,), dtype=torch.int32, device=q_nope.device)
+        tok_rows = torch.empty((max(1, n_idx * page_size),), dtype=torch.int32, device=q_nope.device)
+        mla_paged_prefill_pages(q_nope, q_pe, ckv_cache, kpe_cache, qo_indptr, kv_indptr, kv_indices,
+                                kv_last_page_len, sm_scale, int(max_q_len), tok_indptr, tok_rows, out, lse)
+        return out, lse
     st = lib().mla_paged_prefill(_ptr(q_nope), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache),
                                  _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices), batch, total_q,
                                  int(max_q_len), num_pages, H, Dc, Dp, page_size, float(sm_scale),
                                  _ptr(out), _ptr(lse), _stream(q_nope.device))
     _check(st, "mla_paged_prefill")
     return out, lse
+
+
+def mla_paged_prefill_pages(q_nope, q_pe, ckv_cache, kpe_cache, qo_indptr, kv_indptr, kv_indices,
+                            kv_last_page_len, sm_scale: float, max_q_len: int, token_indptr: torch.Tensor,
+                            token_rows: torch.Tensor, out: torch.Tensor, lse: torch.Tensor) -> None:
+    """MLA prefill over pages of several tokens into caller buffers (asynchronous);
+    token_indptr [batch + 1] and token_rows [num_kv_indices * page_size] int32 are scratch."""
+    for n, t in (("q_nope", q_nope), ("q_pe", q_pe), ("ckv_cache", ckv_cache), ("kpe_cache", kpe_cache),
+                 ("out", out)):
+        _dev(n, t, torch.bfloat16, 3)
+    for n, t in (("qo_indptr", qo_indptr), ("kv_indptr", kv_indptr), ("kv_indices", kv_indices),
+                 ("token_indptr", token_indptr), ("token_rows", token_rows)):
+        _dev(n, t, torch.int32, 1)
+    _dev("lse", lse, torch.float32, 2)
+    if kv_last_page_len is not None:
+        _dev("kv_last_page_len", kv_last_page_len, torch.int32, 1)
+    total_q, H, Dc = q_nope.shape
+    Dp = q_pe.shape[2]
+    num_pages, page_size, _ = ckv_cache.shape
+    batch = qo_indptr.shape[0] - 1
+    n_idx = kv_indices.numel()
+    if token_indptr.numel() < batch + 1 or token_rows.numel() < n_idx * page_size:
+        raise ValueError("token_indptr / token_rows scratch too small")
+    if kv_last_page_len is not None and kv_last_page_len.numel() < batch:
+        raise ValueError("kv_last_page_len must hold one entry per batch")
+    st = lib().mla_paged_prefill_pages(
+        _ptr(q_nope), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache), _ptr(qo_indptr), _ptr(kv_indptr),
+        _ptr(kv_indices), _ptr(kv_last_page_len), batch, total_q, int(max_q_len), num_pages, n_idx, H, Dc, Dp,
+        page_size, float(sm_scale), _ptr(token_indptr), _ptr(token_rows), _ptr(out), _ptr(lse),
+        _stream(q_nope.device))
+    _check(st, "mla_paged_prefill_pages")
 
 
 def read_bandwidth(buf: torch.Tensor, sink: torch.Tensor) -> None:

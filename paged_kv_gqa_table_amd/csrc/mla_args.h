@@ -24,6 +24,18 @@ struct MlaArgs {
 
 hipError_t launch_mla_prefill(const MlaArgs& a, hipStream_t s);
 
+// Pages of several tokens: token-level offsets and pool rows for the prefill kernel above.
+struct MlaPagesArgs {
+  const int32_t* kv_indptr;         // [batch + 1] in pages
+  const int32_t* kv_indices;        // [num_kv_indices] page ids
+  const int32_t* last_len;          // [batch] tokens in each batch's last page, or null (full)
+  int batch, num_kv_indices, num_pages, ps;
+  int32_t* tok_indptr;              // [batch + 1] out: token offsets
+  int32_t* tok_rows;                // [num_kv_indices * ps] out: pool row (page * ps + slot) per token
+};
+
+hipError_t launch_mla_expand_pages(const MlaPagesArgs& a, hipStream_t s);
+
 // Workgroup cap for persistent-style grids on the current device (host side).
 int dense_grid_cap();
 

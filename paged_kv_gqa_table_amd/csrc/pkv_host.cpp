@@ -339,6 +339,47 @@ extern "C" int mla_paged_prefill(const void* q_nope, const void* q_pe, const voi
   return hip_status(pkv::launch_mla_prefill(a, reinterpret_cast<hipStream_t>(stream)), "mla_paged_prefill launch");
 }
 
+extern "C" int mla_paged_prefill_pages(const void* q_nope, const void* q_pe, const void* ckv_cache,
+                                       const void* kpe_cache, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                       const int32_t* kv_indices, const int32_t* kv_last_page_len, int batch,
+                                       int total_q, int max_q_len, int num_pages, int num_kv_indices,
+                                       int num_heads, int ckv_dim, int kpe_dim, int page_size, float sm_scale,
+                                       int32_t* token_indptr, int32_t* token_rows, void* out, float* lse,
+                                       void* stream) {
+  if (batch < 0 || total_q < 0 || max_q_len < 0 || num_pages < 0 || num_kv_indices < 0 || num_heads <= 0 ||
+      ckv_dim <= 0 || kpe_dim <= 0 || page_size <= 0)
+    return fail(PKV_EINVAL, "mla_paged_prefill_pages: bad sizes");
+  if (!std::isfinite(sm_scale)) return fail(PKV_EINVAL, "mla_paged_prefill_pages: sm_scale is not finite");
+  if (num_heads != 16 || ckv_dim != 512 || kpe_dim != 64)
+    return fail(PKV_EUNSUPPORTED,
+                "mla_paged_prefill_pages: compiled for num_heads 16, ckv_dim 512, kpe_dim 64 (got %d, %d, %d)",
+                num_heads, ckv_dim, kpe_dim);
+  if (batch > pkv::kMlaMaxBatch)
+    return fail(PKV_EUNSUPPORTED, "mla_paged_prefill_pages: batch %d exceeds %d", batch, pkv::kMlaMaxBatch);
+  if ((int64_t)num_pages * page_size >= INT32_MAX || (int64_t)num_kv_indices * page_size >= INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "mla_paged_prefill_pages: more than 2^31 tokens");
+  if (total_q == 0 || batch == 0) return PKV_OK;
+  if (!q_nope || !q_pe || !ckv_cache || !kpe_cache || !qo_indptr || !kv_indptr || !kv_indices || !out || !lse ||
+      !token_indptr || !token_rows)
+    return fail(PKV_EINVAL, "mla_paged_prefill_pages: NULL pointer argument");
+  if (max_q_len <= 0) return fail(PKV_EINVAL, "mla_paged_prefill_pages: max_q_len must be positive when total_q > 0");
+  if (num_pages <= 0) return fail(PKV_EINVAL, "mla_paged_prefill_pages: num_pages must be positive when total_q > 0");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  pkv::MlaPagesArgs e;
+  e.kv_indptr = kv_indptr; e.kv_indices = kv_indices; e.last_len = kv_last_page_len;
+  e.batch = batch; e.num_kv_indices = num_kv_indices; e.num_pages = num_pages; e.ps = page_size;
+  e.tok_indptr = token_indptr; e.tok_rows = token_rows;
+  int st = hip_status(pkv::launch_mla_expand_pages(e, s), "mla_paged_prefill_pages index launch");
+  if (st != PKV_OK) return st;
+  pkv::MlaArgs a;
+  a.q_nope = q_nope; a.q_pe = q_pe; a.ckv = ckv_cache; a.kpe = kpe_cache;
+  a.qo_indptr = qo_indptr; a.kv_indptr = token_indptr; a.kv_indices = token_rows;
+  a.batch = batch; a.total_q = total_q; a.max_q_len = max_q_len; a.num_pages = num_pages * page_size;
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  a.out = out; a.lse = lse;
+  return hip_status(pkv::launch_mla_prefill(a, s), "mla_paged_prefill_pages launch");
+}
+
 extern "C" int pkv_read_bandwidth(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (bytes == 0) return PKV_OK;
   if (!buf || !sink) return fail(PKV_EINVAL, "pkv_read_bandwidth: NULL pointer argument");

@@ -277,6 +277,7 @@ class MlaCase:
     kv_indptr: torch.Tensor  # [batch + 1] int32
     kv_indices: torch.Tensor  # [kv_indptr[-1]] int32
     sm_scale: float
+    kv_last_page_len: Optional[torch.Tensor] = None  # [batch] int32 when pages hold several tokens
 
     @property
     def batch(self) -> int:
@@ -291,6 +292,17 @@ class MlaCase:
         return int(self.ckv_cache.shape[0])
 
     @property
+    def page_size(self) -> int:
+        return int(self.ckv_cache.shape[1])
+
+    def kv_lens(self) -> List[int]:
+        """Key tokens per batch: pages times page size, the last page counted by its length."""
+        kv = self.kv_indptr.tolist()
+        ps = self.page_size
+        last = self.kv_last_page_len.tolist() if self.kv_last_page_len is not None else [ps] * self.batch
+        return [((kv[b + 1] - kv[b] - 1) * ps + last[b]) if kv[b + 1] > kv[b] else 0 for b in range(self.batch)]
+
+    @property
     def max_q_len(self) -> int:
         d = (self.qo_indptr[1:] - self.qo_indptr[:-1])
         return int(d.max().item()) if d.numel() else 0
@@ -298,11 +310,11 @@ class MlaCase:
     def visible_pairs(self) -> int:
         """Number of (query token, key token) pairs the causal mask keeps, per head."""
         qo = self.qo_indptr.tolist()
-        kv = self.kv_indptr.tolist()
+        kvl = self.kv_lens()
         tot = 0
         for b in range(self.batch):
             ql = qo[b + 1] - qo[b]
-            kl = kv[b + 1] - kv[b]
+            kl = kvl[b]
             pre = kl - ql
             tot += sum(pre + i + 1 for i in range(ql))
         return tot
@@ -333,6 +345,36 @@ def make_mla(q_lens: Sequence[int], prefixes: Sequence[int], num_heads: int = 16
                    kv_indices=torch.from_numpy(perm), sm_scale=float(sm_scale))
 
 
+def make_mla_paged(q_lens: Sequence[int], prefixes: Sequence[int], page_size: int, num_heads: int = 16,
+                   ckv_dim: int = 512, kpe_dim: int = 64, seed: int = 4, sm_scale: Optional[float] = None,
+                   extra_pages: int = 3, rng=None, name: str = "mla_paged") -> MlaCase:
+    """A batch over pages of page_size tokens: batch b gets ceil(kv_len / page_size) pages
+    from a random permutation of the pool, its last page holding the remainder
+    (kv_last_page_len); every slot of the pool is drawn, unowned slots too.
+    Draw order: page permutation -> q_nope -> q_pe -> ckv -> kpe."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    kv_lens = np.asarray(prefixes, dtype=np.int64) + q_lens
+    pages_b = (kv_lens + page_size - 1) // page_size
+    last = np.where(pages_b > 0, kv_lens - (pages_b - 1) * page_size, page_size).astype(np.int32)
+    qo = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    kv = np.concatenate([[0], np.cumsum(pages_b)]).astype(np.int32)
+    num_pages = int(kv[-1]) + extra_pages
+    perm = rng.permutation(num_pages)[: int(kv[-1])].astype(np.int32)
+    total_q = int(qo[-1])
+    q_nope = rng.standard_normal((total_q, num_heads, ckv_dim), dtype=np.float32)
+    q_pe = rng.standard_normal((total_q, num_heads, kpe_dim), dtype=np.float32)
+    ckv = rng.standard_normal((num_pages, page_size, ckv_dim), dtype=np.float32)
+    kpe = rng.standard_normal((num_pages, page_size, kpe_dim), dtype=np.float32)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(192.0)
+    return MlaCase(name=name, q_nope=_cast(q_nope, "bf16"), q_pe=_cast(q_pe, "bf16"),
+                   ckv_cache=_cast(ckv, "bf16"), kpe_cache=_cast(kpe, "bf16"),
+                   qo_indptr=torch.from_numpy(qo), kv_indptr=torch.from_numpy(kv),
+                   kv_indices=torch.from_numpy(perm), sm_scale=float(sm_scale),
+                   kv_last_page_len=torch.from_numpy(last))
+
+
 def mla_prefill_b8(seed: int = 4) -> MlaCase:
     """B=8, 16 heads, ckv 512, kpe 64, page_size 1; q_len U[1,512], prefix U[0,4096]."""
     rng = np.random.default_rng(seed)
@@ -340,6 +382,16 @@ def mla_prefill_b8(seed: int = 4) -> MlaCase:
     prefixes = rng.integers(0, 4096, 8, endpoint=True)
     return make_mla(q_lens, prefixes, rng=rng, sm_scale=1.0 / math.sqrt(192.0),
                     name="mla_prefill_b8_h16_ckv512_kpe64")
+
+
+def mla_prefill_b8_pages(page_size: int, seed: int = 4) -> MlaCase:
+    """The same batch shapes as mla_prefill_b8 (same q_len and prefix draws) over pages of
+    page_size tokens."""
+    rng = np.random.default_rng(seed)
+    q_lens = rng.integers(1, 512, 8, endpoint=True)
+    prefixes = rng.integers(0, 4096, 8, endpoint=True)
+    return make_mla_paged(q_lens, prefixes, page_size, rng=rng, sm_scale=1.0 / math.sqrt(192.0),
+                          name=f"mla_prefill_b8_pages{page_size}")
 
 
 def all_decode_names() -> List[str]:

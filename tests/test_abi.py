@@ -199,3 +199,14 @@ def test_paged_attention_v2_validation(L):
     with pytest.raises(NotImplementedError):
         pkv.paged_attention_v2(None, None, None, None, None, None, None, 2, 0.1, None, None, 16, 0,
                                alibi_slopes=object())
+
+
+def test_mla_pages_validation(L):
+    def call(ps=16, heads=16, tok_rows=FAKE, batch=2, total_q=4, num_pages=8, n_idx=4):
+        return L.mla_paged_prefill_pages(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, batch, total_q, 2, num_pages,
+                                         n_idx, heads, 512, 64, ps, 0.1, FAKE, tok_rows, FAKE, FAKE, None)
+    assert call(ps=0) == EINVAL
+    assert call(heads=8) == EUNSUP
+    assert call(tok_rows=None) == EINVAL
+    assert call(ps=1 << 20, num_pages=4096) == EUNSUP   # 2^32 pool rows
+    assert call(batch=0) == OK

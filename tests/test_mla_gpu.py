@@ -117,3 +117,55 @@ def test_mla_deterministic():
     o1, l1 = run_gpu(case)
     o2, l2 = run_gpu(case)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# --------------------------------------------------------------------------------------
+# Pages of several tokens (mla_paged_prefill_pages)
+# --------------------------------------------------------------------------------------
+
+def run_gpu_paged(case, nan_tail=False):
+    t = [getattr(case, k).to("cuda") for k in FIELDS]
+    if nan_tail:  # slots past each batch's last token, and unowned pages, hold NaN
+        ckv, kpe = t[2].clone(), t[3].clone()
+        owned = torch.zeros(case.num_pages, case.page_size, dtype=torch.bool)
+        kv = case.kv_indptr.tolist()
+        idx = case.kv_indices.tolist()
+        last = case.kv_last_page_len.tolist()
+        for b in range(case.batch):
+            for j in range(kv[b], kv[b + 1]):
+                owned[idx[j], : (last[b] if j == kv[b + 1] - 1 else case.page_size)] = True
+        mask = (~owned).to("cuda")
+        ckv[mask] = float("nan")
+        kpe[mask] = float("nan")
+        t[2], t[3] = ckv, kpe
+    out = torch.full_like(t[0], float("nan"))
+    lse = torch.full(t[0].shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+    pkv.mla_paged_prefill(*t, case.sm_scale, out=out, lse=lse, kv_last_page_len=case.kv_last_page_len.to("cuda"))
+    torch.cuda.synchronize()
+    return out.cpu().to(torch.float64).numpy(), lse.cpu().to(torch.float64).numpy()
+
+
+def run_oracle_paged(case):
+    return oracle.mla_prefill(*(getattr(case, k) for k in FIELDS), case.sm_scale,
+                              kv_last_page_len=case.kv_last_page_len)
+
+
+@pytest.mark.parametrize("page_size", [1, 2, 16, 64])
+def test_mla_multi_token_pages(page_size):
+    case = inputs.make_mla_paged([5, 40, 1, 17, 3, 0], [30, 0, 100, 7, 64, 9], page_size, seed=page_size)
+    say(f"mla pages: page_size={page_size} total_q={case.total_q} pages={case.num_pages}")
+    o, l = run_gpu_paged(case)
+    ro, rl = run_oracle_paged(case)
+    check(o, l, ro, rl, f"page_size={page_size}")
+    o2, l2 = run_gpu_paged(case, nan_tail=True)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2), "slots past the last token leaked into the output"
+
+
+def test_mla_prefill_b8_pages_of_16():
+    """The benchmarked MLA batch's shapes (q_len U[1,512], prefix U[0,4096]) over 16-token pages."""
+    case = inputs.mla_prefill_b8_pages(16)
+    say(f"mla_prefill_b8 over 16-token pages: total_q={case.total_q} pages={case.num_pages}")
+    o, l = run_gpu_paged(case)
+    ro, rl = run_oracle_paged(case)
+    e, le = check(o, l, ro, rl, "b8 pages of 16")
+    say(f"  max abs err {e:.3e}, lse err {le:.3e}")
