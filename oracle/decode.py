@@ -107,18 +107,34 @@ def _kv_head(h: int, group: int) -> int:
     return h // group
 
 
-def _scores(q_vec: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
-    """s_t = scale * <q, k_t> for every token t of the sequence."""
-    return scale * (K @ q_vec)
+def _scores(q_vec: np.ndarray, K: np.ndarray, scale: float, slope=None) -> np.ndarray:
+    """s_t = scale * <q, k_t> for every token t of the sequence, plus the ALiBi bias when a
+    slope is given.
+
+    ALiBi (Press, Smith and Lewis, "Train Short, Test Long: Attention with Linear Biases
+    Enables Input Length Extrapolation", ICLR 2022) adds -m_h * (i - j) to the score of
+    query position i on key position j, with a fixed slope m_h per head. The decoded token
+    is the sequence's last position, i = n - 1, so key t gets -m_h * (n - 1 - t): zero for
+    the token itself and more negative the older the key. (The PagedAttention V2 page's
+    launcher takes alibi_slopes but never defines or uses them; this is the published
+    definition.)
+    """
+    s = scale * (K @ q_vec)
+    if slope is not None:
+        n = K.shape[0]
+        s = s - float(slope) * ((n - 1) - np.arange(n))
+    return s
 
 
 def decode(query, key_cache, value_cache, layout: str, block_tables, seq_lens, scale: float,
-           num_kv_heads: int, block_size: int):
+           num_kv_heads: int, block_size: int, alibi_slopes=None):
     """Unsplit decode attention. Returns (out [S,H,D], lse [S,H]) in float64.
 
     out[b,h] = sum_t softmax(s)_t v_t and lse[b,h] = log sum_t exp(s_t), natural log,
-    over the sequence's len_b tokens. len_b = 0 gives zeros and -inf.
+    over the sequence's len_b tokens (with the ALiBi bias of head h when alibi_slopes [H]
+    is given). len_b = 0 gives zeros and -inf.
     """
+    slopes = None if alibi_slopes is None else _as_f64(alibi_slopes)
     q = _as_f64(query)
     bt = _as_int(block_tables)
     lens = _as_int(seq_lens)
@@ -135,7 +151,7 @@ def decode(query, key_cache, value_cache, layout: str, block_tables, seq_lens, s
         K, V = gather_sequence(key_cache, value_cache, layout, bt[b], n, block_size)
         for h in range(H):
             kh = _kv_head(h, G)
-            s = _scores(q[b, h], K[kh], scale)
+            s = _scores(q[b, h], K[kh], scale, None if slopes is None else slopes[h])
             M = s.max()
             e = np.exp(s - M)
             Z = e.sum()
@@ -171,7 +187,8 @@ def partition_ranges(n: int, block_size: int, partition_size: int, num_splits: i
 
 def decode_partials(query, key_cache, value_cache, layout: str, block_tables, seq_lens,
                     scale: float, num_kv_heads: int, block_size: int, partition_size: int,
-                    max_num_partitions: int, num_splits: int = 0, normalized: bool = False):
+                    max_num_partitions: int, num_splits: int = 0, normalized: bool = False,
+                    alibi_slopes=None):
     """Split-K partials per (b, h, p): (acc [S,H,P,D], m [S,H,P], l [S,H,P]) in float64.
 
     Partition p of sequence b covers the token range ``partition_ranges`` gives (fixed
@@ -181,8 +198,10 @@ def decode_partials(query, key_cache, value_cache, layout: str, block_tables, se
     keeps it), or acc / l when ``normalized`` (the PagedAttention V2 page's tmp_output,
     with l its exp_sums and m its max_logits). Partitions past the sequence's last one
     carry the sentinel m = -inf, l = 0 (PagedAttention V2 page, unused-partition branch);
-    their acc is left 0 here and is not part of the contract.
+    their acc is left 0 here and is not part of the contract. With alibi_slopes [H] every
+    score carries the ALiBi bias of its absolute position in the sequence (see _scores).
     """
+    slopes = None if alibi_slopes is None else _as_f64(alibi_slopes)
     q = _as_f64(query)
     bt = _as_int(block_tables)
     lens = _as_int(seq_lens)
@@ -205,7 +224,7 @@ def decode_partials(query, key_cache, value_cache, layout: str, block_tables, se
         K, V = gather_sequence(key_cache, value_cache, layout, bt[b], n, block_size)
         for h in range(H):
             kh = _kv_head(h, G)
-            s = _scores(q[b, h], K[kh], scale)
+            s = _scores(q[b, h], K[kh], scale, None if slopes is None else slopes[h])
             for p, (t0, t1) in enumerate(ranges):
                 sp = s[t0:t1]
                 mp = sp.max()

@@ -394,5 +394,14 @@ def mla_prefill_b8_pages(page_size: int, seed: int = 4) -> MlaCase:
                           name=f"mla_prefill_b8_pages{page_size}")
 
 
+def mla_decode_b64(seed: int = 6) -> MlaCase:
+    """MLA decode shapes: 64 sequences of one new token each (q_len 1) over prefixes
+    U[1024, 4096], 16 heads, ckv 512, kpe 64, page_size 1."""
+    rng = np.random.default_rng(seed)
+    prefixes = rng.integers(1024, 4096, 64, endpoint=True)
+    return make_mla(np.ones(64, dtype=np.int64), prefixes, rng=rng, sm_scale=1.0 / math.sqrt(192.0),
+                    name="mla_decode_b64_h16_ckv512_kpe64")
+
+
 def all_decode_names() -> List[str]:
     return ["tiny_fp32", "llama_gqa4", "wide_gqa6", "skewed_gqa8"]

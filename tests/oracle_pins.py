@@ -392,6 +392,70 @@ def pin_normalized_partials(orc):
         _close(s3, ref_lse, 1e-12, what=f"{layout} normalized NS=3 reduce lse")
 
 
+def pin_alibi_closed_forms(orc):
+    """ALiBi against closed forms. With a zero query only the bias remains, so the weights are
+    geometric: w_t = r^(n-1-t) / Z with r = e^-m and Z = (1 - r^n) / (1 - r), and
+    lse = ln Z. With one token the bias is zero. With two tokens the older one loses m:
+    weights e^(s0 - m) and e^s1, worked out here with math.exp."""
+    for layout in ("token_major", "xpacked"):
+        lens = [1, 2, 7, 30, 0]
+        H, KVH, D, bs = 4, 2, 8, 4
+        q, kc, vc, bt, lens_a, K, V = _tiny_case(41, lens, H, KVH, D, bs, layout)
+        slopes = np.array([0.5, 0.25, 0.125, 0.0625])
+        out0, lse0 = orc.decode(np.zeros_like(q), kc, vc, layout, bt, lens_a, 0.7, KVH, bs, alibi_slopes=slopes)
+        for b, n in enumerate(lens):
+            if n == 0:
+                assert np.all(out0[b] == 0.0) and np.all(lse0[b] == -np.inf)
+                continue
+            for h in range(H):
+                r = math.exp(-slopes[h])
+                Z = (1.0 - r ** n) / (1.0 - r)
+                w = np.array([r ** (n - 1 - t) for t in range(n)]) / Z
+                _close(out0[b, h], w @ V[b][h // 2], 1e-12, what=f"alibi zero-query out n={n}")
+                _close(lse0[b, h], math.log(Z), 1e-12, what=f"alibi zero-query lse n={n}")
+        out, lse = orc.decode(q, kc, vc, layout, bt, lens_a, 0.7, KVH, bs, alibi_slopes=slopes)
+        for h in range(H):
+            kv = h // 2
+            s0 = 0.7 * float(K[0][kv][0] @ q[0, h])      # one token: no bias
+            _close(lse[0, h], s0, 1e-12, what="alibi one token lse")
+            _close(out[0, h], V[0][kv][0], 1e-12, what="alibi one token out")
+            a0 = 0.7 * float(K[1][kv][0] @ q[1, h]) - slopes[h]   # two tokens: the older loses m
+            a1 = 0.7 * float(K[1][kv][1] @ q[1, h])
+            e0, e1 = math.exp(a0), math.exp(a1)
+            _close(out[1, h], (e0 * V[1][kv][0] + e1 * V[1][kv][1]) / (e0 + e1), 1e-12, what="alibi two tokens")
+            _close(lse[1, h], math.log(e0 + e1), 1e-12, what="alibi two tokens lse")
+
+
+def pin_alibi_split_invariance(orc):
+    """Partials carry each token's absolute position: any split reduces to the unsplit
+    ALiBi result; zero slopes give the plain result bit for bit."""
+    lens = [1, 16, 37, 100, 0]
+    H, KVH, D, bs = 6, 3, 8, 4
+    slopes = np.array([0.3, 0.1, 0.05, 0.02, 0.01, 0.7])
+    for layout in ("token_major", "xpacked"):
+        q, kc, vc, bt, lens_a, K, V = _tiny_case(43, lens, H, KVH, D, bs, layout)
+        out, lse = orc.decode(q, kc, vc, layout, bt, lens_a, 0.3, KVH, bs, alibi_slopes=slopes)
+        for ps in (4, 12, 64):
+            P = -(-max(lens) // ps)
+            acc, m, l = orc.decode_partials(q, kc, vc, layout, bt, lens_a, 0.3, KVH, bs, ps, P,
+                                            alibi_slopes=slopes)
+            o2, s2 = orc.reduce_partials(acc, m, l, lens_a, ps)
+            _close(o2, out, 1e-12, what=f"alibi split ps={ps}")
+            _close(s2, lse, 1e-12, what=f"alibi split lse ps={ps}")
+        o0, s0 = orc.decode(q, kc, vc, layout, bt, lens_a, 0.3, KVH, bs, alibi_slopes=np.zeros(H))
+        o1, s1 = orc.decode(q, kc, vc, layout, bt, lens_a, 0.3, KVH, bs)
+        assert np.array_equal(o0, o1) and np.array_equal(s0, s1), "zero slopes"
+        # a bias only differences of which matter: out is unchanged by the reference
+        # position, so compare against brute force with keys re-weighted by e^-m(n-1-t)
+        for b, n in enumerate(lens):
+            for h in range(H):
+                if n == 0:
+                    continue
+                logits = 0.3 * (K[b][h // 2] @ q[b, h])
+                w = sps.softmax(logits) * np.exp(-slopes[h] * ((n - 1) - np.arange(n)))
+                _close(out[b, h], (w / w.sum()) @ V[b][h // 2], 1e-12, what="alibi reweighting")
+
+
 # ----------------------------------------------------------------------------------------
 # MLA pins
 # ----------------------------------------------------------------------------------------
@@ -564,7 +628,7 @@ def pin_mla_multi_token_pages(orc):
 DECODE_PINS = [pin_decode_worked_example, pin_reduce_worked_example, pin_decode_brute_force,
                pin_decode_special_cases, pin_split_invariance, pin_partition_stats,
                pin_sentinel_padding, pin_page_permutation, pin_empty_sequence, pin_split_policy,
-               pin_normalized_partials]
+               pin_normalized_partials, pin_alibi_closed_forms, pin_alibi_split_invariance]
 MLA_PINS = [pin_mla_worked_example, pin_mla_sdpa, pin_mla_causal_perturbation,
             pin_mla_special_cases, pin_mla_multi_token_pages]
 ALL_PINS = DECODE_PINS + MLA_PINS

@@ -169,3 +169,13 @@ def test_mla_prefill_b8_pages_of_16():
     ro, rl = run_oracle_paged(case)
     e, le = check(o, l, ro, rl, "b8 pages of 16")
     say(f"  max abs err {e:.3e}, lse err {le:.3e}")
+
+
+def test_mla_decode_shapes():
+    """One new token per sequence (q_len 1): every key is visible."""
+    case = inputs.mla_decode_b64()
+    say(f"mla decode shapes: batch={case.batch} pages={case.num_pages}")
+    o, l = run_gpu(case)
+    ro, rl = run_oracle(case)
+    e, le = check(o, l, ro, rl, "mla decode b64")
+    say(f"  max abs err {e:.3e}, lse err {le:.3e}")

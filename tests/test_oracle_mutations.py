@@ -28,7 +28,7 @@ MUTATIONS = [
      "x-packed V dim reversed"),
     ("decode.py", "(d // x)[None, :], off[:, None], (d % x)[None, :]",
      "(d % x * 0 + d // x)[None, :], off[:, None], (x - 1 - d % x)[None, :]", 0, "x-packed K lane reversed"),
-    ("decode.py", "return scale * (K @ q_vec)", "return (K @ q_vec)", 0, "scale dropped"),
+    ("decode.py", "s = scale * (K @ q_vec)", "s = (K @ q_vec)", 0, "scale dropped"),
     ("decode.py", "out[b, h] = (e @ V[kh]) / Z", "out[b, h] = (e @ V[kh])", 0, "normalization dropped"),
     ("decode.py", "lse[b, h] = M + np.log(Z)", "lse[b, h] = np.log(Z)", 0, "max term dropped from lse"),
     ("decode.py", "acc[b, h, p] = e @ V[kh][t0:t1]", "acc[b, h, p] = (e @ V[kh][t0:t1]) / e.sum()", 0,
@@ -48,6 +48,12 @@ MUTATIONS = [
      "normalized partial not divided by l"),
     ("decode.py", "out[b, h] = ((w * l[b, h, :nparts]) @ acc[b, h, :nparts]) / Z",
      "out[b, h] = (w @ acc[b, h, :nparts]) / Z", 0, "normalized reduce without exp-sums weight"),
+    ("decode.py", "s = s - float(slope) * ((n - 1) - np.arange(n))", "s = s + float(slope) * ((n - 1) - np.arange(n))",
+     0, "ALiBi sign"),
+    ("decode.py", "s = s - float(slope) * ((n - 1) - np.arange(n))", "s = s - float(slope) * (n - np.arange(n))", 0,
+     "ALiBi query position n instead of n - 1"),
+    ("decode.py", "s = _scores(q[b, h], K[kh], scale, None if slopes is None else slopes[h])",
+     "s = _scores(q[b, h], K[kh], scale, None if slopes is None else slopes[kh])", 0, "ALiBi slope of the kv head"),
     ("mla.py", "vis = min(prefix + i + 1, kv_len)", "vis = min(prefix + i, kv_len)", 0, "causal off by one"),
     ("mla.py", "return sm_scale * (qn_row @ Kc.T + qp_row @ Kp.T)", "return sm_scale * (qn_row @ Kc.T)", 0,
      "kpe term dropped"),
