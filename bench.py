@@ -376,6 +376,13 @@ def main():
             rp = bench_mla(mp, 20, 3)
             extra["mla_prefill_b8_pages16"] = {"us": rp["ms"] * 1e3, "TFLOP_s": rp["tflops"],
                                                "frac_of_bf16_mfma_peak": rp["tflops"] / BF16_MFMA_PEAK_TFLOPS}
+            del mp
+            md = inputs.mla_decode_b64()
+            rd = bench_mla(md, 20, 3)
+            kv_b = sum(md.kv_lens()) * (512 + 64) * 2  # ckv + kpe bytes of every key, read once
+            extra["mla_decode_b64"] = {"us": rd["ms"] * 1e3, "kv_GB_s": kv_b / (rd["ms"] * 1e-3) / 1e9,
+                                       "frac_of_hbm_peak": kv_b / (rd["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                       "kernel": "mla_paged_prefill (q_len 1)"}
         except NotImplementedError as e:
             extra["mla_prefill_b8"] = {"error": str(e)}
         result["extra"] = extra

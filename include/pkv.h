@@ -222,9 +222,13 @@ int paged_decode(const void* query, int dtype,
  *   tmp_output  [num_seqs, num_heads, max_num_partitions, head_size] float32
  *   query [num_seqs, num_heads, head_size]; key_cache [num_blocks, num_kv_heads,
  *   head_size / x, block_size, x]; value_cache [num_blocks, num_kv_heads, head_size, block_size]
- * [PAv2]'s launcher accepts alibi_slopes, kv_cache_dtype, k_scale and v_scale but never
- * uses them; here alibi_slopes must be NULL (PKV_EUNSUPPORTED otherwise), and the other
- * three have no argument (the cache is read in `dtype`, unscaled).
+ * alibi_slopes  [num_heads] float32 device array, or NULL. [PAv2]'s launcher accepts the
+ *   argument without defining or using it; here it is the published ALiBi bias (Press,
+ *   Smith and Lewis, ICLR 2022): the score of key t of sequence b for head h becomes
+ *   scale * <q, k_t> - alibi_slopes[h] * (len_b - 1 - t), the decoded token being the
+ *   sequence's last position.
+ * [PAv2]'s kv_cache_dtype, k_scale and v_scale have no argument here (the cache is read
+ * in `dtype`, unscaled).
  * PKV_EINVAL / PKV_EUNSUPPORTED: as paged_decode_partial with partition_size = 512.
  */
 int paged_attention_v2(void* out, float* exp_sums, float* max_logits, float* tmp_output,

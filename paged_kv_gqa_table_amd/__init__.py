@@ -364,11 +364,14 @@ def paged_attention_v2(out: torch.Tensor, exp_sums: torch.Tensor, max_logits: to
     """The PagedAttention V2 launcher's call, argument for argument (asynchronous).
 
     x-packed caches, 512-token partitions; tmp_output holds each partition's normalized
-    average, exp_sums its l and max_logits its m. ALiBi, fp8 caches and K/V scales are
-    accepted by that launcher but unused there, and are refused here unless absent.
+    average, exp_sums its l and max_logits its m. ``alibi_slopes`` [H] float32 adds the
+    ALiBi bias -slope_h * (len - 1 - t). fp8 caches and K/V scales are accepted by that
+    launcher but unused there, and are refused here unless absent.
     """
     if alibi_slopes is not None:
-        raise NotImplementedError("paged_attention_v2: alibi_slopes are not supported")
+        _dev("alibi_slopes", alibi_slopes, torch.float32, 1)
+        if alibi_slopes.numel() != query.shape[1]:
+            raise ValueError("alibi_slopes must hold one slope per query head")
     if kv_cache_dtype != "auto" or float(k_scale) != 1.0 or float(v_scale) != 1.0:
         raise NotImplementedError("paged_attention_v2: only kv_cache_dtype='auto' with unit k/v scales")
     S, H, D, nb, bs = _check_decode_inputs(query, key_cache, value_cache, block_tables, seq_lens,
@@ -382,7 +385,7 @@ def paged_attention_v2(out: torch.Tensor, exp_sums: torch.Tensor, max_logits: to
     st = lib().paged_attention_v2(
         _ptr(out), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_output), _ptr(query), _DTYPE[query.dtype],
         _ptr(key_cache), _ptr(value_cache), int(num_kv_heads), float(scale), _ptr(block_tables),
-        block_tables.shape[1], _ptr(seq_lens), S, H, D, bs, nb, int(max_seq_len), P, None,
+        block_tables.shape[1], _ptr(seq_lens), S, H, D, bs, nb, int(max_seq_len), P, _ptr(alibi_slopes),
         _stream(query.device))
     _check(st, "paged_attention_v2")
 

@@ -21,6 +21,8 @@ struct DecodePartialArgs {
   int ppp;                // pages per partition = ps / 16; unused when nsplit > 0
   int nsplit;             // > 0: NUM_SPLITS policy, ceil(pages_b / nsplit) pages per partition
   int normalize;          // != 0: store acc / l instead of acc
+  const float* alibi;     // [H] ALiBi slopes (natural-log units), or null: score of key t
+                          // gets -slope_h * (len - 1 - t)
   int P;                  // max_num_partitions: stride of the partial arrays
   float* acc;             // [S, H, P, D]; may be null in final mode when P == 1
   float* m;               // [S, H, P]

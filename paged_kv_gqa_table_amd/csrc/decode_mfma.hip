@@ -59,7 +59,7 @@ struct MfmaSmem {
   float red_l[W][16];
 };
 
-template <int D, bool XP, int W, bool FINAL>
+template <int D, bool XP, int W, bool FINAL, bool ALIBI>
 __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const int G, const int b, const int kvh,
                                                const int p, const int len, MfmaSmem<W, D>& sm) {
   constexpr int BS = 16;
@@ -99,6 +99,8 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
     for (int s = 0; s < KS; ++s) qb[s] = hl < G ? ld16(qrow + (s * 32 + g * 8) * 2) : make_uint4(0, 0, 0, 0);
   }
 
+  // ALiBi slope of this lane's head in base-2 units (heads past G: 0)
+  const float slope2 = (ALIBI && hl < G) ? a.alibi[kvh * G + hl] * kLog2e : 0.f;
   f32x4_t acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -168,7 +170,9 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
     float tmax = kNegInf;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      x[j] = (4 * g + j < ntok) ? st[j] * a.scale_log2 : kNegInf;
+      float xv = st[j] * a.scale_log2;
+      if constexpr (ALIBI) xv = fmaf(slope2, (float)(pg * BS + 4 * g + j - (len - 1)), xv);
+      x[j] = (4 * g + j < ntok) ? xv : kNegInf;
       tmax = fmaxf(tmax, x[j]);
     }
     tmax = fmaxf(tmax, xor_lanes(tmax, 16));
@@ -269,7 +273,7 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
     if (nparts > 1) finish_item_fused<D, true, W>(a, b, kvh, G, nparts);
 }
 
-template <int D, bool XP, int W, bool DENSE, bool FINAL>
+template <int D, bool XP, int W, bool DENSE, bool FINAL, bool ALIBI>
 __global__ __launch_bounds__(64 * W) void decode_partial_mfma_kernel(DecodePartialArgs a, int G, int grid_parts) {
   __shared__ MfmaSmem<W, D> sm;
   if constexpr (DENSE) {
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(64 * W) void decode_partial_mfma_kernel(DecodeParti
       p = uniform(p);
       int len = a.lens[b];
       len = len > a.len_cap ? a.len_cap : len;
-      mfma_partition<D, XP, W, FINAL>(a, G, b, kvh, p, uniform(len), sm);
+      mfma_partition<D, XP, W, FINAL, ALIBI>(a, G, b, kvh, p, uniform(len), sm);
     }
   } else {
     const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -302,21 +306,21 @@ __global__ __launch_bounds__(64 * W) void decode_partial_mfma_kernel(DecodeParti
         if (p == 0) write_empty_rows<D, true>(a, b, kvh, G);
       return;
     }
-    mfma_partition<D, XP, W, FINAL>(a, G, b, kvh, p, len, sm);
+    mfma_partition<D, XP, W, FINAL, ALIBI>(a, G, b, kvh, p, len, sm);
   }
 }
 
-template <int D, bool XP, bool FINAL>
+template <int D, bool XP, bool FINAL, bool ALIBI>
 hipError_t launch_mfma_f(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
   constexpr int W = 4;
   if (use_dense_worklist(a.S, a.KVH, grid_parts)) {
     const long upper = (long)a.S * a.KVH * grid_parts;
     const int grid = (int)(upper < dense_grid_cap() ? upper : dense_grid_cap());
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, true, FINAL>), dim3(grid), dim3(64 * W),
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, true, FINAL, ALIBI>), dim3(grid), dim3(64 * W),
                        worklist_lds_words(a.S) * sizeof(int), s, a, G, grid_parts);
   } else {
     dim3 grid(grid_parts, a.KVH, a.S);
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, false, FINAL>), grid, dim3(64 * W), 0, s, a, G,
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, false, FINAL, ALIBI>), grid, dim3(64 * W), 0, s, a, G,
                        grid_parts);
   }
   return hipGetLastError();
@@ -324,8 +328,10 @@ hipError_t launch_mfma_f(const DecodePartialArgs& a, int G, int grid_parts, hipS
 
 template <int D, bool XP>
 hipError_t launch_mfma_d(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
-  return a.out != nullptr ? launch_mfma_f<D, XP, true>(a, G, grid_parts, s)
-                          : launch_mfma_f<D, XP, false>(a, G, grid_parts, s);
+  if (a.alibi != nullptr)  // ALiBi: partials only
+    return a.out != nullptr ? hipErrorNotSupported : launch_mfma_f<D, XP, false, true>(a, G, grid_parts, s);
+  return a.out != nullptr ? launch_mfma_f<D, XP, true, false>(a, G, grid_parts, s)
+                          : launch_mfma_f<D, XP, false, false>(a, G, grid_parts, s);
 }
 
 template <bool XP>

@@ -74,7 +74,7 @@ struct ValuSmem {
 };
 
 // One work item: partials of (b, kvh, p) for the G heads of kv head kvh.
-template <bool BF16, int D, int G, bool XP, int LPT, int W, bool FINAL>
+template <bool BF16, int D, int G, bool XP, int LPT, int W, bool FINAL, bool ALIBI>
 __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const int b, const int kvh,
                                                const int p, const int len, ValuSmem<W, G, D, XP>& sm) {
   using C = ValuCfg<BF16, D, G, XP, LPT, W>;
@@ -227,7 +227,10 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
         const float v = group_sum<LPT>(s[g][j]);
-        s[g][j] = (tg + TPI * j < ntok) ? v * a.scale_log2 : kNegInf;
+        float x = v * a.scale_log2;
+        if constexpr (ALIBI)
+          x = fmaf(a.alibi[kvh * G + g] * kLog2e, (float)(pg * BS + tg + TPI * j - (len - 1)), x);
+        s[g][j] = (tg + TPI * j < ntok) ? x : kNegInf;
       }
 
     // ---- online softmax with a wave-uniform running max per head
@@ -429,7 +432,7 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
     if (nparts > 1) finish_item_fused<D, BF16, W>(a, b, kvh, G, nparts);
 }
 
-template <bool BF16, int D, int G, bool XP, int LPT, int W, bool DENSE, int WPE, bool FINAL>
+template <bool BF16, int D, int G, bool XP, int LPT, int W, bool DENSE, int WPE, bool FINAL, bool ALIBI>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(WPE, 8))) void decode_partial_valu_kernel(DecodePartialArgs a, int grid_parts) {
   __shared__ ValuSmem<W, G, D, XP> sm;
   if constexpr (DENSE) {
@@ -446,7 +449,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(WPE, 8))
       p = uniform(p);
       int len = a.lens[b];
       len = len > a.len_cap ? a.len_cap : len;
-      valu_partition<BF16, D, G, XP, LPT, W, FINAL>(a, b, kvh, p, uniform(len), sm);
+      valu_partition<BF16, D, G, XP, LPT, W, FINAL, ALIBI>(a, b, kvh, p, uniform(len), sm);
     }
   } else {
     const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -463,11 +466,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(WPE, 8))
         if (p == 0) write_empty_rows<D, BF16>(a, b, kvh, G);
       return;
     }
-    valu_partition<BF16, D, G, XP, LPT, W, FINAL>(a, b, kvh, p, len, sm);
+    valu_partition<BF16, D, G, XP, LPT, W, FINAL, ALIBI>(a, b, kvh, p, len, sm);
   }
 }
 
-template <bool BF16, bool XP, int D, int G, bool FINAL>
+template <bool BF16, bool XP, int D, int G, bool FINAL, bool ALIBI>
 hipError_t launch_valu_fin(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
   constexpr int EB = BF16 ? 2 : 4;
 #ifndef PKV_VALU_ROW_BYTES_LPT16
@@ -483,11 +486,11 @@ hipError_t launch_valu_fin(const DecodePartialArgs& a, int grid_parts, hipStream
   if (use_dense_worklist(a.S, a.KVH, grid_parts)) {
     const long upper = (long)a.S * a.KVH * grid_parts;
     const int grid = (int)(upper < dense_grid_cap() ? upper : dense_grid_cap());
-    hipLaunchKernelGGL((decode_partial_valu_kernel<BF16, D, G, XP, LPT, W, true, WPE, FINAL>), dim3(grid), dim3(64 * W),
+    hipLaunchKernelGGL((decode_partial_valu_kernel<BF16, D, G, XP, LPT, W, true, WPE, FINAL, ALIBI>), dim3(grid), dim3(64 * W),
                        worklist_lds_words(a.S) * sizeof(int), s, a, grid_parts);
   } else {
     dim3 grid(grid_parts, a.KVH, a.S);
-    hipLaunchKernelGGL((decode_partial_valu_kernel<BF16, D, G, XP, LPT, W, false, WPE, FINAL>), grid, dim3(64 * W), 0,
+    hipLaunchKernelGGL((decode_partial_valu_kernel<BF16, D, G, XP, LPT, W, false, WPE, FINAL, ALIBI>), grid, dim3(64 * W), 0,
                        s, a, grid_parts);
   }
   return hipGetLastError();
@@ -495,8 +498,10 @@ hipError_t launch_valu_fin(const DecodePartialArgs& a, int grid_parts, hipStream
 
 template <bool BF16, bool XP, int D, int G>
 hipError_t launch_valu_one(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
-  return a.out != nullptr ? launch_valu_fin<BF16, XP, D, G, true>(a, grid_parts, s)
-                          : launch_valu_fin<BF16, XP, D, G, false>(a, grid_parts, s);
+  if (a.alibi != nullptr)  // ALiBi: partials only
+    return a.out != nullptr ? hipErrorNotSupported : launch_valu_fin<BF16, XP, D, G, false, true>(a, grid_parts, s);
+  return a.out != nullptr ? launch_valu_fin<BF16, XP, D, G, true, false>(a, grid_parts, s)
+                          : launch_valu_fin<BF16, XP, D, G, false, false>(a, grid_parts, s);
 }
 
 template <bool BF16, bool XP, int D>

@@ -71,8 +71,9 @@ struct Bf16Smem {
 // NUM_SPLITS policy, so an item's first page depends on its sequence's length and the
 // page ids of the next item are fetched after its length (one more round trip per item).
 // FINAL: the launch produces the output (final mode of DecodePartialArgs); compiled
-// separately so that the plain partial kernel carries none of its code.
-template <int D, int G, bool XP, int W, bool DENSE, bool SPLIT, bool FINAL>
+// separately so that the plain partial kernel carries none of its code. ALIBI: scores
+// carry the ALiBi bias (compiled only for the plain partial mode).
+template <int D, int G, bool XP, int W, bool DENSE, bool SPLIT, bool FINAL, bool ALIBI>
 __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const DenseItems& wl, int first_item,
                                            Bf16Smem<W, G, D>& sm) {
   using C = Bf16Cfg<D, XP>;
@@ -179,6 +180,10 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
     const int pg_begin = p * ppp;
     const int pg_end = min(pg_begin + ppp, (len + BS - 1) / BS);
     const int n_my = pg_end - pg_begin - w > 0 ? (pg_end - pg_begin - w + W - 1) / W : 0;
+    // ALiBi slope of each head in base-2 units (uniform); unused without ALIBI
+    float slope2[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) slope2[g] = ALIBI ? a.alibi[kvh * G + g] * kLog2e : 0.f;
     const char* kbase = reinterpret_cast<const char*>(a.kc) + (size_t)kvh * PAGEB;
     const char* vbase = reinterpret_cast<const char*>(a.vc) + (size_t)kvh * PAGEB;
     int cache_base = 0;  // first page (in this wave's order) whose id is in pid_cache
@@ -297,7 +302,9 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const float v = group_sum<8>(s[g][j]);
-          s[g][j] = (kt + 8 * j < ntok) ? v * a.scale_log2 : kNegInf;
+          float x = v * a.scale_log2;
+          if constexpr (ALIBI) x = fmaf(slope2[g], (float)(pg * BS + kt + 8 * j - (len - 1)), x);
+          s[g][j] = (kt + 8 * j < ntok) ? x : kNegInf;
         }
 
       // ---- softmax: wave-uniform max per head, lazy re-basing (branch-free)
@@ -476,7 +483,7 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
 // 128 VGPRs without spilling, else no constraint.
 constexpr int bf16_min_waves(int D, int G) { return (D == 64 && G <= 5) || (D == 128 && G <= 4) ? 4 : 1; }
 
-template <int D, int G, bool XP, int W, bool DENSE, bool SPLIT, bool FINAL>
+template <int D, int G, bool XP, int W, bool DENSE, bool SPLIT, bool FINAL, bool ALIBI>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(bf16_min_waves(D, G), 8))) void decode_partial_bf16_kernel(DecodePartialArgs a, int grid_parts) {
   __shared__ Bf16Smem<W, G, D> sm;
   if constexpr (DENSE) {
@@ -487,9 +494,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(bf16_min
     write_sentinels(wl, a.H, grid_parts, a.P, a.m, a.l);
     if constexpr (FINAL) write_empty_outputs<D, true>(wl, a);
     const int first = wg_item(wl, blockIdx.x, gridDim.x, 0);
-    if (first >= 0) bf16_items<D, G, XP, W, true, SPLIT, FINAL>(a, wl, first, sm);
+    if (first >= 0) bf16_items<D, G, XP, W, true, SPLIT, FINAL, ALIBI>(a, wl, first, sm);
   } else {
-    bf16_items<D, G, XP, W, false, SPLIT, FINAL>(a, DenseItems{}, blockIdx.x, sm);
+    bf16_items<D, G, XP, W, false, SPLIT, FINAL, ALIBI>(a, DenseItems{}, blockIdx.x, sm);
   }
 }
 
@@ -500,7 +507,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(bf16_min
 #ifndef PKV_DENSE_RATIO
 #define PKV_DENSE_RATIO 0
 #endif
-template <bool XP, int D, int G, bool SPLIT, bool FINAL>
+template <bool XP, int D, int G, bool SPLIT, bool FINAL, bool ALIBI>
 hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
   constexpr int W = PKV_BF16_WAVES;
   const long upper = (long)a.S * a.KVH * grid_parts;
@@ -515,14 +522,14 @@ hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream
 #ifndef PKV_RESIDENT_RATIO
 #define PKV_RESIDENT_RATIO 4
 #endif
-    int cap = resident_grid(reinterpret_cast<const void*>(&decode_partial_bf16_kernel<D, G, XP, W, true, SPLIT, FINAL>),
+    int cap = resident_grid(reinterpret_cast<const void*>(&decode_partial_bf16_kernel<D, G, XP, W, true, SPLIT, FINAL, ALIBI>),
                             64 * W, lds);
     if (upper > (long)PKV_RESIDENT_RATIO * cap) cap = dense_grid_cap();
     const int grid = (int)(upper < cap ? upper : cap);
-    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, true, SPLIT, FINAL>), dim3(grid), dim3(64 * W), lds,
-                       s, a, grid_parts);
+    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, true, SPLIT, FINAL, ALIBI>), dim3(grid), dim3(64 * W),
+                       lds, s, a, grid_parts);
   } else if constexpr (!SPLIT && !FINAL) {
-    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, false, false, false>), dim3((unsigned)upper),
+    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, false, false, false, ALIBI>), dim3((unsigned)upper),
                        dim3(64 * W), 0, s, a, grid_parts);
   } else {
     return hipErrorNotSupported;  // NUM_SPLITS and one-launch decode use the work list (kMaxDenseSeqs sequences)
@@ -533,11 +540,13 @@ hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream
 template <bool XP, int D, int G>
 hipError_t launch_bf16_g(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
   const bool fin = a.out != nullptr;
+  if (a.alibi != nullptr)  // ALiBi: plain partials only
+    return (fin || a.nsplit > 0) ? hipErrorNotSupported : launch_bf16_one<XP, D, G, false, false, true>(a, grid_parts, s);
   if (a.nsplit > 0)
-    return fin ? launch_bf16_one<XP, D, G, true, true>(a, grid_parts, s)
-               : launch_bf16_one<XP, D, G, true, false>(a, grid_parts, s);
-  return fin ? launch_bf16_one<XP, D, G, false, true>(a, grid_parts, s)
-             : launch_bf16_one<XP, D, G, false, false>(a, grid_parts, s);
+    return fin ? launch_bf16_one<XP, D, G, true, true, false>(a, grid_parts, s)
+               : launch_bf16_one<XP, D, G, true, false, false>(a, grid_parts, s);
+  return fin ? launch_bf16_one<XP, D, G, false, true, false>(a, grid_parts, s)
+             : launch_bf16_one<XP, D, G, false, false, false>(a, grid_parts, s);
 }
 
 template <bool XP, int D>

@@ -103,6 +103,7 @@ struct Phase1Mode {
   void* out;            // final mode when not null
   float* lse;
   int* counters;
+  const float* alibi;   // [num_heads] ALiBi slopes or null (plain partials only)
 };
 
 // Validation and dispatch shared by every decode entry point. `who` names the entry point
@@ -179,6 +180,7 @@ int decode_phase1(const char* who, const void* query, int dtype, const void* key
   a.ppp = a.ps / block_size;
   a.len_cap = (int)std::min<int64_t>(table_tokens, a.nsplit > 0 ? table_tokens : (int64_t)max_num_partitions * a.ps);
   a.normalize = mode.normalize;
+  a.alibi = mode.alibi;
   a.P = max_num_partitions;
   a.acc = partial_acc; a.m = partial_m; a.l = partial_l;
   a.out = mode.out; a.lse = mode.lse; a.counters = mode.counters;
@@ -236,7 +238,7 @@ extern "C" int paged_decode_partial(const void* query, int dtype, const void* ke
                                     float scale, int partition_size, int max_num_partitions,
                                     int max_seq_len, float* partial_acc, float* partial_m,
                                     float* partial_l, void* stream) {
-  const Phase1Mode mode{partition_size, 0, 0, nullptr, nullptr, nullptr};
+  const Phase1Mode mode{partition_size, 0, 0, nullptr, nullptr, nullptr, nullptr};
   return decode_phase1("paged_decode_partial", query, dtype, key_cache, value_cache, layout, block_tables,
                        max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, scale, max_num_partitions, max_seq_len, partial_acc, partial_m, partial_l, mode,
@@ -259,7 +261,7 @@ extern "C" int paged_decode_split_partial(const void* query, int dtype, const vo
                                           int num_blocks, float scale, int num_splits, int max_seq_len,
                                           float* partial_acc, float* partial_m, float* partial_l, void* stream) {
   if (num_splits <= 0) return fail(PKV_EINVAL, "paged_decode_split_partial: num_splits must be positive");
-  const Phase1Mode mode{0, num_splits, 0, nullptr, nullptr, nullptr};
+  const Phase1Mode mode{0, num_splits, 0, nullptr, nullptr, nullptr, nullptr};
   return decode_phase1("paged_decode_split_partial", query, dtype, key_cache, value_cache, layout, block_tables,
                        max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, scale, num_splits, max_seq_len, partial_acc, partial_m, partial_l, mode, stream);
@@ -281,7 +283,7 @@ extern "C" int paged_decode(const void* query, int dtype, const void* key_cache,
                             int max_num_partitions, int max_seq_len, float* partial_acc, float* partial_m,
                             float* partial_l, int32_t* counters, void* out, float* lse, void* stream) {
   if (!out) return fail(PKV_EINVAL, "paged_decode: NULL pointer argument (out)");
-  const Phase1Mode mode{partition_size, num_splits, 0, out, lse, counters};
+  const Phase1Mode mode{partition_size, num_splits, 0, out, lse, counters, nullptr};
   return decode_phase1("paged_decode", query, dtype, key_cache, value_cache, layout, block_tables,
                        max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, scale, max_num_partitions, max_seq_len, partial_acc, partial_m, partial_l, mode,
@@ -294,9 +296,7 @@ extern "C" int paged_attention_v2(void* out, float* exp_sums, float* max_logits,
                                   int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_heads,
                                   int head_size, int block_size, int num_blocks, int max_seq_len,
                                   int max_num_partitions, const float* alibi_slopes, void* stream) {
-  if (alibi_slopes != nullptr)
-    return fail(PKV_EUNSUPPORTED, "paged_attention_v2: alibi_slopes are not supported (pass NULL)");
-  const Phase1Mode mode{kPagedAttentionV2Partition, 0, 1, nullptr, nullptr, nullptr};
+  const Phase1Mode mode{kPagedAttentionV2Partition, 0, 1, nullptr, nullptr, nullptr, alibi_slopes};
   int st = decode_phase1("paged_attention_v2", query, dtype, key_cache, value_cache, PKV_KV_XPACKED, block_tables,
                          max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_size, block_size,
                          num_blocks, scale, max_num_partitions, max_seq_len, tmp_output, max_logits, exp_sums, mode,

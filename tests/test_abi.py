@@ -192,13 +192,12 @@ def test_paged_attention_v2_validation(L):
     def call(alibi=None, D=128, bs=16, P=1, max_seq_len=512, H=8):
         return L.paged_attention_v2(FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 2, 0.1, FAKE, 32, FAKE, 2, H, D, bs,
                                     64, max_seq_len, P, alibi, None)
-    assert call(alibi=FAKE) == EUNSUP        # ALiBi slopes: accepted by the page's launcher, unused there
     assert call(P=1, max_seq_len=513) == EINVAL  # 512-token partitions: 513 tokens need two
     assert call(H=7) == EINVAL               # 7 heads over 2 kv heads
     assert call(D=96) == EUNSUP
-    with pytest.raises(NotImplementedError):
+    with pytest.raises(NotImplementedError):  # fp8 caches: accepted by the page's launcher, unused there
         pkv.paged_attention_v2(None, None, None, None, None, None, None, 2, 0.1, None, None, 16, 0,
-                               alibi_slopes=object())
+                               kv_cache_dtype="fp8")
 
 
 def test_mla_pages_validation(L):

@@ -196,3 +196,35 @@ def test_lengths_past_max_seq_len_stay_in_bounds():
         and torch.isnan(l_buf[S * H * P:]).all(), "write past the partial arrays"
     ref = oracle_subset(case, [1, 2])
     check_out(_np(out)[1:], ref["out"], "bf16", "sequences within the contract")
+
+
+@pytest.mark.parametrize("dtype,D,H,KVH", [("bf16", 128, 8, 2), ("bf16", 256, 12, 2), ("bf16", 128, 16, 2),
+                                           ("bf16", 128, 32, 2), ("f32", 64, 6, 3)])
+def test_paged_attention_v2_alibi(dtype, D, H, KVH):
+    """ALiBi slopes through the PagedAttention V2 entry point, several partitions per
+    sequence (each score biased by its absolute position)."""
+    case = inputs.make_decode(EDGE_LENS, H, KVH, D, dtype=dtype, layout="xpacked", seed=13 * D + H)
+    dev = to_dev(case)
+    S = case.num_seqs
+    P = case.num_partitions(512)
+    # the usual geometric slopes; smaller for f32, whose 1e-5 bound on m cannot hold for
+    # maxima of several hundred (float32 spacing there is 3e-5 and more)
+    shrink = 1.0 / 64 if dtype == "f32" else 1.0
+    slopes = torch.tensor([shrink * 2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32)
+    say(f"paged_attention_v2 + ALiBi: {dtype} D={D} H={H} KVH={KVH}")
+    tmp = torch.full((S, H, P, D), float("nan"), dtype=torch.float32, device="cuda")
+    es = torch.full((S, H, P), float("nan"), dtype=torch.float32, device="cuda")
+    ml = torch.full((S, H, P), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full((S, H, D), float("nan"), dtype=case.query.dtype, device="cuda")
+    pkv.paged_attention_v2(out, es, ml, tmp, dev["q"], dev["k"], dev["v"], KVH, case.scale, dev["bt"],
+                           dev["lens"], case.block_size, case.max_seq_len, alibi_slopes=slopes.to("cuda"))
+    torch.cuda.synchronize()
+    r = oracle.decode_partials(case.query, case.key_cache, case.value_cache, "xpacked", case.block_tables,
+                               case.seq_lens, case.scale, KVH, case.block_size, 512, P, normalized=True,
+                               alibi_slopes=slopes)
+    _check_ranged_partials(_np(tmp), _np(ml), _np(es), r, case.seq_lens.numpy(),
+                           lambda n: oracle.partition_ranges(n, case.block_size, 512), dtype, "v2 alibi",
+                           normalized=True)
+    ref, _ = oracle.decode(case.query, case.key_cache, case.value_cache, "xpacked", case.block_tables,
+                           case.seq_lens, case.scale, KVH, case.block_size, alibi_slopes=slopes)
+    check_out(_np(out), ref, dtype, "v2 alibi out")
