@@ -501,15 +501,21 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(bf16_min
 }
 
 
+// Waves per work item. With 3 at head_dim 128 a CU holds 5 workgroups (15 waves) instead
+// of 4, so a batch like llama_gqa4 (1,272 items) starts every item at once instead of
+// running a second, partial round on a quarter of the slots: measured 58.2-58.6 us
+// against 59.2 us per phase-1 launch there. At head_dim 256 the fourth wave pays off
+// (wide_gqa6: 220 us with 4, 234 us with 3).
 #ifndef PKV_BF16_WAVES
-#define PKV_BF16_WAVES 4
+#define PKV_BF16_WAVES 0
 #endif
+constexpr int bf16_waves(int D) { return PKV_BF16_WAVES > 0 ? PKV_BF16_WAVES : (D == 128 ? 3 : 4); }
 #ifndef PKV_DENSE_RATIO
 #define PKV_DENSE_RATIO 0
 #endif
 template <bool XP, int D, int G, bool SPLIT, bool FINAL, bool ALIBI>
 hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
-  constexpr int W = PKV_BF16_WAVES;
+  constexpr int W = bf16_waves(D);
   const long upper = (long)a.S * a.KVH * grid_parts;
   // The dense work list costs one extra memory round trip per workgroup but keeps every
   // workgroup busy and balanced; on MI355X it was faster than the plain partition grid even
