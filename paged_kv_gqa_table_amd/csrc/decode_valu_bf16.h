@@ -510,17 +510,25 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(bf16_min
 #define PKV_BF16_WAVES 0
 #endif
 constexpr int bf16_waves(int D) { return PKV_BF16_WAVES > 0 ? PKV_BF16_WAVES : (D == 128 ? 3 : 4); }
-#ifndef PKV_DENSE_RATIO
-#define PKV_DENSE_RATIO 0
-#endif
 template <bool XP, int D, int G, bool SPLIT, bool FINAL, bool ALIBI>
 hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
   constexpr int W = bf16_waves(D);
   const long upper = (long)a.S * a.KVH * grid_parts;
-  // The dense work list costs one extra memory round trip per workgroup but keeps every
-  // workgroup busy and balanced; on MI355X it was faster than the plain partition grid even
-  // for uniform lengths, so the plain grid (ratio > 0) is kept only for very large batches.
-  if (use_dense_worklist(a.S, a.KVH, grid_parts) && upper > (long)PKV_DENSE_RATIO * dense_grid_cap() / 4) {
+  // The dense work list costs one extra memory round trip per workgroup (the lengths before
+  // the first page ids) but keeps every workgroup busy and balanced. The plain (partition,
+  // sequence, kv head) grid needs no such trip: its empty partitions exit at once and free
+  // their slots, so when the whole grid is resident within about two rounds it is the
+  // faster of the two (llama_gqa4, 2,048 workgroups on 1,280 slots: 58.2 against 59.2 us).
+  // Larger grids keep the list.
+  bool plain = !use_dense_worklist(a.S, a.KVH, grid_parts);
+  if constexpr (!SPLIT && !FINAL) {
+    if (!plain) {
+      const int pcap = resident_grid(
+          reinterpret_cast<const void*>(&decode_partial_bf16_kernel<D, G, XP, W, false, false, false, ALIBI>), 64 * W, 0);
+      plain = upper <= 2L * pcap;
+    }
+  }
+  if (!plain) {
     // one workgroup per resident slot (every workgroup starts at once and walks its items
     // with the next one prefetched) unless there are many items per slot, where the
     // hardware's own refill of finished slots balances uneven items better
