@@ -13,6 +13,7 @@
  *                         normalized partials (tmp_output, exp_sums, max_logits)
  *   mla_paged_prefill     MLA causal paged prefill (page_size 1), base-2 LSE
  *   mla_paged_prefill_pages  the same over pages of several tokens
+ *   mla_paged_decode      MLA decode (one new token per sequence), split-K
  * and a measurement helper, pkv_read_bandwidth (a plain streaming read of a buffer),
  * that no part of the attention path uses.
  *
@@ -302,6 +303,38 @@ int mla_paged_prefill_pages(const void* q_nope, const void* q_pe,
                             int page_size, float sm_scale,
                             int32_t* token_indptr, int32_t* token_rows,
                             void* out, float* lse, void* stream);
+
+/*
+ * mla_paged_decode -- MLA decode: one new token per sequence ([MLA]'s computation with
+ * q_len = 1, so the token sees all kv_len keys), split-K over the latent cache on the
+ * matrix cores, then the combine; two launches on `stream`.
+ *
+ * Batch b's keys are tok_j = kv_indices[kv_indptr[b] + j], j < kv_len_b (page_size 1).
+ * Split s covers keys [s * split_tokens, min((s+1) * split_tokens, kv_len_b)); its partials
+ * are m = max_j x_j (natural log), l = sum_j exp(x_j - m), acc = sum_j exp(x_j - m) ckv_j,
+ * with x_j = sm_scale (q_nope[b,h] . ckv_j + q_pe[b,h] . kpe_j); splits past the last get
+ * m = -inf, l = 0. The combine writes
+ *   out[b,h,:] = sum_j softmax(x)_j ckv_j   bf16 (RNE);  lse[b,h] = log2 sum_j exp(x_j)
+ * and kv_len_b = 0 gives out = 0, lse = -inf.
+ *   q_nope [batch, 16, 512] bf16, q_pe [batch, 16, 64] bf16
+ *   ckv_cache [num_pages, 1, 512] bf16, kpe_cache [num_pages, 1, 64] bf16
+ *   kv_indptr [batch + 1] int32 (kv_indptr[batch] = num_kv_indices), kv_indices int32 in [0, num_pages)
+ *   partial_acc [batch, 16, max_num_splits, 512], partial_m / partial_l [batch, 16, max_num_splits]
+ *              float32: caller-owned scratch
+ *   out [batch, 16, 512] bf16, lse [batch, 16] float32 (base 2)
+ * max_kv_len bounds every kv_len_b (a longer batch is cut to max_num_splits splits).
+ * PKV_EINVAL: NULL pointers with batch > 0, non-positive split_tokens or max_num_splits,
+ *   max_num_splits < ceil(max_kv_len / split_tokens), num_pages = 0 with batch > 0.
+ * PKV_EUNSUPPORTED: anything but num_heads 16, ckv_dim 512, kpe_dim 64, page_size 1.
+ */
+int mla_paged_decode(const void* q_nope, const void* q_pe,
+                     const void* ckv_cache, const void* kpe_cache,
+                     const int32_t* kv_indptr, const int32_t* kv_indices,
+                     int batch, int num_pages, int num_kv_indices, int max_kv_len,
+                     int num_heads, int ckv_dim, int kpe_dim, int page_size, float sm_scale,
+                     int split_tokens, int max_num_splits,
+                     float* partial_acc, float* partial_m, float* partial_l,
+                     void* out, float* lse, void* stream);
 
 /* Measurement helper, not part of the attention path: reads `bytes` bytes of device memory
  * at `buf` once, as a plain streaming read (16-byte loads, grid-stride over the buffer), on

@@ -18,6 +18,7 @@ Entry points (same names as the C ABI):
                               partitions, normalized tmp_output / exp_sums / max_logits)
   mla_paged_prefill(...)      MLA causal paged prefill, base-2 LSE (page_size 1, or pages of
                               several tokens through mla_paged_prefill_pages)
+  mla_paged_decode(...)       MLA decode (one new token per sequence), split-K
 read_bandwidth(...) is a measurement helper (a plain streaming read of a buffer), not part
 of the attention path.
 """
@@ -32,7 +33,7 @@ import torch
 
 __all__ = ["paged_decode_partial", "paged_decode_reduce", "paged_decode_split_partial",
            "paged_decode_split_reduce", "paged_decode", "paged_decode_into", "paged_attention_v2",
-           "mla_paged_prefill", "mla_paged_prefill_pages", "read_bandwidth", "lib", "library_path", "PkvError", "TOKEN_MAJOR",
+           "mla_paged_prefill", "mla_paged_prefill_pages", "mla_paged_decode", "read_bandwidth", "lib", "library_path", "PkvError", "TOKEN_MAJOR",
            "XPACKED", "num_partitions"]
 
 TOKEN_MAJOR = "token_major"
@@ -88,6 +89,9 @@ def lib() -> ctypes.CDLL:
     L.mla_paged_prefill_pages.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                           i32, f32, vp, vp, vp, vp, vp]
     L.mla_paged_prefill_pages.restype = i32
+    L.mla_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
+                                   vp, vp, vp, vp, vp, vp]
+    L.mla_paged_decode.restype = i32
     L.pkv_read_bandwidth.argtypes = [vp, ctypes.c_size_t, vp, vp]
     L.pkv_read_bandwidth.restype = i32
     L.pkv_last_error.argtypes = []
@@ -471,6 +475,48 @@ def mla_paged_prefill_pages(q_nope, q_pe, ckv_cache, kpe_cache, qo_indptr, kv_in
         page_size, float(sm_scale), _ptr(token_indptr), _ptr(token_rows), _ptr(out), _ptr(lse),
         _stream(q_nope.device))
     _check(st, "mla_paged_prefill_pages")
+
+
+def mla_paged_decode(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.Tensor, kpe_cache: torch.Tensor,
+                     kv_indptr: torch.Tensor, kv_indices: torch.Tensor, sm_scale: float,
+                     split_tokens: int = 256, max_kv_len: Optional[int] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     partials: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """MLA decode, one new token per sequence: q_nope [B, 16, 512], q_pe [B, 16, 64].
+    Returns (out [B, 16, 512] bf16, lse [B, 16] base 2). ``max_kv_len`` defaults to the
+    largest kv_indptr step (one device-to-host read); ``partials`` (acc, m, l) scratch is
+    allocated when not given."""
+    for n, t in (("q_nope", q_nope), ("q_pe", q_pe), ("ckv_cache", ckv_cache), ("kpe_cache", kpe_cache)):
+        _dev(n, t, torch.bfloat16, 3)
+    _dev("kv_indptr", kv_indptr, torch.int32, 1)
+    _dev("kv_indices", kv_indices, torch.int32, 1)
+    B, H, Dc = q_nope.shape
+    Dp = q_pe.shape[2]
+    num_pages, page_size, _ = ckv_cache.shape
+    if kv_indptr.numel() != B + 1 or q_pe.shape[:2] != q_nope.shape[:2]:
+        raise ValueError("q_nope / q_pe must be [batch, heads, dim] and kv_indptr [batch + 1]")
+    if max_kv_len is None:
+        max_kv_len = int((kv_indptr[1:] - kv_indptr[:-1]).max().item()) if B > 0 else 0
+    P = max(1, -(-int(max_kv_len) // int(split_tokens)))
+    dev = q_nope.device
+    if partials is None:
+        partials = (torch.empty((B, H, P, Dc), dtype=torch.float32, device=dev),
+                    torch.empty((B, H, P), dtype=torch.float32, device=dev),
+                    torch.empty((B, H, P), dtype=torch.float32, device=dev))
+    acc, m, l = partials
+    _check_partials(acc, m, l, B, H, Dc)
+    if out is None:
+        out = torch.empty((B, H, Dc), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _dev("out", out, torch.bfloat16, 3)
+    _dev("lse", lse, torch.float32, 2)
+    st = lib().mla_paged_decode(_ptr(q_nope), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache), _ptr(kv_indptr),
+                                _ptr(kv_indices), B, num_pages, kv_indices.numel(), int(max_kv_len), H, Dc, Dp,
+                                page_size, float(sm_scale), int(split_tokens), m.shape[2], _ptr(acc), _ptr(m),
+                                _ptr(l), _ptr(out), _ptr(lse), _stream(dev))
+    _check(st, "mla_paged_decode")
+    return out, lse
 
 
 def read_bandwidth(buf: torch.Tensor, sink: torch.Tensor) -> None:

@@ -21,9 +21,15 @@ namespace pkv {
 // over its first np partitions and writes out[row, :] (and lse[row] when lse is not null).
 // Each lane owns D / 64 contiguous output dims, so every acc row is one coalesced read;
 // m and l of the first 64 partitions and 8 acc rows go out before anything waits.
+// Eight floats (a lane's share of a 512-wide row) as one 32-byte access.
+struct alignas(32) Float8 {
+  float4 a, b;
+};
+
+// lse_scale multiplies the written LSE (1 for natural log, 1 / ln 2 for base 2).
 template <int D, bool OUT_BF16>
 PKV_DEVICE void reduce_row_wave(const float* acc, const float* pm, const float* pl, int P, int np,
-                                bool normalized, size_t row, void* out, float* lse) {
+                                bool normalized, size_t row, void* out, float* lse, float lse_scale = 1.f) {
   constexpr int DPL = D / 64;  // output dims per lane
   constexpr int CH = 8;        // partition rows of acc in flight per lane
   const int lane = threadIdx.x & 63;
@@ -37,7 +43,9 @@ PKV_DEVICE void reduce_row_wave(const float* acc, const float* pm, const float* 
     const float* mrow = pm + row * P;
     const float* lrow = pl + row * P;
     const float* arow = acc + row * P * D + lane * DPL;
-    using VecT = typename std::conditional<DPL == 4, float4, typename std::conditional<DPL == 2, float2, float>::type>::type;
+    using VecT = typename std::conditional<
+        DPL == 8, Float8,
+        typename std::conditional<DPL == 4, float4, typename std::conditional<DPL == 2, float2, float>::type>::type>::type;
     const float m0 = lane < np ? mrow[lane] : kNegInf;  // partition `lane`
     const float l0 = lane < np ? lrow[lane] : 0.f;
     VecT buf[CH];
@@ -83,7 +91,10 @@ PKV_DEVICE void reduce_row_wave(const float* acc, const float* pm, const float* 
   const size_t ob = row * D + lane * DPL;
   if constexpr (OUT_BF16) {
     uint16_t* dst = reinterpret_cast<uint16_t*>(out) + ob;
-    if constexpr (DPL == 4) {
+    if constexpr (DPL == 8) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                                  pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+    } else if constexpr (DPL == 4) {
       *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     } else if constexpr (DPL == 2) {
       *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(o[0], o[1]);
@@ -95,7 +106,7 @@ PKV_DEVICE void reduce_row_wave(const float* acc, const float* pm, const float* 
 #pragma unroll
     for (int i = 0; i < DPL; ++i) dst[i] = o[i];
   }
-  if (lse != nullptr && lane == 0) lse[row] = (np > 0) ? M + __logf(Z) : kNegInf;
+  if (lse != nullptr && lane == 0) lse[row] = (np > 0) ? (M + __logf(Z)) * lse_scale : kNegInf;
 }
 
 // Number of partitions of a sequence of len tokens under the launch's partition map.

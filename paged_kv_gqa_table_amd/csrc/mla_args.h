@@ -36,6 +36,28 @@ struct MlaPagesArgs {
 
 hipError_t launch_mla_expand_pages(const MlaPagesArgs& a, hipStream_t s);
 
+// MLA decode (one new token per sequence), split-K over the latent cache.
+struct MlaDecodeArgs {
+  const void* q_nope;         // [batch, 16, 512] bf16
+  const void* q_pe;           // [batch, 16, 64] bf16
+  const void* ckv;            // [num_pages, 1, 512] bf16 (also V)
+  const void* kpe;            // [num_pages, 1, 64] bf16
+  const int32_t* kv_indptr;   // [batch + 1]
+  const int32_t* kv_indices;  // [kv_indptr[batch]] token ids
+  int batch, num_pages, num_kv_indices;
+  int split;                  // tokens per split (multiple of 16)
+  int P;                      // max_num_splits: stride of the partial arrays
+  int len_cap;                // lengths are clamped to P * split tokens
+  float sm_scale_log2;        // sm_scale * log2(e)
+  float* acc;                 // [batch, 16, P, 512]
+  float* m;                   // [batch, 16, P] natural log
+  float* l;                   // [batch, 16, P]
+  void* out;                  // [batch, 16, 512] bf16
+  float* lse;                 // [batch, 16] base 2
+};
+
+hipError_t launch_mla_decode(const MlaDecodeArgs& a, int grid_parts, hipStream_t s);
+
 // Workgroup cap for persistent-style grids on the current device (host side).
 int dense_grid_cap();
 

@@ -380,6 +380,43 @@ extern "C" int mla_paged_prefill_pages(const void* q_nope, const void* q_pe, con
   return hip_status(pkv::launch_mla_prefill(a, s), "mla_paged_prefill_pages launch");
 }
 
+extern "C" int mla_paged_decode(const void* q_nope, const void* q_pe, const void* ckv_cache, const void* kpe_cache,
+                                const int32_t* kv_indptr, const int32_t* kv_indices, int batch, int num_pages,
+                                int num_kv_indices, int max_kv_len, int num_heads, int ckv_dim, int kpe_dim,
+                                int page_size, float sm_scale, int split_tokens, int max_num_splits,
+                                float* partial_acc, float* partial_m, float* partial_l, void* out, float* lse,
+                                void* stream) {
+  if (batch < 0 || num_pages < 0 || num_kv_indices < 0 || max_kv_len < 0 || num_heads <= 0 || ckv_dim <= 0 ||
+      kpe_dim <= 0 || page_size <= 0 || split_tokens <= 0 || max_num_splits <= 0)
+    return fail(PKV_EINVAL, "mla_paged_decode: bad sizes");
+  if (!std::isfinite(sm_scale)) return fail(PKV_EINVAL, "mla_paged_decode: sm_scale is not finite");
+  if (num_heads != 16 || ckv_dim != 512 || kpe_dim != 64 || page_size != 1)
+    return fail(PKV_EUNSUPPORTED,
+                "mla_paged_decode: compiled for num_heads 16, ckv_dim 512, kpe_dim 64, page_size 1 (got %d, %d, %d, %d)",
+                num_heads, ckv_dim, kpe_dim, page_size);
+  const int64_t grid_parts = ((int64_t)max_kv_len + split_tokens - 1) / split_tokens;
+  if (grid_parts > max_num_splits)
+    return fail(PKV_EINVAL, "mla_paged_decode: max_num_splits %d < ceil(max_kv_len / split_tokens) = %lld",
+                max_num_splits, (long long)grid_parts);
+  if ((int64_t)batch * (grid_parts > 0 ? grid_parts : 1) >= INT32_MAX || (int64_t)batch * 16 >= INT32_MAX / 2)
+    return fail(PKV_EUNSUPPORTED, "mla_paged_decode: grid too large");
+  if (batch == 0) return PKV_OK;
+  if (!q_nope || !q_pe || !ckv_cache || !kpe_cache || !kv_indptr || !kv_indices || !partial_acc || !partial_m ||
+      !partial_l || !out || !lse)
+    return fail(PKV_EINVAL, "mla_paged_decode: NULL pointer argument");
+  if (num_pages <= 0) return fail(PKV_EINVAL, "mla_paged_decode: num_pages must be positive");
+  pkv::MlaDecodeArgs a;
+  a.q_nope = q_nope; a.q_pe = q_pe; a.ckv = ckv_cache; a.kpe = kpe_cache;
+  a.kv_indptr = kv_indptr; a.kv_indices = kv_indices;
+  a.batch = batch; a.num_pages = num_pages; a.num_kv_indices = num_kv_indices;
+  a.split = split_tokens; a.P = max_num_splits;
+  a.len_cap = (int)std::min<int64_t>((int64_t)max_num_splits * split_tokens, INT32_MAX);
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  a.acc = partial_acc; a.m = partial_m; a.l = partial_l; a.out = out; a.lse = lse;
+  return hip_status(pkv::launch_mla_decode(a, (int)grid_parts, reinterpret_cast<hipStream_t>(stream)),
+                    "mla_paged_decode launch");
+}
+
 extern "C" int pkv_read_bandwidth(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (bytes == 0) return PKV_OK;
   if (!buf || !sink) return fail(PKV_EINVAL, "pkv_read_bandwidth: NULL pointer argument");

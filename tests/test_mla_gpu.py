@@ -179,3 +179,47 @@ def test_mla_decode_shapes():
     ro, rl = run_oracle(case)
     e, le = check(o, l, ro, rl, "mla decode b64")
     say(f"  max abs err {e:.3e}, lse err {le:.3e}")
+
+
+# --------------------------------------------------------------------------------------
+# MLA decode, split-K (mla_paged_decode): the oracle is the prefill oracle with q_len 1
+# --------------------------------------------------------------------------------------
+
+def run_decode_gpu(case, split, max_kv_len=None):
+    t = {k: getattr(case, k).to("cuda") for k in FIELDS}
+    out, lse = pkv.mla_paged_decode(t["q_nope"], t["q_pe"], t["ckv_cache"], t["kpe_cache"], t["kv_indptr"],
+                                    t["kv_indices"], case.sm_scale, split_tokens=split, max_kv_len=max_kv_len)
+    torch.cuda.synchronize()
+    return out.cpu().to(torch.float64).numpy(), lse.cpu().to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("split", [16, 48, 256, 4096])
+def test_mla_split_decode_edges(split):
+    """Edge lengths (0, 1, 15, 16, 17, ...) against the oracle, for splits from one key
+    group to the whole sequence."""
+    kv = [0, 1, 15, 16, 17, 100, 255, 256, 257, 1000, 2049]
+    case = inputs.make_mla(np.ones(len(kv), dtype=np.int64), np.maximum(np.array(kv) - 1, 0), seed=split,
+                           extra_pages=5)
+    # kv_len 0: the generator gives every batch one query token, so build that batch's keys empty
+    kvp = case.kv_indptr.clone()
+    kvp[1:] = torch.cumsum(torch.tensor([max(k, 0) for k in kv], dtype=torch.int32), 0)
+    idx = case.kv_indices[: int(kvp[-1])]
+    case = inputs.MlaCase(name="mla_decode_edges", q_nope=case.q_nope, q_pe=case.q_pe, ckv_cache=case.ckv_cache,
+                          kpe_cache=case.kpe_cache, qo_indptr=case.qo_indptr, kv_indptr=kvp, kv_indices=idx,
+                          sm_scale=case.sm_scale)
+    say(f"mla split decode: split={split} kv_lens={kv}")
+    o, l = run_decode_gpu(case, split)
+    ro, rl = run_oracle(case)
+    check(o, l, ro, rl, f"split={split}")
+    assert np.all(o[0] == 0.0) and np.all(np.isneginf(l[0])), "empty batch"
+
+
+def test_mla_split_decode_b64():
+    case = inputs.mla_decode_b64()
+    say(f"mla split decode b64: pages={case.num_pages}")
+    o, l = run_decode_gpu(case, 256)
+    ro, rl = run_oracle(case)
+    e, le = check(o, l, ro, rl, "split decode b64")
+    o2, l2 = run_gpu(case)  # the prefill kernel with q_len 1: the same values within bf16
+    check(o, l, o2, l2, "split decode vs prefill kernel")
+    say(f"  max abs err {e:.3e}, lse err {le:.3e}")
