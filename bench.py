@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama_gqa4",
-                    choices=["llama_gqa4", "wide_gqa6", "skewed_gqa8", "tiny_fp32", "mla_prefill_b8"])
+                    choices=["llama_gqa4", "wide_gqa6", "skewed_gqa8", "tiny_fp32", "mla_prefill_b8", "mla_decode_b64"])
     ap.add_argument("--copies", type=int, default=0, help="KV pool copies to cycle (0 = auto)")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -335,6 +335,23 @@ def main():
     pkv.lib()  # fail loudly if the HIP library is missing
 
     result = {}
+    if args.workload == "mla_decode_b64":
+        case = inputs.mla_decode_b64()
+        r = bench_mla_decode(case, args.steps, args.warmup, split=1024)
+        kv_b = sum(case.kv_lens()) * (512 + 64) * 2
+        gbs = kv_b / (r["ms"] * 1e-3) / 1e9
+        result = {
+            "metric": "MLA decode ckv+kpe HBM GB/s and us per decode step (both launches), 1x MI355X",
+            "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": r["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": case.name, "batch": case.batch, "split_tokens": 1024,
+                       "kv_bytes_per_step": kv_b},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        }
+        print(json.dumps(result), flush=True)
+        return
     if args.workload == "mla_prefill_b8":
         case = inputs.mla_prefill_b8()
         r = bench_mla(case, args.steps, args.warmup)
@@ -423,10 +440,10 @@ def main():
             extra["mla_decode_b64_prefill_kernel"] = {
                 "us": rd["ms"] * 1e3, "kv_GB_s": kv_b / (rd["ms"] * 1e-3) / 1e9,
                 "frac_of_hbm_peak": kv_b / (rd["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, "kernel": "mla_paged_prefill (q_len 1)"}
-            rs = bench_mla_decode(md, 50, 5, split=256)
+            rs = bench_mla_decode(md, 50, 5, split=1024)
             extra["mla_decode_b64"] = {"us": rs["ms"] * 1e3, "kv_GB_s": kv_b / (rs["ms"] * 1e-3) / 1e9,
                                        "frac_of_hbm_peak": kv_b / (rs["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                       "kernel": "mla_paged_decode (split-K, 256-key splits, both launches)"}
+                                       "kernel": "mla_paged_decode (split-K, 1024-key splits, both launches)"}
         except NotImplementedError as e:
             extra["mla_prefill_b8"] = {"error": str(e)}
         result["extra"] = extra

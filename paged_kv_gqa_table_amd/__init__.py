@@ -479,11 +479,15 @@ def mla_paged_prefill_pages(q_nope, q_pe, ckv_cache, kpe_cache, qo_indptr, kv_in
 
 def mla_paged_decode(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.Tensor, kpe_cache: torch.Tensor,
                      kv_indptr: torch.Tensor, kv_indices: torch.Tensor, sm_scale: float,
-                     split_tokens: int = 256, max_kv_len: Optional[int] = None,
+                     split_tokens: Optional[int] = None, max_kv_len: Optional[int] = None,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                      partials: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
     """MLA decode, one new token per sequence: q_nope [B, 16, 512], q_pe [B, 16, 64].
-    Returns (out [B, 16, 512] bf16, lse [B, 16] base 2). ``max_kv_len`` defaults to the
+    Returns (out [B, 16, 512] bf16, lse [B, 16] base 2). ``split_tokens`` keys per split;
+    by default the longest sequence is cut into as many splits as keep every (split,
+    sequence) item in one round of one workgroup per compute unit (measured fastest: each
+    split costs a 32 KB partial row and an LDS merge, and a second round waits for the
+    first). ``max_kv_len`` defaults to the
     largest kv_indptr step (one device-to-host read); ``partials`` (acc, m, l) scratch is
     allocated when not given."""
     for n, t in (("q_nope", q_nope), ("q_pe", q_pe), ("ckv_cache", ckv_cache), ("kpe_cache", kpe_cache)):
@@ -497,8 +501,12 @@ def mla_paged_decode(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.
         raise ValueError("q_nope / q_pe must be [batch, heads, dim] and kv_indptr [batch + 1]")
     if max_kv_len is None:
         max_kv_len = int((kv_indptr[1:] - kv_indptr[:-1]).max().item()) if B > 0 else 0
-    P = max(1, -(-int(max_kv_len) // int(split_tokens)))
     dev = q_nope.device
+    if split_tokens is None:
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        per_seq = max(1, cus // max(1, B))
+        split_tokens = max(16, -(-max(1, -(-int(max_kv_len) // per_seq)) // 16) * 16)
+    P = max(1, -(-int(max_kv_len) // int(split_tokens)))
     if partials is None:
         partials = (torch.empty((B, H, P, Dc), dtype=torch.float32, device=dev),
                     torch.empty((B, H, P), dtype=torch.float32, device=dev),
