@@ -102,6 +102,14 @@ def gather_sequence(key_cache, value_cache, layout: str, block_table_row, n: int
     return K, V
 
 
+def _dequant(x: np.ndarray, cache_scale: float) -> np.ndarray:
+    """Values of a quantized cache: the stored value (already upcast exactly to float64)
+    times the cache's scale. The PagedAttention V2 page's launcher takes kv_cache_dtype,
+    k_scale and v_scale without defining them; the plainest reading is a per-tensor
+    dequantization factor, 1 for an unquantized cache."""
+    return x * float(cache_scale)
+
+
 def _kv_head(h: int, group: int) -> int:
     """Query head h belongs to the contiguous group of kv head h // G (both decode pages)."""
     return h // group
@@ -127,12 +135,15 @@ def _scores(q_vec: np.ndarray, K: np.ndarray, scale: float, slope=None) -> np.nd
 
 
 def decode(query, key_cache, value_cache, layout: str, block_tables, seq_lens, scale: float,
-           num_kv_heads: int, block_size: int, alibi_slopes=None):
+           num_kv_heads: int, block_size: int, alibi_slopes=None, k_scale: float = 1.0,
+           v_scale: float = 1.0):
     """Unsplit decode attention. Returns (out [S,H,D], lse [S,H]) in float64.
 
     out[b,h] = sum_t softmax(s)_t v_t and lse[b,h] = log sum_t exp(s_t), natural log,
     over the sequence's len_b tokens (with the ALiBi bias of head h when alibi_slopes [H]
-    is given). len_b = 0 gives zeros and -inf.
+    is given). len_b = 0 gives zeros and -inf. A quantized cache (float8 pools) holds
+    k_t / k_scale and v_t / v_scale: the keys and values used are the stored values times
+    k_scale and v_scale (see _dequant).
     """
     slopes = None if alibi_slopes is None else _as_f64(alibi_slopes)
     q = _as_f64(query)
@@ -149,6 +160,7 @@ def decode(query, key_cache, value_cache, layout: str, block_tables, seq_lens, s
         if n == 0:
             continue
         K, V = gather_sequence(key_cache, value_cache, layout, bt[b], n, block_size)
+        K, V = _dequant(K, k_scale), _dequant(V, v_scale)
         for h in range(H):
             kh = _kv_head(h, G)
             s = _scores(q[b, h], K[kh], scale, None if slopes is None else slopes[h])
@@ -188,7 +200,7 @@ def partition_ranges(n: int, block_size: int, partition_size: int, num_splits: i
 def decode_partials(query, key_cache, value_cache, layout: str, block_tables, seq_lens,
                     scale: float, num_kv_heads: int, block_size: int, partition_size: int,
                     max_num_partitions: int, num_splits: int = 0, normalized: bool = False,
-                    alibi_slopes=None):
+                    alibi_slopes=None, k_scale: float = 1.0, v_scale: float = 1.0):
     """Split-K partials per (b, h, p): (acc [S,H,P,D], m [S,H,P], l [S,H,P]) in float64.
 
     Partition p of sequence b covers the token range ``partition_ranges`` gives (fixed
@@ -222,6 +234,7 @@ def decode_partials(query, key_cache, value_cache, layout: str, block_tables, se
         if len(ranges) > P:
             raise ValueError("max_num_partitions too small for this sequence")
         K, V = gather_sequence(key_cache, value_cache, layout, bt[b], n, block_size)
+        K, V = _dequant(K, k_scale), _dequant(V, v_scale)
         for h in range(H):
             kh = _kv_head(h, G)
             s = _scores(q[b, h], K[kh], scale, None if slopes is None else slopes[h])

@@ -456,6 +456,42 @@ def pin_alibi_split_invariance(orc):
                 _close(out[b, h], (w / w.sum()) @ V[b][h // 2], 1e-12, what="alibi reweighting")
 
 
+def pin_quantized_cache(orc):
+    """float8 (e4m3) pools: with unit scales the result is dense brute force on the stored
+    values; k_scale acts exactly like a factor on the softmax scale (out and lse); v_scale
+    multiplies out and leaves lse alone; the same for split partials."""
+    lens = [1, 16, 37, 0, 70]
+    H, KVH, D, bs = 4, 2, 16, 4  # x-packed fp8 keys: x = 16 one-byte elements per chunk
+    for layout in ("token_major", "xpacked"):
+        rng = np.random.default_rng(47)
+        K = [torch.from_numpy(rng.standard_normal((KVH, n, D))).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+             for n in lens]
+        V = [torch.from_numpy(rng.standard_normal((KVH, n, D))).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+             for n in lens]
+        pages = sum(-(-n // bs) for n in lens)
+        kc, vc, bt = scatter_pool(K, V, lens, bs, pages + 3, layout, x=16, rng=rng)
+        kc8 = torch.from_numpy(kc).to(torch.float8_e4m3fn)
+        vc8 = torch.from_numpy(vc).to(torch.float8_e4m3fn)
+        q = rng.standard_normal((len(lens), H, D))
+        lens_a = np.asarray(lens)
+        out, lse = orc.decode(q, kc8, vc8, layout, bt, lens_a, 0.4, KVH, bs)
+        ref_out, ref_lse = _brute_decode(q, K, V, lens_a, 0.4, H // KVH)
+        _close(out, ref_out, 1e-12, what="fp8 pools, unit scales")
+        _close(lse, ref_lse, 1e-12, what="fp8 pools, unit scales lse")
+        o_k, s_k = orc.decode(q, kc8, vc8, layout, bt, lens_a, 0.4, KVH, bs, k_scale=0.25)
+        o_s, s_s = orc.decode(q, kc8, vc8, layout, bt, lens_a, 0.1, KVH, bs)
+        _close(o_k, o_s, 1e-12, what="k_scale as a softmax-scale factor")
+        _close(s_k, s_s, 1e-12, what="k_scale as a softmax-scale factor (lse)")
+        o_v, s_v = orc.decode(q, kc8, vc8, layout, bt, lens_a, 0.4, KVH, bs, v_scale=3.0)
+        _close(o_v, 3.0 * out, 1e-12, what="v_scale multiplies out")
+        _close(s_v, lse, 1e-12, what="v_scale leaves lse")
+        acc, m, l = orc.decode_partials(q, kc8, vc8, layout, bt, lens_a, 0.4, KVH, bs, 16, 5, k_scale=0.25,
+                                        v_scale=3.0)
+        o2, s2 = orc.reduce_partials(acc, m, l, lens_a, 16)
+        _close(o2, 3.0 * o_s, 1e-12, what="quantized partials")
+        _close(s2, s_s, 1e-12, what="quantized partials lse")
+
+
 # ----------------------------------------------------------------------------------------
 # MLA pins
 # ----------------------------------------------------------------------------------------
@@ -628,7 +664,8 @@ def pin_mla_multi_token_pages(orc):
 DECODE_PINS = [pin_decode_worked_example, pin_reduce_worked_example, pin_decode_brute_force,
                pin_decode_special_cases, pin_split_invariance, pin_partition_stats,
                pin_sentinel_padding, pin_page_permutation, pin_empty_sequence, pin_split_policy,
-               pin_normalized_partials, pin_alibi_closed_forms, pin_alibi_split_invariance]
+               pin_normalized_partials, pin_alibi_closed_forms, pin_alibi_split_invariance,
+               pin_quantized_cache]
 MLA_PINS = [pin_mla_worked_example, pin_mla_sdpa, pin_mla_causal_perturbation,
             pin_mla_special_cases, pin_mla_multi_token_pages]
 ALL_PINS = DECODE_PINS + MLA_PINS

@@ -54,6 +54,10 @@ MUTATIONS = [
      "ALiBi query position n instead of n - 1"),
     ("decode.py", "s = _scores(q[b, h], K[kh], scale, None if slopes is None else slopes[h])",
      "s = _scores(q[b, h], K[kh], scale, None if slopes is None else slopes[kh])", 0, "ALiBi slope of the kv head"),
+    ("decode.py", "K, V = _dequant(K, k_scale), _dequant(V, v_scale)\n        for h in range(H):\n            kh = _kv_head(h, G)\n            s = _scores(q[b, h], K[kh], scale, None if slopes is None else slopes[h])\n            M = s.max()",
+     "K, V = _dequant(K, v_scale), _dequant(V, k_scale)\n        for h in range(H):\n            kh = _kv_head(h, G)\n            s = _scores(q[b, h], K[kh], scale, None if slopes is None else slopes[h])\n            M = s.max()",
+     0, "cache scales swapped"),
+    ("decode.py", "return x * float(cache_scale)", "return x", 0, "cache scale dropped"),
     ("mla.py", "vis = min(prefix + i + 1, kv_len)", "vis = min(prefix + i, kv_len)", 0, "causal off by one"),
     ("mla.py", "return sm_scale * (qn_row @ Kc.T + qp_row @ Kp.T)", "return sm_scale * (qn_row @ Kc.T)", 0,
      "kpe term dropped"),
