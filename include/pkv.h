@@ -60,7 +60,7 @@ typedef enum {
   PKV_EHIP = 3           /* the HIP runtime reported an error for the launch        */
 } pkv_status;
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 /* K/V caches only (paged_attention_v2) */ } pkv_dtype;
 
 typedef enum {
   /* K and V: [num_blocks, num_kv_heads, block_size, head_dim]            ([FD] kernel arguments) */
@@ -228,8 +228,12 @@ int paged_decode(const void* query, int dtype,
  *   Smith and Lewis, ICLR 2022): the score of key t of sequence b for head h becomes
  *   scale * <q, k_t> - alibi_slopes[h] * (len_b - 1 - t), the decoded token being the
  *   sequence's last position.
- * [PAv2]'s kv_cache_dtype, k_scale and v_scale have no argument here (the cache is read
- * in `dtype`, unscaled).
+ * kv_cache_dtype  `dtype` (the cache holds the query's type; k_scale = v_scale = 1 required),
+ *   or PKV_FP8_E4M3: key_cache / value_cache hold float8 e4m3 (OCP) values, x-packed with
+ *   x = 16; the keys and values used are k_scale and v_scale times the stored values
+ *   ([PAv2]'s launcher takes these three arguments without using them; this is the plainest
+ *   reading, a per-tensor dequantization factor). Needs a bf16 query and at most 8 query
+ *   heads per kv head.
  * PKV_EINVAL / PKV_EUNSUPPORTED: as paged_decode_partial with partition_size = 512.
  */
 int paged_attention_v2(void* out, float* exp_sums, float* max_logits, float* tmp_output,
@@ -240,7 +244,8 @@ int paged_attention_v2(void* out, float* exp_sums, float* max_logits, float* tmp
                        const int32_t* seq_lens,
                        int num_seqs, int num_heads, int head_size, int block_size,
                        int num_blocks, int max_seq_len, int max_num_partitions,
-                       const float* alibi_slopes, void* stream);
+                       const float* alibi_slopes, int kv_cache_dtype, float k_scale,
+                       float v_scale, void* stream);
 
 /*
  * mla_paged_prefill -- MLA causal paged prefill, page_size 1 ([MLA]).

@@ -81,7 +81,7 @@ def lib() -> ctypes.CDLL:
                                i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.paged_decode.restype = i32
     L.paged_attention_v2.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, i32, vp, i32, i32, i32, i32,
-                                     i32, i32, i32, vp, vp]
+                                     i32, i32, i32, vp, i32, f32, f32, vp]
     L.paged_attention_v2.restype = i32
     L.mla_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                     f32, vp, vp, vp]
@@ -369,17 +369,45 @@ def paged_attention_v2(out: torch.Tensor, exp_sums: torch.Tensor, max_logits: to
 
     x-packed caches, 512-token partitions; tmp_output holds each partition's normalized
     average, exp_sums its l and max_logits its m. ``alibi_slopes`` [H] float32 adds the
-    ALiBi bias -slope_h * (len - 1 - t). fp8 caches and K/V scales are accepted by that
-    launcher but unused there, and are refused here unless absent.
+    ALiBi bias -slope_h * (len - 1 - t). ``kv_cache_dtype`` "fp8" / "fp8_e4m3": the caches
+    are torch.float8_e4m3fn (x-packed with x = 16) and the keys and values used are k_scale
+    and v_scale times the stored values.
     """
     if alibi_slopes is not None:
         _dev("alibi_slopes", alibi_slopes, torch.float32, 1)
         if alibi_slopes.numel() != query.shape[1]:
             raise ValueError("alibi_slopes must hold one slope per query head")
-    if kv_cache_dtype != "auto" or float(k_scale) != 1.0 or float(v_scale) != 1.0:
-        raise NotImplementedError("paged_attention_v2: only kv_cache_dtype='auto' with unit k/v scales")
-    S, H, D, nb, bs = _check_decode_inputs(query, key_cache, value_cache, block_tables, seq_lens,
-                                           num_kv_heads, XPACKED)
+    if kv_cache_dtype in ("fp8", "fp8_e4m3"):
+        kv_code = 2
+        if key_cache.dtype != torch.float8_e4m3fn or value_cache.dtype != torch.float8_e4m3fn:
+            raise ValueError("kv_cache_dtype='fp8' needs torch.float8_e4m3fn caches")
+        # geometry checks on byte views (same shapes, one byte per element)
+        kc_chk, vc_chk = key_cache.view(torch.uint8), value_cache.view(torch.uint8)
+    elif kv_cache_dtype == "auto":
+        if float(k_scale) != 1.0 or float(v_scale) != 1.0:
+            raise ValueError("k_scale / v_scale apply to a float8 cache only")
+        kv_code = None
+        kc_chk, vc_chk = key_cache, value_cache
+    else:
+        raise NotImplementedError(f"paged_attention_v2: kv_cache_dtype {kv_cache_dtype!r}")
+    if query.dtype not in _DTYPE:
+        raise ValueError(f"query dtype {query.dtype} not supported")
+    _dev("query", query, ndim=3)
+    _dev("key_cache", key_cache)
+    _dev("value_cache", value_cache)
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("seq_lens", seq_lens, torch.int32, 1)
+    S, H, D = query.shape
+    nb, bs, kd = _pool_geometry(kc_chk, XPACKED)
+    x_expect = 16 // key_cache.element_size()
+    if kd != D or kc_chk.shape[4] != x_expect or kc_chk.shape[1] != num_kv_heads:
+        raise ValueError("key_cache must be [num_blocks, num_kv_heads, head_size / x, block_size, x]")
+    if tuple(vc_chk.shape) != (nb, num_kv_heads, D, bs):
+        raise ValueError("value_cache must be [num_blocks, num_kv_heads, head_size, block_size]")
+    if kv_code is None:
+        if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
+            raise ValueError("caches must have the query's dtype")
+        kv_code = _DTYPE[query.dtype]
     if bs != int(block_size):
         raise ValueError(f"block_size {block_size} does not match the cache ({bs})")
     P = _check_partials(tmp_output, max_logits, exp_sums, S, H, D)
@@ -390,7 +418,7 @@ def paged_attention_v2(out: torch.Tensor, exp_sums: torch.Tensor, max_logits: to
         _ptr(out), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_output), _ptr(query), _DTYPE[query.dtype],
         _ptr(key_cache), _ptr(value_cache), int(num_kv_heads), float(scale), _ptr(block_tables),
         block_tables.shape[1], _ptr(seq_lens), S, H, D, bs, nb, int(max_seq_len), P, _ptr(alibi_slopes),
-        _stream(query.device))
+        kv_code, float(k_scale), float(v_scale), _stream(query.device))
     _check(st, "paged_attention_v2")
 
 

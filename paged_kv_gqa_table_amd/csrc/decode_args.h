@@ -23,6 +23,8 @@ struct DecodePartialArgs {
   int normalize;          // != 0: store acc / l instead of acc
   const float* alibi;     // [H] ALiBi slopes (natural-log units), or null: score of key t
                           // gets -slope_h * (len - 1 - t)
+  int kv_fp8;             // != 0: K/V pools hold float8 e4m3 (query and out stay bf16)
+  float v_scale;          // float8 V dequantization factor (k_scale is folded into scale_log2)
   int P;                  // max_num_partitions: stride of the partial arrays
   float* acc;             // [S, H, P, D]; may be null in final mode when P == 1
   float* m;               // [S, H, P]

@@ -26,6 +26,23 @@ namespace pkv {
 
 constexpr float kRebaseBf16 = 8.f;  // log2 headroom of the lazy softmax re-basing
 
+// 8 K/V elements as bf16 pairs: bf16 as loaded, or 8 float8 e4m3 values converted
+// (every e4m3 value is exactly representable in bf16).
+PKV_DEVICE uint4 as_bf16x8(const uint4& v) { return v; }
+PKV_DEVICE uint4 as_bf16x8(const uint2& v) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true);
+  return make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]),
+                    pack_bf16x2(d[0], d[1]));
+}
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+PKV_DEVICE uint2 ld8_nt(const void* p) {  // non-temporal 8-byte load (float8 K/V)
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v[0], v[1]);
+}
+
 template <int D, bool XP>
 struct Bf16Cfg {
   static constexpr int BS = 16;
@@ -72,14 +89,18 @@ struct Bf16Smem {
 // page ids of the next item are fetched after its length (one more round trip per item).
 // FINAL: the launch produces the output (final mode of DecodePartialArgs); compiled
 // separately so that the plain partial kernel carries none of its code. ALIBI: scores
-// carry the ALiBi bias (compiled only for the plain partial mode).
-template <int D, int G, bool XP, int W, bool DENSE, bool SPLIT, bool FINAL, bool ALIBI>
+// carry the ALiBi bias (compiled only for the plain partial mode). FP8: the K/V pools hold
+// float8 e4m3 values (one byte each, same element order; x-packed keys in 16-element
+// chunks), loaded 8 bytes where bf16 loads 16 and converted exactly to bf16 right before
+// use; k_scale is folded into scale_log2 and v_scale multiplies the merged accumulator.
+template <int D, int G, bool XP, int W, bool DENSE, bool SPLIT, bool FINAL, bool ALIBI, bool FP8 = false>
 __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const DenseItems& wl, int first_item,
                                            Bf16Smem<W, G, D>& sm) {
   using C = Bf16Cfg<D, XP>;
   constexpr int BS = C::BS, ROWB = C::ROWB, KCPL = C::KCPL, LV = C::LV, VT = C::VT, VCPL = C::VCPL;
   constexpr int NVC = C::NVC, NACC = C::NACC, NVREG = C::NVREG;
-  constexpr int PAGEB = BS * ROWB;
+  constexpr int KVROWB = FP8 ? D : ROWB;       // bytes of a K/V token row (the query stays bf16)
+  constexpr int PAGEB = BS * KVROWB;
   constexpr int QCH = G * (ROWB / 16);          // 16-byte chunks of the G query rows
 
   const int lane = threadIdx.x & 63;
@@ -137,10 +158,14 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
             (__attribute__((address_space(3))) void*)(&sm.q_lds[slot][0][0] + c0 * 4), 16, 0, 0);
     }
   };
+  // byte offset of the 8 key elements 8 cc .. 8 cc + 7 of token t within a page
   auto k_off = [&](int t, int cc) -> int {
-    if constexpr (XP) return (cc * BS + t) * 16;
+    if constexpr (XP && FP8) return ((cc >> 1) * BS + t) * 16 + (cc & 1) * 8;
+    else if constexpr (XP) return (cc * BS + t) * 16;
+    else if constexpr (FP8) return t * KVROWB + cc * 8;
     else return t * ROWB + cc * 16;
   };
+  constexpr int CHB = FP8 ? 8 : 16;  // bytes of 8 K/V elements
 
   // ---- the first item: ids, length and q in one memory round trip
   int nb, nkvh, np;
@@ -200,14 +225,20 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
         pid_cache = id < 0 ? 0 : (id >= a.NB ? a.NB - 1 : id);
       }
     };
-    uint4 kr[2][KCPL];
-    uint4 vr[NVREG];
+    using KVReg = typename std::conditional<FP8, uint2, uint4>::type;  // 8 elements as loaded
+    KVReg kr[2][KCPL];
+    KVReg vraw[NVREG];
     // Pages are loaded non-temporally, except each wave's last page of the item: the loop
     // refills the registers past the end by re-reading that page (so the loads stay
     // unconditional and need no merge copies), which must then be an L2 hit, not HBM.
-    auto ldkv = [&](auto nt, const char* p) -> uint4 {
-      if constexpr (decltype(nt)::value) return ld16_kv(p);
-      else return ld16(p);
+    auto ldkv = [&](auto nt, const char* p) -> KVReg {
+      if constexpr (FP8) {
+        if constexpr (decltype(nt)::value) return ld8_nt(p);
+        else return *reinterpret_cast<const uint2*>(p);
+      } else {
+        if constexpr (decltype(nt)::value) return ld16_kv(p);
+        else return ld16(p);
+      }
     };
     auto issue_k = [&](auto nt, int i) {
       const char* kp = page_ptr(kbase, i);
@@ -220,13 +251,13 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
       const char* vp = page_ptr(vbase, i);
       if constexpr (XP) {
 #pragma unroll
-        for (int q = 0; q < NVC; ++q) vr[q] = ldkv(nt, vp + (size_t)(64 * q + lane) * 16);
+        for (int q = 0; q < NVC; ++q) vraw[q] = ldkv(nt, vp + (size_t)(64 * q + lane) * CHB);
       } else {
 #pragma unroll
         for (int j = 0; j < VT; ++j)
 #pragma unroll
           for (int k = 0; k < VCPL; ++k)
-            vr[j * VCPL + k] = ldkv(nt, vp + (vt + (64 / LV) * j) * ROWB + (vc + LV * k) * 16);
+            vraw[j * VCPL + k] = ldkv(nt, vp + (vt + (64 / LV) * j) * KVROWB + (vc + LV * k) * CHB);
       }
     };
     using Streaming = std::true_type;  // non-temporal loads
@@ -287,10 +318,11 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
           float d0 = 0.f, d1 = 0.f;
 #pragma unroll
           for (int k = 0; k < KCPL; ++k) {
-            d0 = dot2_bf16(qv[k].x, kr[j][k].x, d0);
-            d1 = dot2_bf16(qv[k].y, kr[j][k].y, d1);
-            d0 = dot2_bf16(qv[k].z, kr[j][k].z, d0);
-            d1 = dot2_bf16(qv[k].w, kr[j][k].w, d1);
+            const uint4 kk = as_bf16x8(kr[j][k]);
+            d0 = dot2_bf16(qv[k].x, kk.x, d0);
+            d1 = dot2_bf16(qv[k].y, kk.y, d1);
+            d0 = dot2_bf16(qv[k].z, kk.z, d0);
+            d1 = dot2_bf16(qv[k].w, kk.w, d1);
           }
           s[g][j] = d0 + d1;
         }
@@ -335,6 +367,10 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
       }
       wave_lds_fence();
 
+      // V as bf16 pairs (a conversion under FP8, a plain copy otherwise)
+      uint4 vr[NVREG];
+#pragma unroll
+      for (int q = 0; q < NVREG; ++q) vr[q] = as_bf16x8(vraw[q]);
       // ---- tail page: zero V of invalid tokens (their slots may hold anything, even NaN)
       if (ntok < BS) {
         if constexpr (XP) {
@@ -469,6 +505,7 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
         o = fmaf(f, sm.red_acc[v][g][d], o);
         L = fmaf(f, sm.red_l[v][g], L);
       }
+      if constexpr (FP8) o *= a.v_scale;
       store_item_value<D, true>(a, bh0 + g, p, d, o, M, L, single);
     }
     __syncthreads();
@@ -483,7 +520,7 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
 // 128 VGPRs without spilling, else no constraint.
 constexpr int bf16_min_waves(int D, int G) { return (D == 64 && G <= 5) || (D == 128 && G <= 4) ? 4 : 1; }
 
-template <int D, int G, bool XP, int W, bool DENSE, bool SPLIT, bool FINAL, bool ALIBI>
+template <int D, int G, bool XP, int W, bool DENSE, bool SPLIT, bool FINAL, bool ALIBI, bool FP8>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(bf16_min_waves(D, G), 8))) void decode_partial_bf16_kernel(DecodePartialArgs a, int grid_parts) {
   __shared__ Bf16Smem<W, G, D> sm;
   if constexpr (DENSE) {
@@ -494,9 +531,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(bf16_min
     write_sentinels(wl, a.H, grid_parts, a.P, a.m, a.l);
     if constexpr (FINAL) write_empty_outputs<D, true>(wl, a);
     const int first = wg_item(wl, blockIdx.x, gridDim.x, 0);
-    if (first >= 0) bf16_items<D, G, XP, W, true, SPLIT, FINAL, ALIBI>(a, wl, first, sm);
+    if (first >= 0) bf16_items<D, G, XP, W, true, SPLIT, FINAL, ALIBI, FP8>(a, wl, first, sm);
   } else {
-    bf16_items<D, G, XP, W, false, SPLIT, FINAL, ALIBI>(a, DenseItems{}, blockIdx.x, sm);
+    bf16_items<D, G, XP, W, false, SPLIT, FINAL, ALIBI, FP8>(a, DenseItems{}, blockIdx.x, sm);
   }
 }
 
@@ -510,7 +547,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(bf16_min
 #define PKV_BF16_WAVES 0
 #endif
 constexpr int bf16_waves(int D) { return PKV_BF16_WAVES > 0 ? PKV_BF16_WAVES : (D == 128 ? 3 : 4); }
-template <bool XP, int D, int G, bool SPLIT, bool FINAL, bool ALIBI>
+template <bool XP, int D, int G, bool SPLIT, bool FINAL, bool ALIBI, bool FP8 = false>
 hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
   constexpr int W = bf16_waves(D);
   const long upper = (long)a.S * a.KVH * grid_parts;
@@ -524,7 +561,8 @@ hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream
   if constexpr (!SPLIT && !FINAL) {
     if (!plain) {
       const int pcap = resident_grid(
-          reinterpret_cast<const void*>(&decode_partial_bf16_kernel<D, G, XP, W, false, false, false, ALIBI>), 64 * W, 0);
+          reinterpret_cast<const void*>(&decode_partial_bf16_kernel<D, G, XP, W, false, false, false, ALIBI, FP8>), 64 * W,
+          0);
       plain = upper <= 2L * pcap;
     }
   }
@@ -536,14 +574,15 @@ hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream
 #ifndef PKV_RESIDENT_RATIO
 #define PKV_RESIDENT_RATIO 4
 #endif
-    int cap = resident_grid(reinterpret_cast<const void*>(&decode_partial_bf16_kernel<D, G, XP, W, true, SPLIT, FINAL, ALIBI>),
-                            64 * W, lds);
+    int cap = resident_grid(
+        reinterpret_cast<const void*>(&decode_partial_bf16_kernel<D, G, XP, W, true, SPLIT, FINAL, ALIBI, FP8>), 64 * W,
+        lds);
     if (upper > (long)PKV_RESIDENT_RATIO * cap) cap = dense_grid_cap();
     const int grid = (int)(upper < cap ? upper : cap);
-    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, true, SPLIT, FINAL, ALIBI>), dim3(grid), dim3(64 * W),
-                       lds, s, a, grid_parts);
+    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, true, SPLIT, FINAL, ALIBI, FP8>), dim3(grid),
+                       dim3(64 * W), lds, s, a, grid_parts);
   } else if constexpr (!SPLIT && !FINAL) {
-    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, false, false, false, ALIBI>), dim3((unsigned)upper),
+    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, false, false, false, ALIBI, FP8>), dim3((unsigned)upper),
                        dim3(64 * W), 0, s, a, grid_parts);
   } else {
     return hipErrorNotSupported;  // NUM_SPLITS and one-launch decode use the work list (kMaxDenseSeqs sequences)
@@ -554,6 +593,11 @@ hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream
 template <bool XP, int D, int G>
 hipError_t launch_bf16_g(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
   const bool fin = a.out != nullptr;
+  if (a.kv_fp8) {  // float8 caches: plain partials only (the PagedAttention V2 interface)
+    if (fin || a.nsplit > 0) return hipErrorNotSupported;
+    return a.alibi != nullptr ? launch_bf16_one<XP, D, G, false, false, true, true>(a, grid_parts, s)
+                              : launch_bf16_one<XP, D, G, false, false, false, true>(a, grid_parts, s);
+  }
   if (a.alibi != nullptr)  // ALiBi: plain partials only
     return (fin || a.nsplit > 0) ? hipErrorNotSupported : launch_bf16_one<XP, D, G, false, false, true>(a, grid_parts, s);
   if (a.nsplit > 0)

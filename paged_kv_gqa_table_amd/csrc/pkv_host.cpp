@@ -104,6 +104,8 @@ struct Phase1Mode {
   float* lse;
   int* counters;
   const float* alibi;   // [num_heads] ALiBi slopes or null (plain partials only)
+  int kv_fp8;           // K/V pools in float8 e4m3 (plain partials only)
+  float k_scale, v_scale;
 };
 
 // Validation and dispatch shared by every decode entry point. `who` names the entry point
@@ -181,6 +183,9 @@ int decode_phase1(const char* who, const void* query, int dtype, const void* key
   a.len_cap = (int)std::min<int64_t>(table_tokens, a.nsplit > 0 ? table_tokens : (int64_t)max_num_partitions * a.ps);
   a.normalize = mode.normalize;
   a.alibi = mode.alibi;
+  a.kv_fp8 = mode.kv_fp8;
+  a.v_scale = mode.v_scale;
+  if (mode.kv_fp8) a.scale_log2 *= mode.k_scale;
   a.P = max_num_partitions;
   a.acc = partial_acc; a.m = partial_m; a.l = partial_l;
   a.out = mode.out; a.lse = mode.lse; a.counters = mode.counters;
@@ -188,7 +193,9 @@ int decode_phase1(const char* who, const void* query, int dtype, const void* key
 
   hipError_t e;
   const bool xp = layout == PKV_KV_XPACKED;
-  if (bf16 && G >= 8) {
+  if (mode.kv_fp8) {
+    e = xp ? pkv::launch_decode_valu_bf16_xp(a, G, grid_parts, s) : pkv::launch_decode_valu_bf16_tm(a, G, grid_parts, s);
+  } else if (bf16 && G >= 8) {
     e = xp ? pkv::launch_decode_mfma_bf16_xp(a, G, grid_parts, s)
            : pkv::launch_decode_mfma_bf16_tm(a, G, grid_parts, s);
   } else if (bf16) {
@@ -238,7 +245,7 @@ extern "C" int paged_decode_partial(const void* query, int dtype, const void* ke
                                     float scale, int partition_size, int max_num_partitions,
                                     int max_seq_len, float* partial_acc, float* partial_m,
                                     float* partial_l, void* stream) {
-  const Phase1Mode mode{partition_size, 0, 0, nullptr, nullptr, nullptr, nullptr};
+  const Phase1Mode mode{partition_size, 0, 0, nullptr, nullptr, nullptr, nullptr, 0, 1.f, 1.f};
   return decode_phase1("paged_decode_partial", query, dtype, key_cache, value_cache, layout, block_tables,
                        max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, scale, max_num_partitions, max_seq_len, partial_acc, partial_m, partial_l, mode,
@@ -261,7 +268,7 @@ extern "C" int paged_decode_split_partial(const void* query, int dtype, const vo
                                           int num_blocks, float scale, int num_splits, int max_seq_len,
                                           float* partial_acc, float* partial_m, float* partial_l, void* stream) {
   if (num_splits <= 0) return fail(PKV_EINVAL, "paged_decode_split_partial: num_splits must be positive");
-  const Phase1Mode mode{0, num_splits, 0, nullptr, nullptr, nullptr, nullptr};
+  const Phase1Mode mode{0, num_splits, 0, nullptr, nullptr, nullptr, nullptr, 0, 1.f, 1.f};
   return decode_phase1("paged_decode_split_partial", query, dtype, key_cache, value_cache, layout, block_tables,
                        max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, scale, num_splits, max_seq_len, partial_acc, partial_m, partial_l, mode, stream);
@@ -283,7 +290,7 @@ extern "C" int paged_decode(const void* query, int dtype, const void* key_cache,
                             int max_num_partitions, int max_seq_len, float* partial_acc, float* partial_m,
                             float* partial_l, int32_t* counters, void* out, float* lse, void* stream) {
   if (!out) return fail(PKV_EINVAL, "paged_decode: NULL pointer argument (out)");
-  const Phase1Mode mode{partition_size, num_splits, 0, out, lse, counters, nullptr};
+  const Phase1Mode mode{partition_size, num_splits, 0, out, lse, counters, nullptr, 0, 1.f, 1.f};
   return decode_phase1("paged_decode", query, dtype, key_cache, value_cache, layout, block_tables,
                        max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, scale, max_num_partitions, max_seq_len, partial_acc, partial_m, partial_l, mode,
@@ -295,8 +302,21 @@ extern "C" int paged_attention_v2(void* out, float* exp_sums, float* max_logits,
                                   int num_kv_heads, float scale, const int32_t* block_tables,
                                   int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_heads,
                                   int head_size, int block_size, int num_blocks, int max_seq_len,
-                                  int max_num_partitions, const float* alibi_slopes, void* stream) {
-  const Phase1Mode mode{kPagedAttentionV2Partition, 0, 1, nullptr, nullptr, nullptr, alibi_slopes};
+                                  int max_num_partitions, const float* alibi_slopes, int kv_cache_dtype,
+                                  float k_scale, float v_scale, void* stream) {
+  if (kv_cache_dtype != dtype && kv_cache_dtype != PKV_FP8_E4M3)
+    return fail(PKV_EINVAL, "paged_attention_v2: kv_cache_dtype %d is neither the query dtype nor PKV_FP8_E4M3",
+                kv_cache_dtype);
+  const bool fp8 = kv_cache_dtype == PKV_FP8_E4M3;
+  if (!std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PKV_EINVAL, "paged_attention_v2: k_scale / v_scale not finite");
+  if (!fp8 && (k_scale != 1.f || v_scale != 1.f))
+    return fail(PKV_EINVAL, "paged_attention_v2: k_scale / v_scale apply to a float8 cache only");
+  if (fp8 && (dtype != PKV_BF16 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || num_heads / num_kv_heads > 8))
+    return fail(PKV_EUNSUPPORTED, "paged_attention_v2: a float8 cache needs a bf16 query and at most 8 query heads "
+                "per kv head");
+  const Phase1Mode mode{kPagedAttentionV2Partition, 0, 1, nullptr, nullptr, nullptr, alibi_slopes, fp8 ? 1 : 0,
+                        k_scale, v_scale};
   int st = decode_phase1("paged_attention_v2", query, dtype, key_cache, value_cache, PKV_KV_XPACKED, block_tables,
                          max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_size, block_size,
                          num_blocks, scale, max_num_partitions, max_seq_len, tmp_output, max_logits, exp_sums, mode,

@@ -189,15 +189,19 @@ def test_split_entry_points_validation(L):
 
 
 def test_paged_attention_v2_validation(L):
-    def call(alibi=None, D=128, bs=16, P=1, max_seq_len=512, H=8):
-        return L.paged_attention_v2(FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 2, 0.1, FAKE, 32, FAKE, 2, H, D, bs,
-                                    64, max_seq_len, P, alibi, None)
+    def call(alibi=None, D=128, bs=16, P=1, max_seq_len=512, H=8, dtype=1, kv_dtype=1, ks=1.0, vs=1.0):
+        return L.paged_attention_v2(FAKE, FAKE, FAKE, FAKE, FAKE, dtype, FAKE, FAKE, 2, 0.1, FAKE, 32, FAKE, 2, H, D, bs,
+                                    64, max_seq_len, P, alibi, kv_dtype, ks, vs, None)
     assert call(P=1, max_seq_len=513) == EINVAL  # 512-token partitions: 513 tokens need two
     assert call(H=7) == EINVAL               # 7 heads over 2 kv heads
     assert call(D=96) == EUNSUP
-    with pytest.raises(NotImplementedError):  # fp8 caches: accepted by the page's launcher, unused there
+    assert call(kv_dtype=0) == EINVAL           # an f32 cache under a bf16 query
+    assert call(ks=2.0) == EINVAL               # scales belong to a float8 cache
+    assert call(kv_dtype=2, dtype=0) == EUNSUP  # a float8 cache needs a bf16 query
+    assert call(kv_dtype=2, H=32) == EUNSUP     # ... and at most 8 query heads per kv head
+    with pytest.raises(NotImplementedError):
         pkv.paged_attention_v2(None, None, None, None, None, None, None, 2, 0.1, None, None, 16, 0,
-                               kv_cache_dtype="fp8")
+                               kv_cache_dtype="int4")
 
 
 def test_mla_pages_validation(L):

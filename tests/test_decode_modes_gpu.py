@@ -228,3 +228,35 @@ def test_paged_attention_v2_alibi(dtype, D, H, KVH):
     ref, _ = oracle.decode(case.query, case.key_cache, case.value_cache, "xpacked", case.block_tables,
                            case.seq_lens, case.scale, KVH, case.block_size, alibi_slopes=slopes)
     check_out(_np(out), ref, dtype, "v2 alibi out")
+
+
+@pytest.mark.parametrize("D,H,KVH,alibi", [(128, 8, 2, False), (256, 24, 4, False), (64, 4, 4, False),
+                                          (128, 16, 2, True)])
+def test_paged_attention_v2_fp8_cache(D, H, KVH, alibi):
+    """float8 e4m3 caches (x-packed, x = 16) with k_scale / v_scale through the PagedAttention
+    V2 entry point: partials and output against the oracle on the same float8 pools."""
+    case = inputs.make_decode(EDGE_LENS, H, KVH, D, dtype="bf16", layout="xpacked", seed=17 * D + H)
+    k8, v8 = inputs.fp8_xpacked_pools(case)
+    S, P = case.num_seqs, case.num_partitions(512)
+    k_scale, v_scale = 0.5, 2.0
+    slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32) if alibi else None
+    say(f"paged_attention_v2 fp8 cache: D={D} H={H} KVH={KVH} alibi={alibi}")
+    dev = to_dev(case)
+    tmp = torch.full((S, H, P, D), float("nan"), dtype=torch.float32, device="cuda")
+    es = torch.full((S, H, P), float("nan"), dtype=torch.float32, device="cuda")
+    ml = torch.full((S, H, P), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full((S, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pkv.paged_attention_v2(out, es, ml, tmp, dev["q"], k8.to("cuda"), v8.to("cuda"), KVH, case.scale, dev["bt"],
+                           dev["lens"], case.block_size, case.max_seq_len,
+                           alibi_slopes=None if slopes is None else slopes.to("cuda"), kv_cache_dtype="fp8",
+                           k_scale=k_scale, v_scale=v_scale)
+    torch.cuda.synchronize()
+    r = oracle.decode_partials(case.query, k8, v8, "xpacked", case.block_tables, case.seq_lens, case.scale, KVH,
+                               case.block_size, 512, P, normalized=True, alibi_slopes=slopes, k_scale=k_scale,
+                               v_scale=v_scale)
+    _check_ranged_partials(_np(tmp), _np(ml), _np(es), r, case.seq_lens.numpy(),
+                           lambda n: oracle.partition_ranges(n, case.block_size, 512), "bf16", "v2 fp8",
+                           normalized=True)
+    ref, _ = oracle.decode(case.query, k8, v8, "xpacked", case.block_tables, case.seq_lens, case.scale, KVH,
+                           case.block_size, alibi_slopes=slopes, k_scale=k_scale, v_scale=v_scale)
+    check_out(_np(out), ref, "bf16", "v2 fp8 out")
