@@ -137,6 +137,43 @@ def bench_decode(case, steps, warmup, copies=0, one_launch=False):
     )
 
 
+def bench_decode_fp8(case, steps, warmup):
+    """The same batch with a float8 e4m3 cache (x-packed, x = 16) through paged_attention_v2,
+    both phases per step, pools cycled as in bench_decode. KV bytes are one per element."""
+    import torch
+    import paged_kv_gqa_table_amd as pkv
+    from paged_kv_gqa_table_amd import inputs
+    dev = "cuda"
+    k8, v8 = inputs.fp8_xpacked_pools(case)
+    k8, v8 = k8.to(dev), v8.to(dev)
+    pool_bytes = 2 * k8.numel()
+    copies = max(1, min(8, math.ceil(3 * MALL_BYTES / max(1, pool_bytes))))
+    pools = [(k8, v8)] + [(k8.clone(), v8.clone()) for _ in range(copies - 1)]
+    q, bt, lens = case.query.to(dev), case.block_tables.to(dev), case.seq_lens.to(dev)
+    S, H, D = case.num_seqs, case.num_heads, case.head_dim
+    P = case.num_partitions(512)
+    tmp = torch.empty((S, H, P, D), dtype=torch.float32, device=dev)
+    es = torch.empty((S, H, P), dtype=torch.float32, device=dev)
+    ml = torch.empty((S, H, P), dtype=torch.float32, device=dev)
+    out = torch.empty((S, H, D), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        kc, vc = pools[i % copies]
+        pkv.paged_attention_v2(out, es, ml, tmp, q, kc, vc, case.num_kv_heads, case.scale, bt, lens,
+                               case.block_size, case.max_seq_len, kv_cache_dtype="fp8", k_scale=1.0, v_scale=1.0)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    kv_bytes = int(case.seq_lens.sum()) * case.num_kv_heads * 2 * D
+    return dict(ms=ms, kv_bytes=kv_bytes)
+
+
 def read_ceiling(nbytes=1 << 30, reps=20):
     """Median bandwidth of the library's plain streaming read over a buffer 4x the size of
     the Infinity Cache (GB/s): the reference the paged gathers are compared with."""
@@ -404,6 +441,11 @@ def main():
     result["roofline"]["frac_of_measured_read_ceiling"] = achieved / ceiling
     if not args.no_extra and args.workload == "llama_gqa4":
         extra = {}
+        rf = bench_decode_fp8(case, max(20, args.steps // 2), 5)
+        extra["llama_gqa4_fp8_cache_v2"] = {
+            "us_per_step": rf["ms"] * 1e3, "kv_bytes": rf["kv_bytes"],
+            "GB_s": rf["kv_bytes"] / (rf["ms"] * 1e-3) / 1e9,
+            "kernel": "paged_attention_v2 (float8 e4m3 x-packed cache, both phases)"}
         ro = bench_decode(case, max(20, args.steps // 2), 5, one_launch=True)
         extra["llama_gqa4_one_launch"] = {"us_per_step": ro["wall_ms_per_step"] * 1e3,
                                           "GB_s": kv / (ro["wall_ms_per_step"] * 1e-3) / 1e9,
