@@ -260,3 +260,18 @@ def test_paged_attention_v2_fp8_cache(D, H, KVH, alibi):
     ref, _ = oracle.decode(case.query, k8, v8, "xpacked", case.block_tables, case.seq_lens, case.scale, KVH,
                            case.block_size, alibi_slopes=slopes, k_scale=k_scale, v_scale=v_scale)
     check_out(_np(out), ref, "bf16", "v2 fp8 out")
+
+
+def test_python_paged_decode_defaults():
+    """The Python wrapper: default (two launches when there are several partitions, one when
+    a single partition holds every sequence), NUM_SPLITS, and lse output."""
+    case = inputs.make_decode([3, 700, 1500, 0], 8, 2, 128, dtype="bf16", seed=23)
+    dev = to_dev(case)
+    ref = oracle_subset(case, list(range(case.num_seqs)))
+    args = (dev["q"], dev["k"], dev["v"], dev["bt"], dev["lens"], case.scale, 2)
+    say("python paged_decode defaults")
+    for kw in (dict(), dict(max_num_partitions=1), dict(num_splits=4), dict(one_launch=True)):
+        out, lse = pkv.paged_decode(*args, return_lse=True, **kw)
+        torch.cuda.synchronize()
+        check_out(_np(out), ref["out"], "bf16", f"paged_decode {kw}")
+        check_lse(_np(lse), ref["lse"], "bf16", f"paged_decode {kw}")
