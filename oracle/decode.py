@@ -14,7 +14,7 @@ Sources (the pages this restates; no code is taken from them):
     ``_flash_decode_combine_kernel`` (M = max m_s, f = exp(m_s - M),
     out = sum f * acc_s / sum f * l_s; zeros for an empty context).
 
-Readings taken where the pages differ or are silent (each listed in the design doc):
+Readings taken where the pages differ or are silent:
   partial acc is unnormalized (normalized on request, for the PagedAttention V2
   interface); partial m is in natural-log units of the scaled
   score; partitions are token ranges [p*ps, min((p+1)*ps, len)); an empty
