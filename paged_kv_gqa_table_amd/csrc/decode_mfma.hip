@@ -273,8 +273,16 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
     if (nparts > 1) finish_item_fused<D, true, W>(a, b, kvh, G, nparts);
 }
 
+// Waves per SIMD the register allocation must allow. Left alone, the compiler parks the
+// output accumulators in AGPRs and lands at 148-168 registers (three waves per SIMD); held
+// to 128, the partial kernels at D <= 128 fit without spills and four 4-wave workgroups
+// share a CU. The one-launch (FINAL) kernels would spill at 128, and D = 256 cannot fit.
+template <int D, bool FINAL>
+constexpr int mfma_min_waves() { return (D <= 128 && !FINAL) ? 4 : 1; }
+
 template <int D, bool XP, int W, bool DENSE, bool FINAL, bool ALIBI>
-__global__ __launch_bounds__(64 * W) void decode_partial_mfma_kernel(DecodePartialArgs a, int G, int grid_parts) {
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(mfma_min_waves<D, FINAL>())))
+void decode_partial_mfma_kernel(DecodePartialArgs a, int G, int grid_parts) {
   __shared__ MfmaSmem<W, D> sm;
   if constexpr (DENSE) {
     extern __shared__ int s_worklist[];

@@ -11,10 +11,12 @@
 //  * P <= 16: one wave per (sequence, head) (reduce_row_wave in decode_epilogue.h, shared
 //    with the one-launch decode); each lane owns D / 64 contiguous output dims, so every
 //    partition row of acc is one coalesced 256 B - 1 KiB read, 8 rows in flight.
-//  * P > 16: one workgroup of 4 waves per (sequence, head); wave w combines its quarter of
-//    the partitions the same way (16 rows in flight), then the four waves' (max, sum,
-//    accumulator) merge through LDS with the same weighting, so a sequence of 128
-//    partitions takes two memory round trips instead of sixteen. (For short contexts the
+//  * P > 16: one workgroup of 4 waves per (sequence, head). A row of more than 8
+//    partitions: wave w combines its quarter of them the same way (16 rows in flight),
+//    then the four waves' (max, sum, accumulator) merge through LDS with the same
+//    weighting, so a sequence of 128 partitions takes two memory round trips instead of
+//    sixteen. A row of at most 8 in such a batch takes the one-wave path (one round trip)
+//    and the other three waves leave at once. (For batches of short contexts only, the
 //    four-fold launch costs more than it saves.)
 // Partitions past P_b are never read (their acc rows are not even written by phase 1).
 #include <type_traits>
@@ -44,6 +46,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeReduceArgs a) 
 
 constexpr int kReduceWaves = 4;
 constexpr int kReduceSplitP = 16;  // partition bound above which a row gets 4 waves
+constexpr int kReduceOneWaveP = 8;  // rows reduce_row_wave combines in one memory round trip
 
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_split_kernel(DecodeReduceArgs a) {
@@ -56,6 +59,11 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_split_kernel(
   const int row = blockIdx.x;  // b * H + h
   if (row >= a.S * a.H) return;  // uniform over the workgroup
   const int np = reduce_parts(a, row / a.H);
+  if (np <= kReduceOneWaveP) {  // a short row: one wave, as in decode_reduce_kernel; the
+    if (w == 0)                 // others leave at once and free their slots for other rows
+      reduce_row_wave<D, OUT_BF16>(a.acc, a.m, a.l, a.P, np, a.normalized != 0, (size_t)row, a.out, a.lse);
+    return;  // uniform over the workgroup: no barrier follows for it
+  }
   // this wave's partitions [p0, p1)
   const int per = (np + kReduceWaves - 1) / kReduceWaves;
   const int p0 = min(np, w * per), p1 = min(np, p0 + per);
