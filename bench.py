@@ -249,6 +249,8 @@ def bench_mla_decode(case, steps, warmup, split):
     kvl = (case.kv_indptr[1:] - case.kv_indptr[:-1])
     max_kv = int(kvl.max().item())
     B, H = case.batch, 16
+    if split is None:
+        split = pkv.mla_decode_default_split(B, max_kv, case.kv_indices.numel(), dev)
     P = -(-max_kv // split)
     parts = (torch.empty((B, H, P, 512), dtype=torch.float32, device=dev),
              torch.empty((B, H, P), dtype=torch.float32, device=dev),
@@ -271,7 +273,7 @@ def bench_mla_decode(case, steps, warmup, split):
         evs[i][1].record()
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in evs)
-    return dict(ms=sum(ms) / len(ms), median_ms=ms[len(ms) // 2])
+    return dict(ms=sum(ms) / len(ms), median_ms=ms[len(ms) // 2], split=split)
 
 
 def cpu_baseline_decode(case, budget_s):
@@ -374,7 +376,7 @@ def main():
     result = {}
     if args.workload == "mla_decode_b64":
         case = inputs.mla_decode_b64()
-        r = bench_mla_decode(case, args.steps, args.warmup, split=1024)
+        r = bench_mla_decode(case, args.steps, args.warmup, split=None)
         kv_b = sum(case.kv_lens()) * (512 + 64) * 2
         gbs = kv_b / (r["ms"] * 1e-3) / 1e9
         result = {
@@ -382,7 +384,7 @@ def main():
             "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": r["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": case.name, "batch": case.batch, "split_tokens": 1024,
+            "config": {"workload": case.name, "batch": case.batch, "split_tokens": r["split"],
                        "kv_bytes_per_step": kv_b},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None},
@@ -482,10 +484,11 @@ def main():
             extra["mla_decode_b64_prefill_kernel"] = {
                 "us": rd["ms"] * 1e3, "kv_GB_s": kv_b / (rd["ms"] * 1e-3) / 1e9,
                 "frac_of_hbm_peak": kv_b / (rd["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, "kernel": "mla_paged_prefill (q_len 1)"}
-            rs = bench_mla_decode(md, 50, 5, split=1024)
+            rs = bench_mla_decode(md, 50, 5, split=None)
             extra["mla_decode_b64"] = {"us": rs["ms"] * 1e3, "kv_GB_s": kv_b / (rs["ms"] * 1e-3) / 1e9,
                                        "frac_of_hbm_peak": kv_b / (rs["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                       "kernel": "mla_paged_decode (split-K, 1024-key splits, both launches)"}
+                                       "split_tokens": rs["split"],
+                                       "kernel": "mla_paged_decode (split-K, default splits, both launches)"}
         except NotImplementedError as e:
             extra["mla_prefill_b8"] = {"error": str(e)}
         result["extra"] = extra

@@ -31,7 +31,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["paged_decode_partial", "paged_decode_reduce", "paged_decode_split_partial",
+__all__ = ["mla_decode_default_split", "paged_decode_partial", "paged_decode_reduce", "paged_decode_split_partial",
            "paged_decode_split_reduce", "paged_decode", "paged_decode_into", "paged_attention_v2",
            "mla_paged_prefill", "mla_paged_prefill_pages", "mla_paged_decode", "read_bandwidth", "lib", "library_path", "PkvError", "TOKEN_MAJOR",
            "XPACKED", "num_partitions"]
@@ -505,17 +505,32 @@ def mla_paged_prefill_pages(q_nope, q_pe, ckv_cache, kpe_cache, qo_indptr, kv_in
     _check(st, "mla_paged_prefill_pages")
 
 
+def mla_decode_default_split(batch: int, max_kv_len: int, total_keys: int, device=None) -> int:
+    """Keys per split for an MLA decode such that every non-empty (split, sequence) item runs
+    in one round of one workgroup per compute unit (CU). Two bounds each guarantee that:
+    max_kv_len / (CUs // batch) keeps the batch x splits grid within the CUs, and, for
+    batches of at most 256 (whose non-empty items the kernel packs onto the lowest workgroup
+    ids), total_keys / (CUs - batch) keeps the items, at most total / split + batch, within
+    them. The shorter is taken, rounded up to 16 keys. Shorter splits than that lose: each
+    split costs a 32 KB partial row and an LDS merge, and a second round waits for the first."""
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    B = max(1, int(batch))
+    per_seq = max(1, cus // B)
+    split = -(-max(1, int(max_kv_len)) // per_seq)
+    if B <= 256 and cus > B and total_keys > 0:
+        split = min(split, -(-int(total_keys) // (cus - B)))
+    return max(16, -(-split // 16) * 16)
+
+
 def mla_paged_decode(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.Tensor, kpe_cache: torch.Tensor,
                      kv_indptr: torch.Tensor, kv_indices: torch.Tensor, sm_scale: float,
                      split_tokens: Optional[int] = None, max_kv_len: Optional[int] = None,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                      partials: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
     """MLA decode, one new token per sequence: q_nope [B, 16, 512], q_pe [B, 16, 64].
-    Returns (out [B, 16, 512] bf16, lse [B, 16] base 2). ``split_tokens`` keys per split;
-    by default the longest sequence is cut into as many splits as keep every (split,
-    sequence) item in one round of one workgroup per compute unit (measured fastest: each
-    split costs a 32 KB partial row and an LDS merge, and a second round waits for the
-    first). ``max_kv_len`` defaults to the
+    Returns (out [B, 16, 512] bf16, lse [B, 16] base 2). ``split_tokens`` keys per split,
+    by default ``mla_decode_default_split`` (the shortest split that keeps every item in one
+    round of one workgroup per compute unit). ``max_kv_len`` defaults to the
     largest kv_indptr step (one device-to-host read); ``partials`` (acc, m, l) scratch is
     allocated when not given."""
     for n, t in (("q_nope", q_nope), ("q_pe", q_pe), ("ckv_cache", ckv_cache), ("kpe_cache", kpe_cache)):
@@ -531,9 +546,7 @@ def mla_paged_decode(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.
         max_kv_len = int((kv_indptr[1:] - kv_indptr[:-1]).max().item()) if B > 0 else 0
     dev = q_nope.device
     if split_tokens is None:
-        cus = torch.cuda.get_device_properties(dev).multi_processor_count
-        per_seq = max(1, cus // max(1, B))
-        split_tokens = max(16, -(-max(1, -(-int(max_kv_len) // per_seq)) // 16) * 16)
+        split_tokens = mla_decode_default_split(B, int(max_kv_len), kv_indices.numel(), dev)
     P = max(1, -(-int(max_kv_len) // int(split_tokens)))
     if partials is None:
         partials = (torch.empty((B, H, P, Dc), dtype=torch.float32, device=dev),

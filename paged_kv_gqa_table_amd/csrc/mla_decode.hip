@@ -11,7 +11,8 @@
 //
 // gfx950 design (the operand layouts of the matrix-core GQA decode kernel, the 16 heads
 // being one MFMA tile):
-//  * One workgroup of 4 waves per (split, batch) item, split-major; a wave takes groups of
+//  * One workgroup of 4 waves per (split, batch) item, the non-empty items on the lowest
+//    workgroup ids (mla_item); a wave takes groups of
 //    16 keys round-robin. Token ids are loaded two groups ahead, one per lane (lane l holds
 //    the id of key l % 16 of the group).
 //  * S^T = K Q^T: 18 k-steps of v_mfma_f32_16x16x32_bf16 (16 over ckv, 2 over kpe). A is
@@ -76,10 +77,75 @@ PKV_DEVICE void mla_batch_range(const MlaDecodeArgs& a, int b, int& kv0, int& le
   len = uniform(len);
 }
 
+constexpr int kMdDenseMaxB = 64 * kMdW;  // batches the in-workgroup item scan covers (one per thread)
+
+// (batch, split) of this workgroup. The grid has one workgroup per pair (batch x gp, gp =
+// ceil(max_kv_len / split) splits, so gridDim.x / batch = gp). With
+// at most 256 batches the non-empty pairs come first, batch-major (workgroup i < N takes
+// the i-th non-empty item), then the empty ones in the same order: the items take the
+// lowest workgroup ids, which the dispatcher deals round-robin over the XCDs, so no XCD
+// gets more items than its share. (Split-major, an XCD gets every split of the batches
+// b = x mod 8, and a batch with more splits than the others pushes some XCD into a
+// second round.) Larger batches: split-major.
+PKV_DEVICE void mla_item(const MlaDecodeArgs& a, int& b, int& p) {
+  const int bid = (int)blockIdx.x;
+  if (a.batch > kMdDenseMaxB) {
+    p = bid / a.batch;
+    b = bid - p * a.batch;
+    return;
+  }
+  __shared__ int s_pre[kMdDenseMaxB];  // inclusive prefix sum of the batches' non-empty splits
+  __shared__ int s_hit[2];
+  const int t = threadIdx.x;
+  const int gp = (int)(gridDim.x / (unsigned)a.batch);
+  int n = 0;  // non-empty splits of batch t in the grid: min(ceil(len / split), gp), len as in mla_batch_range
+  if (t < a.batch) {
+    int k0 = a.kv_indptr[t], k1 = a.kv_indptr[t + 1];
+    k0 = k0 < 0 ? 0 : (k0 > a.num_kv_indices ? a.num_kv_indices : k0);
+    k1 = k1 < k0 ? k0 : (k1 > a.num_kv_indices ? a.num_kv_indices : k1);
+    int len = k1 - k0;
+    len = len > a.len_cap ? a.len_cap : len;
+    n = (len + a.split - 1) / a.split;
+    n = n > gp ? gp : n;
+  }
+  s_pre[t] = n;
+  if (t == 0) s_hit[0] = -1;
+  __syncthreads();
+  for (int off = 1; off < kMdDenseMaxB; off <<= 1) {
+    const int v = t >= off ? s_pre[t - off] : 0;
+    __syncthreads();
+    s_pre[t] += v;
+    __syncthreads();
+  }
+  const int incl = s_pre[t], excl = incl - n;
+  const int total = s_pre[kMdDenseMaxB - 1];
+  if (t < a.batch) {
+    if (bid < total) {
+      if (excl <= bid && bid < incl) {
+        s_hit[0] = t;
+        s_hit[1] = bid - excl;
+      }
+    } else {
+      const int j = bid - total;            // j-th empty pair
+      const int e0 = t * gp - excl;        // empty pairs of the batches before t
+      if (e0 <= j && j < e0 + (gp - n)) {  // batch t's splits n .. gp-1
+        s_hit[0] = t;
+        s_hit[1] = n + (j - e0);
+      }
+    }
+  }
+  __syncthreads();
+  b = s_hit[0];
+  p = s_hit[1];
+}
+
 __global__ __launch_bounds__(64 * kMdW) void mla_decode_partial_kernel(MlaDecodeArgs a) {
   __shared__ MlaDecSmem sm;
-  const int p = uniform((int)(blockIdx.x / a.batch));  // split-major
-  const int b = uniform((int)(blockIdx.x - (unsigned)p * a.batch));
+  int b, p;
+  mla_item(a, b, p);
+  if (b < 0) return;  // uniform; not reached when the grid is batch x P pairs
+  b = uniform(b);
+  p = uniform(p);
   const int lane = threadIdx.x & 63;
   const int w = uniform((int)(threadIdx.x >> 6));
   const int g = lane >> 4;

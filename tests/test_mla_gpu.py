@@ -214,10 +214,35 @@ def test_mla_split_decode_edges(split):
     assert np.all(o[0] == 0.0) and np.all(np.isneginf(l[0])), "empty batch"
 
 
-def test_mla_split_decode_b64():
+@pytest.mark.parametrize("n_batch,split", [(300, 64), (256, 48), (257, 48)])
+def test_mla_split_decode_batch_mapping(n_batch, split):
+    """Up to 256 batches the kernel packs the non-empty (split, batch) items onto the lowest
+    workgroup ids after an in-workgroup scan of the lengths; past 256 it maps workgroups
+    split-major. Both against the oracle, with empty batches and ragged lengths."""
+    rng = np.random.default_rng(n_batch + split)
+    kv = rng.integers(0, 300, n_batch)
+    kv[::9] = 0
+    kv[1::17] = split  # exactly one split
+    case = inputs.make_mla(np.ones(n_batch, dtype=np.int64), np.maximum(kv - 1, 0), seed=n_batch, extra_pages=3)
+    kvp = case.kv_indptr.clone()
+    kvp[1:] = torch.cumsum(torch.tensor(kv, dtype=torch.int32), 0)
+    idx = case.kv_indices[: int(kvp[-1])]
+    case = inputs.MlaCase(name="mla_decode_batches", q_nope=case.q_nope, q_pe=case.q_pe, ckv_cache=case.ckv_cache,
+                          kpe_cache=case.kpe_cache, qo_indptr=case.qo_indptr, kv_indptr=kvp, kv_indices=idx,
+                          sm_scale=case.sm_scale)
+    say(f"mla split decode: batches={n_batch} split={split}")
+    o, l = run_decode_gpu(case, split)
+    ro, rl = run_oracle(case)
+    check(o, l, ro, rl, f"batches={n_batch} split={split}")
+    empty = np.flatnonzero(kv == 0)
+    assert np.all(o[empty] == 0.0) and np.all(np.isneginf(l[empty])), "empty batches"
+
+
+@pytest.mark.parametrize("split", [256, None])
+def test_mla_split_decode_b64(split):
     case = inputs.mla_decode_b64()
-    say(f"mla split decode b64: pages={case.num_pages}")
-    o, l = run_decode_gpu(case, 256)
+    say(f"mla split decode b64: pages={case.num_pages} split={split}")
+    o, l = run_decode_gpu(case, split)
     ro, rl = run_oracle(case)
     e, le = check(o, l, ro, rl, "split decode b64")
     o2, l2 = run_gpu(case)  # the prefill kernel with q_len 1: the same values within bf16
