@@ -250,7 +250,7 @@ def bench_mla_decode(case, steps, warmup, split):
     max_kv = int(kvl.max().item())
     B, H = case.batch, 16
     if split is None:
-        split = pkv.mla_decode_default_split(B, max_kv, case.kv_indices.numel(), dev)
+        split = pkv.mla_decode_default_split(B, max_kv, case.kv_indices.numel(), dev, kv_lens=kvl.tolist())
     P = -(-max_kv // split)
     parts = (torch.empty((B, H, P, 512), dtype=torch.float32, device=dev),
              torch.empty((B, H, P), dtype=torch.float32, device=dev),

@@ -27,7 +27,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
-from typing import Optional, Tuple
+from typing import Optional, Sequence, Tuple
 
 import torch
 
@@ -505,13 +505,16 @@ def mla_paged_prefill_pages(q_nope, q_pe, ckv_cache, kpe_cache, qo_indptr, kv_in
     _check(st, "mla_paged_prefill_pages")
 
 
-def mla_decode_default_split(batch: int, max_kv_len: int, total_keys: int, device=None) -> int:
+def mla_decode_default_split(batch: int, max_kv_len: int, total_keys: int, device=None,
+                             kv_lens: Optional[Sequence[int]] = None) -> int:
     """Keys per split for an MLA decode such that every non-empty (split, sequence) item runs
     in one round of one workgroup per compute unit (CU). Two bounds each guarantee that:
     max_kv_len / (CUs // batch) keeps the batch x splits grid within the CUs, and, for
     batches of at most 256 (whose non-empty items the kernel packs onto the lowest workgroup
     ids), total_keys / (CUs - batch) keeps the items, at most total / split + batch, within
-    them. The shorter is taken, rounded up to 16 keys. Shorter splits than that lose: each
+    them. With the lengths on the host (``kv_lens``) and at most 256 batches, the split is
+    instead the shortest multiple of 16 whose items, sum of ceil(len / split), fit the CUs.
+    Otherwise the shorter bound, rounded up to 16 keys. Shorter splits than that lose: each
     split costs a 32 KB partial row and an LDS merge, and a second round waits for the first."""
     cus = torch.cuda.get_device_properties(device).multi_processor_count
     B = max(1, int(batch))
@@ -519,7 +522,21 @@ def mla_decode_default_split(batch: int, max_kv_len: int, total_keys: int, devic
     split = -(-max(1, int(max_kv_len)) // per_seq)
     if B <= 256 and cus > B and total_keys > 0:
         split = min(split, -(-int(total_keys) // (cus - B)))
-    return max(16, -(-split // 16) * 16)
+    split = max(16, -(-split // 16) * 16)
+    if kv_lens is not None and B <= 256 and len(kv_lens) > 0:
+        lens = [max(0, int(x)) for x in kv_lens]
+        def items(sp):
+            return sum(-(-x // sp) for x in lens)
+        lo, hi = 1, split // 16  # in units of 16 keys; `split` itself fits (both bounds above)
+        if items(hi * 16) <= cus:
+            while lo < hi:  # items(s) does not grow with s
+                mid = (lo + hi) // 2
+                if items(mid * 16) <= cus:
+                    hi = mid
+                else:
+                    lo = mid + 1
+            split = hi * 16
+    return split
 
 
 def mla_paged_decode(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.Tensor, kpe_cache: torch.Tensor,
@@ -530,7 +547,8 @@ def mla_paged_decode(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.
     """MLA decode, one new token per sequence: q_nope [B, 16, 512], q_pe [B, 16, 64].
     Returns (out [B, 16, 512] bf16, lse [B, 16] base 2). ``split_tokens`` keys per split,
     by default ``mla_decode_default_split`` (the shortest split that keeps every item in one
-    round of one workgroup per compute unit). ``max_kv_len`` defaults to the
+    round of one workgroup per compute unit; up to 256 batches it reads kv_indptr to the host
+    for that). ``max_kv_len`` defaults to the
     largest kv_indptr step (one device-to-host read); ``partials`` (acc, m, l) scratch is
     allocated when not given."""
     for n, t in (("q_nope", q_nope), ("q_pe", q_pe), ("ckv_cache", ckv_cache), ("kpe_cache", kpe_cache)):
@@ -542,11 +560,17 @@ def mla_paged_decode(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.
     num_pages, page_size, _ = ckv_cache.shape
     if kv_indptr.numel() != B + 1 or q_pe.shape[:2] != q_nope.shape[:2]:
         raise ValueError("q_nope / q_pe must be [batch, heads, dim] and kv_indptr [batch + 1]")
+    host_lens = None
+    if split_tokens is None and 0 < B <= 256:  # one device-to-host read of the offsets
+        ptr = kv_indptr.cpu()
+        host_lens = (ptr[1:] - ptr[:-1]).tolist()
+        if max_kv_len is None:
+            max_kv_len = max(0, max(host_lens))
     if max_kv_len is None:
         max_kv_len = int((kv_indptr[1:] - kv_indptr[:-1]).max().item()) if B > 0 else 0
     dev = q_nope.device
     if split_tokens is None:
-        split_tokens = mla_decode_default_split(B, int(max_kv_len), kv_indices.numel(), dev)
+        split_tokens = mla_decode_default_split(B, int(max_kv_len), kv_indices.numel(), dev, kv_lens=host_lens)
     P = max(1, -(-int(max_kv_len) // int(split_tokens)))
     if partials is None:
         partials = (torch.empty((B, H, P, Dc), dtype=torch.float32, device=dev),
