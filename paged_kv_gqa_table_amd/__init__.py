@@ -506,7 +506,7 @@ def mla_paged_prefill_pages(q_nope, q_pe, ckv_cache, kpe_cache, qo_indptr, kv_in
 
 
 def mla_decode_default_split(batch: int, max_kv_len: int, total_keys: int, device=None,
-                             kv_lens: Optional[Sequence[int]] = None) -> int:
+                             kv_lens: Optional[Sequence[int]] = None, cus: Optional[int] = None) -> int:
     """Keys per split for an MLA decode such that every non-empty (split, sequence) item runs
     in one round of one workgroup per compute unit (CU). Two bounds each guarantee that:
     max_kv_len / (CUs // batch) keeps the batch x splits grid within the CUs, and, for
@@ -515,8 +515,11 @@ def mla_decode_default_split(batch: int, max_kv_len: int, total_keys: int, devic
     them. With the lengths on the host (``kv_lens``) and at most 256 batches, the split is
     instead the shortest multiple of 16 whose items, sum of ceil(len / split), fit the CUs.
     Otherwise the shorter bound, rounded up to 16 keys. Shorter splits than that lose: each
-    split costs a 32 KB partial row and an LDS merge, and a second round waits for the first."""
-    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    split costs a 32 KB partial row and an LDS merge, and a second round waits for the first.
+    ``cus`` is the compute-unit count (default: that of ``device``)."""
+    if cus is None:
+        cus = torch.cuda.get_device_properties(device).multi_processor_count
+    cus = int(cus)
     B = max(1, int(batch))
     per_seq = max(1, cus // B)
     split = -(-max(1, int(max_kv_len)) // per_seq)
@@ -546,11 +549,12 @@ def mla_paged_decode(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.
                      partials: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
     """MLA decode, one new token per sequence: q_nope [B, 16, 512], q_pe [B, 16, 64].
     Returns (out [B, 16, 512] bf16, lse [B, 16] base 2). ``split_tokens`` keys per split,
-    by default ``mla_decode_default_split`` (the shortest split that keeps every item in one
-    round of one workgroup per compute unit; up to 256 batches it reads kv_indptr to the host
-    for that). ``max_kv_len`` defaults to the
-    largest kv_indptr step (one device-to-host read); ``partials`` (acc, m, l) scratch is
-    allocated when not given."""
+    by default ``mla_decode_default_split``. Host reads: with both ``split_tokens`` and
+    ``max_kv_len`` given nothing is read back (the call stays asynchronous, as a decode loop
+    or a captured graph needs: compute the split once and pass it); with ``max_kv_len``
+    given and no split, the split comes from the length bounds alone, again without a read;
+    with neither, kv_indptr is read to the host once (up to 256 batches the split then fits
+    the exact lengths). ``partials`` (acc, m, l) scratch is allocated when not given."""
     for n, t in (("q_nope", q_nope), ("q_pe", q_pe), ("ckv_cache", ckv_cache), ("kpe_cache", kpe_cache)):
         _dev(n, t, torch.bfloat16, 3)
     _dev("kv_indptr", kv_indptr, torch.int32, 1)
@@ -561,13 +565,12 @@ def mla_paged_decode(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.
     if kv_indptr.numel() != B + 1 or q_pe.shape[:2] != q_nope.shape[:2]:
         raise ValueError("q_nope / q_pe must be [batch, heads, dim] and kv_indptr [batch + 1]")
     host_lens = None
-    if split_tokens is None and 0 < B <= 256:  # one device-to-host read of the offsets
+    if max_kv_len is None and B > 0:  # one device-to-host read of the offsets
         ptr = kv_indptr.cpu()
         host_lens = (ptr[1:] - ptr[:-1]).tolist()
-        if max_kv_len is None:
-            max_kv_len = max(0, max(host_lens))
+        max_kv_len = max(0, max(host_lens))
     if max_kv_len is None:
-        max_kv_len = int((kv_indptr[1:] - kv_indptr[:-1]).max().item()) if B > 0 else 0
+        max_kv_len = 0
     dev = q_nope.device
     if split_tokens is None:
         split_tokens = mla_decode_default_split(B, int(max_kv_len), kv_indices.numel(), dev, kv_lens=host_lens)

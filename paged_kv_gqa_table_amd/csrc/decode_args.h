@@ -13,8 +13,9 @@ struct DecodePartialArgs {
   const int32_t* bt;      // [S, mb]
   const int32_t* lens;    // [S]
   int mb;                 // max_blocks_per_seq
-  int len_cap;            // lengths are clamped to this many tokens: min(mb * 16, P * ps), or
-                          // mb * 16 under NUM_SPLITS, so no partition index reaches P
+  int len_cap;            // lengths are clamped to this many tokens: min(mb * 16, launched
+                          // partitions * ps), or mb * 16 under NUM_SPLITS, so no partition
+                          // index reaches the launched grid (or P)
   int S, H, KVH, D, NB;   // sizes; NB = pool blocks
   float scale_log2;       // scale * log2(e): scores are kept in base-2 units inside
   int ps;                 // partition size in tokens (multiple of 16); unused when nsplit > 0

@@ -47,7 +47,7 @@ struct MlaDecodeArgs {
   int batch, num_pages, num_kv_indices;
   int split;                  // tokens per split (multiple of 16)
   int P;                      // max_num_splits: stride of the partial arrays
-  int len_cap;                // lengths are clamped to P * split tokens
+  int len_cap;                // lengths are clamped to (launched splits) * split tokens
   float sm_scale_log2;        // sm_scale * log2(e)
   float* acc;                 // [batch, 16, P, 512]
   float* m;                   // [batch, 16, P] natural log

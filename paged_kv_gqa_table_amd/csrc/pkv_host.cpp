@@ -180,7 +180,9 @@ int decode_phase1(const char* who, const void* query, int dtype, const void* key
     a.nsplit = mode.num_splits;
   }
   a.ppp = a.ps / block_size;
-  a.len_cap = (int)std::min<int64_t>(table_tokens, a.nsplit > 0 ? table_tokens : (int64_t)max_num_partitions * a.ps);
+  // lengths are cut to the partitions this launch covers (a length past max_seq_len breaks
+  // the contract; it must still not push a partition index past the launched grid)
+  a.len_cap = (int)std::min<int64_t>(table_tokens, a.nsplit > 0 ? table_tokens : (int64_t)grid_parts * a.ps);
   a.normalize = mode.normalize;
   a.alibi = mode.alibi;
   a.kv_fp8 = mode.kv_fp8;
@@ -430,7 +432,9 @@ extern "C" int mla_paged_decode(const void* q_nope, const void* q_pe, const void
   a.kv_indptr = kv_indptr; a.kv_indices = kv_indices;
   a.batch = batch; a.num_pages = num_pages; a.num_kv_indices = num_kv_indices;
   a.split = split_tokens; a.P = max_num_splits;
-  a.len_cap = (int)std::min<int64_t>((int64_t)max_num_splits * split_tokens, INT32_MAX);
+  // lengths are cut to the splits phase 1 launches, so the combine never reads a partial
+  // row that phase 1 did not write, even when a kv_len breaks the max_kv_len contract
+  a.len_cap = (int)std::min<int64_t>((int64_t)(grid_parts > 0 ? grid_parts : 1) * split_tokens, INT32_MAX);
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
   a.acc = partial_acc; a.m = partial_m; a.l = partial_l; a.out = out; a.lse = lse;
   return hip_status(pkv::launch_mla_decode(a, (int)grid_parts, reinterpret_cast<hipStream_t>(stream)),

@@ -150,11 +150,12 @@ def test_paged_attention_v2(dtype, D, H, KVH):
     check_out(_np(out), ref["out"], dtype, "v2 out")
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("workload", ["llama_gqa4", "wide_gqa6", "skewed_gqa8"])
 def test_one_launch_full_size(workload):
     """The benchmarked workloads through the one-launch entry point, in the launch
-    configuration the bench times: against the two-phase result everywhere and the oracle
-    on a sample of sequences."""
+    configuration the bench times: against the two-phase result and the oracle on every
+    sequence."""
     case = inputs.decode_workload(workload)
     say(f"one launch full size: {workload}")
     dev = to_dev(case)
@@ -164,11 +165,10 @@ def test_one_launch_full_size(workload):
     out, lse, counters = one_launch(case, dev, ps, P)
     assert int(counters.abs().sum().item()) == 0
     check_out(out, two["out"], case.dtype, "one launch vs two phases")
-    rng = np.random.default_rng(1)
-    seqs = sorted({0, case.num_seqs - 1, *rng.choice(case.num_seqs, 3, replace=False).tolist()})
-    ref = oracle_subset(case, seqs)
-    check_out(out[seqs], ref["out"], case.dtype, "one launch out (sample)")
-    check_lse(lse[seqs], ref["lse"], case.dtype, "one launch lse (sample)")
+    for b in range(case.num_seqs):
+        ref = oracle_subset(case, [b])
+        check_out(out[b:b + 1], ref["out"], case.dtype, f"one launch out b={b}")
+        check_lse(lse[b:b + 1], ref["lse"], case.dtype, f"one launch lse b={b}")
 
 
 def test_lengths_past_max_seq_len_stay_in_bounds():
@@ -275,3 +275,70 @@ def test_python_paged_decode_defaults():
         torch.cuda.synchronize()
         check_out(_np(out), ref["out"], "bf16", f"paged_decode {kw}")
         check_lse(_np(lse), ref["lse"], "bf16", f"paged_decode {kw}")
+
+
+@pytest.mark.timeout(900)
+def test_llama_gqa4_fp8_full():
+    """The llama_gqa4 batch with a float8 e4m3 cache through the PagedAttention V2 entry point,
+    as the bench times it (x-packed, x = 16, unit scales): every sequence's normalized
+    partials and output against the oracle on the same float8 pools."""
+    case = inputs.llama_gqa4()
+    k8, v8 = inputs.fp8_xpacked_pools(case)
+    S, H, D, KVH = case.num_seqs, case.num_heads, case.head_dim, case.num_kv_heads
+    P = case.num_partitions(512)
+    dev = to_dev(case)
+    say(f"llama_gqa4 float8 cache, full size: S={S} P={P}")
+    tmp = torch.full((S, H, P, D), float("nan"), dtype=torch.float32, device="cuda")
+    es = torch.full((S, H, P), float("nan"), dtype=torch.float32, device="cuda")
+    ml = torch.full((S, H, P), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full((S, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pkv.paged_attention_v2(out, es, ml, tmp, dev["q"], k8.to("cuda"), v8.to("cuda"), KVH, case.scale, dev["bt"],
+                           dev["lens"], case.block_size, case.max_seq_len, kv_cache_dtype="fp8", k_scale=1.0,
+                           v_scale=1.0)
+    torch.cuda.synchronize()
+    tmp, es, ml, out = _np(tmp), _np(es), _np(ml), _np(out)
+    lens = case.seq_lens.numpy()
+    for b in range(S):
+        idx = torch.tensor([b])
+        args = (case.query[idx], k8, v8, "xpacked", case.block_tables[idx], case.seq_lens[idx], case.scale, KVH,
+                case.block_size)
+        r = oracle.decode_partials(*args, 512, P, normalized=True)
+        _check_ranged_partials(tmp[b:b + 1], ml[b:b + 1], es[b:b + 1], r, lens[b:b + 1],
+                               lambda n: oracle.partition_ranges(n, case.block_size, 512), "bf16", f"fp8 b={b}",
+                               normalized=True)
+        ref, _ = oracle.decode(*args)
+        check_out(out[b:b + 1], ref, "bf16", f"fp8 out b={b}")
+    say("  every sequence matches the oracle")
+
+
+@pytest.mark.timeout(900)
+def test_llama_gqa4_num_splits_full():
+    """The llama_gqa4 batch under the NUM_SPLITS policy (8 page-aligned splits per sequence),
+    both phases: every sequence's split partials, output and LSE against the oracle."""
+    case = inputs.llama_gqa4()
+    dev = to_dev(case)
+    S, H, D, KVH, ns = case.num_seqs, case.num_heads, case.head_dim, case.num_kv_heads, 8
+    say(f"llama_gqa4 NUM_SPLITS={ns}, full size")
+    acc = torch.full((S, H, ns, D), float("nan"), dtype=torch.float32, device="cuda")
+    m = torch.full((S, H, ns), float("nan"), dtype=torch.float32, device="cuda")
+    l = torch.full((S, H, ns), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full((S, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((S, H), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.paged_decode_split_partial(dev["q"], dev["k"], dev["v"], dev["bt"], dev["lens"], case.scale, KVH,
+                                   case.max_seq_len, acc, m, l, layout=case.layout)
+    pkv.paged_decode_split_reduce(acc, m, l, dev["lens"], case.block_size, out, lse)
+    torch.cuda.synchronize()
+    acc, m, l, out, lse = _np(acc), _np(m), _np(l), _np(out), _np(lse)
+    lens = case.seq_lens.numpy()
+    for b in range(S):
+        idx = torch.tensor([b])
+        args = (case.query[idx], case.key_cache, case.value_cache, case.layout, case.block_tables[idx],
+                case.seq_lens[idx], case.scale, KVH, case.block_size)
+        r = oracle.decode_partials(*args, 0, ns, num_splits=ns)
+        _check_ranged_partials(acc[b:b + 1], m[b:b + 1], l[b:b + 1], r, lens[b:b + 1],
+                               lambda n: oracle.partition_ranges(n, case.block_size, 0, ns), "bf16",
+                               f"NS={ns} b={b}")
+        ro, rl = oracle.decode(*args)
+        check_out(out[b:b + 1], ro, "bf16", f"NS={ns} out b={b}")
+        check_lse(lse[b:b + 1], rl, "bf16", f"NS={ns} b={b}")
+    say("  every sequence matches the oracle")

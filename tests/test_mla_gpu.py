@@ -43,7 +43,8 @@ def check(o, l, ro, rl, what):
     bad = err > ABS + REL * np.abs(ro)
     assert not bad.any(), f"{what}: {bad.sum()} out of tolerance, max abs {err.max()}"
     both = np.isneginf(l) & np.isneginf(rl)
-    lerr = np.where(both, 0.0, np.abs(l - rl))
+    with np.errstate(invalid="ignore"):  # -inf - -inf where both are -inf: masked out here
+        lerr = np.where(both, 0.0, np.abs(l - rl))
     assert np.all(np.isfinite(lerr)) and lerr.max(initial=0) <= LSE_TOL, f"{what}: lse err {lerr.max()}"
     return float(err.max(initial=0)), float(lerr.max(initial=0))
 
