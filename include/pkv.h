@@ -90,7 +90,8 @@ typedef enum {
  *   key_cache,
  *   value_cache   page pools in `layout`, element type `dtype`, num_blocks blocks
  *   block_tables  [num_seqs, max_blocks_per_seq] int32; entries past
- *                 ceil(len_b / block_size) are never read (may be -1)
+ *                 ceil(len_b / block_size) may hold anything (e.g. -1): they can be
+ *                 loaded (within the row) but never select a page that is read
  *   seq_lens      [num_seqs] int32, 0 <= len_b <= max_seq_len
  *   partial_acc   [num_seqs, num_heads, max_num_partitions, head_dim] float32
  *   partial_m,

@@ -70,6 +70,9 @@ hipError_t launch_decode_mfma_bf16_tm(const DecodePartialArgs& a, int G, int gri
 hipError_t launch_decode_mfma_bf16_xp(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeReduceArgs& a, bool out_bf16, hipStream_t s);
 
+// Sets the calling thread's pkv_last_error() message (printf format) and returns `code`.
+int set_last_error(int code, const char* fmt, ...);
+
 // Workgroup cap of the dense decode launches on the current device (host side).
 int dense_grid_cap();
 // Workgroups of `kernel` (block_threads threads, dyn_lds bytes of dynamic LDS) that the

@@ -30,6 +30,24 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
+}  // namespace
+
+namespace pkv {
+// Records the calling thread's message for pkv_last_error() and returns `code`; shared with
+// the entry points defined in other translation units.
+int set_last_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+}  // namespace pkv
+
+namespace {
+
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return PKV_OK;
   if (e == hipErrorNotSupported) return fail(PKV_EUNSUPPORTED, "%s: no compiled kernel for these arguments", what);
