@@ -14,6 +14,8 @@
  *   mla_paged_prefill     MLA causal paged prefill (page_size 1), base-2 LSE
  *   mla_paged_prefill_pages  the same over pages of several tokens
  *   mla_paged_decode      MLA decode (one new token per sequence), split-K
+ *   paged_decode_static   paged_decode for callers that cannot allocate: the partials
+ *                         live in a static device array the library holds
  * and a measurement helper, pkv_read_bandwidth (a plain streaming read of a buffer),
  * that no part of the attention path uses.
  *
@@ -341,6 +343,40 @@ int mla_paged_decode(const void* q_nope, const void* q_pe,
                      int split_tokens, int max_num_splits,
                      float* partial_acc, float* partial_m, float* partial_l,
                      void* out, float* lse, void* stream);
+
+/*
+ * paged_decode_static -- paged_decode without any allocation, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Not a computation of its own: the same two phases as
+ * paged_decode_partial + paged_decode_reduce (or their _split_ forms when num_splits > 0),
+ * with the partials kept in a scratch array that the library holds in device memory.
+ *
+ * Arguments are those of paged_decode without the partial arrays and counters:
+ * out[b,h,:] (element type `dtype`, RNE) and lse[b,h] (natural log; lse may be NULL).
+ * The partitions are ceil(max_seq_len / partition_size) fixed ones, or num_splits splits
+ * under the NUM_SPLITS policy; with a single fixed partition the single-pass kernel runs
+ * and no scratch is touched.
+ *
+ * Scratch: one static array of PKV_STATIC_SCRATCH_BYTES per GPU, held until the process
+ * ends. The partials need num_seqs * num_heads * partitions * (head_dim + 2) floats (each
+ * of the three arrays rounded up to 256 bytes); larger calls are refused with
+ * PKV_EUNSUPPORTED before anything is launched. Every call on one GPU uses that GPU's
+ * array: calls that overlap in time on the same GPU (other streams, other host threads)
+ * race on it and must be serialised by the caller. Phase 1 writes every partial row or
+ * sentinel phase 2 reads, so no call depends on what an earlier one left there.
+ * The function calls no allocating routine. The first call on each device looks up the
+ * array's device address (hipGetSymbolAddress) and keeps it.
+ * PKV_EINVAL / PKV_EUNSUPPORTED: as paged_decode_partial; NULL out; scratch too small.
+ */
+#define PKV_STATIC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int paged_decode_static(const void* query, int dtype,
+                        const void* key_cache, const void* value_cache, int layout,
+                        const int32_t* block_tables, int max_blocks_per_seq,
+                        const int32_t* seq_lens,
+                        int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                        int block_size, int num_blocks, float scale,
+                        int partition_size, int num_splits, int max_seq_len,
+                        void* out, float* lse, void* stream);
 
 /* Measurement helper, not part of the attention path: reads `bytes` bytes of device memory
  * at `buf` once, as a plain streaming read (16-byte loads, grid-stride over the buffer), on

@@ -32,7 +32,8 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 __all__ = ["mla_decode_default_split", "paged_decode_partial", "paged_decode_reduce", "paged_decode_split_partial",
-           "paged_decode_split_reduce", "paged_decode", "paged_decode_into", "paged_attention_v2",
+           "paged_decode_split_reduce", "paged_decode", "paged_decode_into", "paged_decode_static",
+           "paged_attention_v2",
            "mla_paged_prefill", "mla_paged_prefill_pages", "mla_paged_decode", "read_bandwidth", "lib", "library_path", "PkvError", "TOKEN_MAJOR",
            "XPACKED", "num_partitions"]
 
@@ -92,6 +93,9 @@ def lib() -> ctypes.CDLL:
     L.mla_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                    vp, vp, vp, vp, vp, vp]
     L.mla_paged_decode.restype = i32
+    L.paged_decode_static.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                                      i32, i32, vp, vp, vp]
+    L.paged_decode_static.restype = i32
     L.pkv_read_bandwidth.argtypes = [vp, ctypes.c_size_t, vp, vp]
     L.pkv_read_bandwidth.restype = i32
     L.pkv_last_error.argtypes = []
@@ -306,6 +310,31 @@ def paged_decode_into(query: torch.Tensor, key_cache: torch.Tensor, value_cache:
         float(scale), int(partition_size), int(num_splits), P, int(max_seq_len), _ptr(partial_acc),
         _ptr(partial_m), _ptr(partial_l), _ptr(counters), _ptr(out), _ptr(lse), _stream(query.device))
     _check(st, "paged_decode")
+
+
+def paged_decode_static(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                        block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float, num_kv_heads: int,
+                        max_seq_len: int, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                        partition_size: int = 512, num_splits: int = 0, layout: str = TOKEN_MAJOR) -> None:
+    """The C ``paged_decode_static`` into caller buffers (asynchronous): the decode with its
+    partials in the library's static device scratch, so nothing is allocated (neither here
+    nor in the library) and nothing is read back to the host. Calls that overlap in time on
+    one GPU race on that scratch."""
+    S, H, D, nb, bs = _check_decode_inputs(query, key_cache, value_cache, block_tables, seq_lens,
+                                           num_kv_heads, layout)
+    _dev("out", out, query.dtype, 3)
+    if tuple(out.shape) != (S, H, D):
+        raise ValueError("out must be [S, H, D]")
+    if lse is not None:
+        _dev("lse", lse, torch.float32, 2)
+        if tuple(lse.shape) != (S, H):
+            raise ValueError("lse must be [S, H]")
+    st = lib().paged_decode_static(
+        _ptr(query), _DTYPE[query.dtype], _ptr(key_cache), _ptr(value_cache), _LAYOUT[layout],
+        _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, H, num_kv_heads, D, bs, nb,
+        float(scale), int(partition_size), int(num_splits), int(max_seq_len), _ptr(out), _ptr(lse),
+        _stream(query.device))
+    _check(st, "paged_decode_static")
 
 
 def paged_decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
