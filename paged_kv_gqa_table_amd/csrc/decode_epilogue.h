@@ -17,6 +17,41 @@
 
 namespace pkv {
 
+// Partial rows handed between workgroups of one launch (the one-launch decode) are written
+// and read with agent-scope relaxed atomics: on gfx950 these carry the sc1 bit, so a store
+// writes through the XCD's own L2 to the point where every XCD sees it and a load does not
+// take a stale copy from its L2. That hands over exactly the rows concerned; an agent-scope
+// fence instead writes back or invalidates the whole L2 of the XCD it runs on.
+template <bool COHERENT>
+PKV_DEVICE float ld_f32(const float* p) {
+  if constexpr (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+template <bool COHERENT>
+PKV_DEVICE void st_f32(float* p, float v) {
+  if constexpr (COHERENT) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+// A lane's VecT share (4, 8, 16 or 32 bytes) of an acc row; 64-bit words when coherent.
+template <bool COHERENT, typename VecT>
+PKV_DEVICE VecT ld_vec(const float* p) {
+  if constexpr (!COHERENT) {
+    return *reinterpret_cast<const VecT*>(p);
+  } else if constexpr (sizeof(VecT) == 4) {
+    VecT v;
+    *reinterpret_cast<float*>(&v) = ld_f32<true>(p);
+    return v;
+  } else {
+    VecT v;
+    uint64_t* w = reinterpret_cast<uint64_t*>(&v);
+    const uint64_t* src = reinterpret_cast<const uint64_t*>(p);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(VecT) / 8); ++i)
+      w[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return v;
+  }
+}
+
 // One wave combines row `row` (= b * H + h) of the partial arrays (stride P partitions)
 // over its first np partitions and writes out[row, :] (and lse[row] when lse is not null).
 // Each lane owns D / 64 contiguous output dims, so every acc row is one coalesced read;
@@ -26,8 +61,9 @@ struct alignas(32) Float8 {
   float4 a, b;
 };
 
-// lse_scale multiplies the written LSE (1 for natural log, 1 / ln 2 for base 2).
-template <int D, bool OUT_BF16>
+// lse_scale multiplies the written LSE (1 for natural log, 1 / ln 2 for base 2). COHERENT:
+// the partials were written by other workgroups of the same launch (see ld_vec).
+template <int D, bool OUT_BF16, bool COHERENT = false>
 PKV_DEVICE void reduce_row_wave(const float* acc, const float* pm, const float* pl, int P, int np,
                                 bool normalized, size_t row, void* out, float* lse, float lse_scale = 1.f) {
   constexpr int DPL = D / 64;  // output dims per lane
@@ -46,25 +82,25 @@ PKV_DEVICE void reduce_row_wave(const float* acc, const float* pm, const float* 
     using VecT = typename std::conditional<
         DPL == 8, Float8,
         typename std::conditional<DPL == 4, float4, typename std::conditional<DPL == 2, float2, float>::type>::type>::type;
-    const float m0 = lane < np ? mrow[lane] : kNegInf;  // partition `lane`
-    const float l0 = lane < np ? lrow[lane] : 0.f;
+    const float m0 = lane < np ? ld_f32<COHERENT>(mrow + lane) : kNegInf;  // partition `lane`
+    const float l0 = lane < np ? ld_f32<COHERENT>(lrow + lane) : 0.f;
     VecT buf[CH];
 #pragma unroll
     for (int u = 0; u < CH; ++u)
-      if (u < np) buf[u] = *reinterpret_cast<const VecT*>(arow + (size_t)u * D);
+      if (u < np) buf[u] = ld_vec<COHERENT, VecT>(arow + (size_t)u * D);
     float mv = m0;
-    for (int i = lane + 64; i < np; i += 64) mv = fmaxf(mv, mrow[i]);  // more than 64 partitions
+    for (int i = lane + 64; i < np; i += 64) mv = fmaxf(mv, ld_f32<COHERENT>(mrow + i));  // more than 64 partitions
     M = uniform(strided_max<1>(mv));
     const float wl = __expf(m0 - M);  // weight of partition `lane` (0 past np)
     const float cl = normalized ? wl * l0 : wl;  // coefficient of acc row `lane`
     float zl = wl * l0;
-    for (int i = lane + 64; i < np; i += 64) zl += __expf(mrow[i] - M) * lrow[i];
+    for (int i = lane + 64; i < np; i += 64) zl += __expf(ld_f32<COHERENT>(mrow + i) - M) * ld_f32<COHERENT>(lrow + i);
     Z = strided_sum<1>(zl);
     for (int c0 = 0; c0 < np; c0 += CH) {
       if (c0 > 0) {
 #pragma unroll
         for (int u = 0; u < CH; ++u)
-          if (c0 + u < np) buf[u] = *reinterpret_cast<const VecT*>(arow + (size_t)(c0 + u) * D);
+          if (c0 + u < np) buf[u] = ld_vec<COHERENT, VecT>(arow + (size_t)(c0 + u) * D);
       }
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
@@ -74,8 +110,8 @@ PKV_DEVICE void reduce_row_wave(const float* acc, const float* pm, const float* 
           if (pidx < 64) {
             cf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), pidx));
           } else {
-            cf = __expf(mrow[pidx] - M);
-            if (normalized) cf *= lrow[pidx];
+            cf = __expf(ld_f32<COHERENT>(mrow + pidx) - M);
+            if (normalized) cf *= ld_f32<COHERENT>(lrow + pidx);
           }
           const float* f = reinterpret_cast<const float*>(&buf[u]);
 #pragma unroll
@@ -119,7 +155,9 @@ PKV_DEVICE int item_parts(const DecodePartialArgs& a, int len) {
 // Writes the final output when the sequence has a single partition and the launch is in
 // final mode, else the partial row (acc divided by L when the launch asks for normalized
 // partials).
-template <int D, bool OUT_BF16>
+// COHERENT (the one-launch decode): the partial row is written for another workgroup of the
+// same launch to combine, with stores every XCD sees (st_f32).
+template <int D, bool OUT_BF16, bool COHERENT = false>
 PKV_DEVICE void store_item_value(const DecodePartialArgs& a, size_t bh, int p, int d, float o, float M2, float L,
                                  bool single) {
   if (single) {
@@ -130,10 +168,10 @@ PKV_DEVICE void store_item_value(const DecodePartialArgs& a, size_t bh, int p, i
     return;
   }
   const size_t si = bh * a.P + p;
-  a.acc[si * D + d] = a.normalize ? o / L : o;
+  st_f32<COHERENT>(a.acc + si * D + d, a.normalize ? o / L : o);
   if (d == 0) {
-    a.m[si] = M2 * kLn2;
-    a.l[si] = L;
+    st_f32<COHERENT>(a.m + si, M2 * kLn2);
+    st_f32<COHERENT>(a.l + si, L);
   }
 }
 
@@ -142,32 +180,28 @@ PKV_DEVICE void store_item_value(const DecodePartialArgs& a, size_t bh, int p, i
 // completes the count combines the G rows (one wave per head) and resets the counter.
 // Every thread of the workgroup calls this (it holds barriers).
 //
-// Ordering, with the fewest cache operations (each XCD has its own L2, not coherent with
-// the others'): every wave waits until its own partial stores have reached L2, the
-// barrier then orders all of them before thread 0's agent-scope release fence (which writes
-// the L2 back) and its relaxed count; the combining workgroup's thread 0 takes an
-// agent-scope acquire fence (which invalidates the stale cached copies) before a barrier
-// lets its waves read. One release per item and one acquire per (sequence, kv head); a
-// fence in every thread instead made the one-launch decode five times slower.
+// Ordering: the partial rows were stored coherently (store_item_value<.., true>); every wave
+// waits until its own stores have completed, which for these stores means they are visible
+// to every XCD; the barrier orders all of them before thread 0's count (a device-scope
+// atomic, performed where every XCD sees it). The workgroup that completes the count reads
+// the rows back with coherent loads, issued only after the count returned. No cache is
+// written back or invalidated as a whole (an agent-scope fence pair per item made the
+// one-launch decode twice as slow as two launches).
 template <int D, bool OUT_BF16, int W>
 __device__ void finish_item_fused(const DecodePartialArgs& a, int b, int kvh, int G, int np) {
   __shared__ int s_last;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial rows are in L2
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial rows are visible device-wide
   __syncthreads();
   int* ctr = a.counters + (size_t)b * a.KVH + kvh;
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    s_last = atomicAdd(ctr, 1) == np - 1;
-  }
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
   __syncthreads();
   if (s_last) {
-    if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    __syncthreads();
     const int w = threadIdx.x >> 6;
     for (int g = w; g < G; g += W)
-      reduce_row_wave<D, OUT_BF16>(a.acc, a.m, a.l, a.P, np, a.normalize != 0,
-                                   (size_t)b * a.H + (size_t)kvh * G + g, a.out, a.lse);
-    if (threadIdx.x == 0) atomicExch(ctr, 0);
+      reduce_row_wave<D, OUT_BF16, true>(a.acc, a.m, a.l, a.P, np, a.normalize != 0,
+                                         (size_t)b * a.H + (size_t)kvh * G + g, a.out, a.lse);
+    if (threadIdx.x == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();  // s_last is read before any later item's count overwrites it
 }

@@ -17,8 +17,10 @@
 //    load. Token-major V gives a lane 8 dims of one token per 16-byte load; byte permutes
 //    turn the 4 tokens' chunks into 8 A operands (tile n of a 128-dim block holds dims
 //    8 * row + n), so no LDS transpose is needed.
-//  * Per-head running max across the 4 lanes of a head, base-2 exponent, lazy re-basing
-//    behind a wave-uniform branch; the stored m is the exact max in natural-log units.
+//  * Lane-local running max; the 4 lanes of a head share a base-2 exponent reference that
+//    is re-based (behind a wave-uniform branch) only when some score passes it by more than
+//    the headroom; the exact max, reduced over the head's lanes once per item, is stored in
+//    natural-log units.
 #include <type_traits>
 
 #include "common.h"
@@ -175,12 +177,14 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
       x[j] = (4 * g + j < ntok) ? xv : kNegInf;
       tmax = fmaxf(tmax, x[j]);
     }
-    tmax = fmaxf(tmax, xor_lanes(tmax, 16));
-    tmax = fmaxf(tmax, xor_lanes(tmax, 32));
+    // lane-local running max (this lane's tokens); the head's four lanes share the exponent
+    // reference m_ref, which moves only when some score passes it by more than the headroom
     m_true = fmaxf(m_true, tmax);
-    const bool rebase = m_true > m_ref + kMfmaRebase;  // true on the first page (m_ref = -inf)
-    if (__builtin_amdgcn_ballot_w64(rebase) != 0) {
-      const float nref = rebase ? m_true : m_ref;
+    if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kMfmaRebase) != 0) {  // the first page, and rarely later
+      float hm = fmaxf(m_true, xor_lanes(m_true, 16));
+      hm = fmaxf(hm, xor_lanes(hm, 32));  // the head's max so far, in all four of its lanes
+      const bool rebase = hm > m_ref + kMfmaRebase;
+      const float nref = rebase ? hm : m_ref;
       const float alpha = fast_exp2(m_ref - nref);
       m_ref = nref;
       lsum *= alpha;
@@ -232,9 +236,11 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
   for (; i + 2 < n_my; ++i) page(Streaming{}, i);    // refills pages 1 .. n_my-2
   for (; i < n_my; ++i) page(Cached{}, i);  // refills the last page, then re-reads it
 
-  // ---- merge: l over the 4 lanes of a head, then waves through LDS
+  // ---- merge: l and the max over the 4 lanes of a head, then waves through LDS
   lsum += xor_lanes(lsum, 16);
   lsum += xor_lanes(lsum, 32);
+  m_true = fmaxf(m_true, xor_lanes(m_true, 16));
+  m_true = fmaxf(m_true, xor_lanes(m_true, 32));
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -266,7 +272,7 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
       o = fmaf(f, sm.red_acc[v][h][d], o);
       L = fmaf(f, sm.red_l[v][h], L);
     }
-    store_item_value<D, true>(a, bh0 + h, p, d, o, M, L, single);
+    store_item_value<D, true, FINAL>(a, bh0 + h, p, d, o, M, L, single);
   }
   __syncthreads();
   if constexpr (FINAL)

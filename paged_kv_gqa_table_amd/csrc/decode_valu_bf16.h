@@ -10,9 +10,15 @@
 //  * P crosses between the two layouts through a per-wave LDS row of bf16 values, stored
 //    in the order each V lane reads them: one 4-, 8- or 16-byte read gives a lane its
 //    token pairs, ready for v_dot2c_f32_bf16.
+//  * Softmax with a lane-local running max: each page costs one max per head and lane, and
+//    a single ballot asks whether any score passed the wave-uniform exponent reference by
+//    more than the headroom; only then (the first page, and rarely later) is the max
+//    reduced over the wave and the accumulators rescaled. The exact max is reduced once
+//    per item, at the merge. (Reducing it over the wave and rescaling every page cost
+//    about 80 more instructions per page: 58.4 against 56.3 us per llama_gqa4 step.)
 //  * Everything else follows decode_valu.h: dense work list, page ids broadcast with
-//    v_readlane, q rows in LDS, single register buffer with early re-issue, wave-uniform
-//    running max with lazy re-basing, base-2 exponent, LDS merge of the waves.
+//    v_readlane, q rows in LDS, single register buffer with early re-issue, base-2
+//    exponent, LDS merge of the waves.
 #pragma once
 
 #include <type_traits>
@@ -291,7 +297,7 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       m_ref[g] = kNegInf;
-      m_true[g] = kNegInf;
+      m_true[g] = kNegInf;  // lane-local running max here; reduced over the wave at the merge
       lsum[g] = 0.f;
 #pragma unroll
       for (int i = 0; i < NACC; ++i) acc[g][i] = 0.f;
@@ -336,21 +342,40 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
           const float v = group_sum<8>(s[g][j]);
           float x = v * a.scale_log2;
           if constexpr (ALIBI) x = fmaf(slope2[g], (float)(pg * BS + kt + 8 * j - (len - 1)), x);
-          s[g][j] = (kt + 8 * j < ntok) ? x : kNegInf;
+          s[g][j] = x;
         }
+      if (ntok < BS) {  // tail page (uniform): scores of tokens past the end are -inf
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) s[g][j] = (kt + 8 * j < ntok) ? s[g][j] : kNegInf;
+      }
 
-      // ---- softmax: wave-uniform max per head, lazy re-basing (branch-free)
+      // ---- softmax: lane-local running max; the wave-uniform reference m_ref moves (and the
+      // accumulators are rescaled) only when some score exceeds it by more than the headroom
+      bool over = false;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float pm = fmaxf(s[g][0], s[g][1]);
+        m_true[g] = fmaxf(m_true[g], pm);
+        over |= pm > m_ref[g] + kRebaseBf16;
+      }
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float wm = wave_max_uniform<8>(m_true[g]);
+          if (wm > m_ref[g] + kRebaseBf16) {  // uniform
+            const float alpha = fast_exp2(m_ref[g] - wm);  // 0 on the first page
+            m_ref[g] = wm;
+            lsum[g] *= alpha;
+#pragma unroll
+            for (int q = 0; q < NACC; ++q) acc[g][q] *= alpha;
+          }
+        }
+      }
       float pr[G][2];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float pm = wave_max_uniform<8>(fmaxf(s[g][0], s[g][1]));
-        m_true[g] = fmaxf(m_true[g], pm);
-        const float new_ref = (m_true[g] > m_ref[g] + kRebaseBf16) ? m_true[g] : m_ref[g];
-        const float alpha = fast_exp2(m_ref[g] - new_ref);  // 0 on the first page, else 1 unless re-based
-        m_ref[g] = new_ref;
-        lsum[g] *= alpha;
-#pragma unroll
-        for (int q = 0; q < NACC; ++q) acc[g][q] *= alpha;
         pr[g][0] = fast_exp2(s[g][0] - m_ref[g]);
         pr[g][1] = fast_exp2(s[g][1] - m_ref[g]);
         lsum[g] += pr[g][0] + pr[g][1];
@@ -454,6 +479,7 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
     // ---- merge: l over the q.K token groups; acc over the P.V token groups; then waves
 #pragma unroll
     for (int g = 0; g < G; ++g) {
+      m_true[g] = wave_max_uniform<8>(m_true[g]);
       lsum[g] = strided_sum<8>(lsum[g]);
 #pragma unroll
       for (int q = 0; q < NACC; ++q) {
@@ -506,7 +532,7 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
         L = fmaf(f, sm.red_l[v][g], L);
       }
       if constexpr (FP8) o *= a.v_scale;
-      store_item_value<D, true>(a, bh0 + g, p, d, o, M, L, single);
+      store_item_value<D, true, FINAL>(a, bh0 + g, p, d, o, M, L, single);
     }
     __syncthreads();
     if constexpr (FINAL)
@@ -558,10 +584,10 @@ hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream
   // faster of the two (llama_gqa4, 2,048 workgroups on 1,280 slots: 58.2 against 59.2 us).
   // Larger grids keep the list.
   bool plain = !use_dense_worklist(a.S, a.KVH, grid_parts);
-  if constexpr (!SPLIT && !FINAL) {
+  if constexpr (!SPLIT) {
     if (!plain) {
       const int pcap = resident_grid(
-          reinterpret_cast<const void*>(&decode_partial_bf16_kernel<D, G, XP, W, false, false, false, ALIBI, FP8>), 64 * W,
+          reinterpret_cast<const void*>(&decode_partial_bf16_kernel<D, G, XP, W, false, false, FINAL, ALIBI, FP8>), 64 * W,
           0);
       plain = upper <= 2L * pcap;
     }
@@ -581,11 +607,11 @@ hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream
     const int grid = (int)(upper < cap ? upper : cap);
     hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, true, SPLIT, FINAL, ALIBI, FP8>), dim3(grid),
                        dim3(64 * W), lds, s, a, grid_parts);
-  } else if constexpr (!SPLIT && !FINAL) {
-    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, false, false, false, ALIBI, FP8>), dim3((unsigned)upper),
+  } else if constexpr (!SPLIT) {
+    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, false, false, FINAL, ALIBI, FP8>), dim3((unsigned)upper),
                        dim3(64 * W), 0, s, a, grid_parts);
   } else {
-    return hipErrorNotSupported;  // NUM_SPLITS and one-launch decode use the work list (kMaxDenseSeqs sequences)
+    return hipErrorNotSupported;  // NUM_SPLITS uses the work list (kMaxDenseSeqs sequences)
   }
   return hipGetLastError();
 }
