@@ -66,6 +66,7 @@ PKV_DEVICE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // DPP controls (GFX9 encoding).
 constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppQuadRev = 0x1B;       // quad_perm [3,2,1,0] (lane ^ 3)
 constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7-i inside each 8-lane half row
 constexpr int kDppMirror = 0x140;       // lane i <-> 15-i inside each 16-lane row
 constexpr int kDppRor8 = 0x128;         // lane i <- lane (i+8) mod 16 inside a row

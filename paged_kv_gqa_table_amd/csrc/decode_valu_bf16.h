@@ -3,10 +3,13 @@
 // Same computation as decode_valu.h (per-partition m, l and unnormalized acc for the G
 // heads of one kv head; PagedAttention V2 Triton page, _partition_attn_kernel, with the
 // flash-decode post's unnormalized accumulator), with a layout tuned for bf16:
-//  * K and V use different lane layouts. For q.K a token's row is split over 8 lanes (so
-//    each score needs only 3 DPP steps); for P.V over 16 lanes in the token-major layout
-//    (so each lane owns fewer dims and the accumulator is small), or the linear 16-byte
-//    chunk order of the x-packed V layout.
+//  * K and V use different lane layouts. For q.K a token's row is split over 8 lanes; the
+//    2G partial scores of a lane are reduce-scattered over those 8 lanes (a few DPP adds,
+//    lane-permuted registers, see bf16_items), so each lane ends with whole scores and the
+//    softmax runs once per (head, token) instead of once per lane of the row. For P.V a
+//    token row is split over 16 lanes in the token-major layout (so each lane owns fewer
+//    dims and the accumulator is small), or read in the linear 16-byte chunk order of the
+//    x-packed V layout.
 //  * P crosses between the two layouts through a per-wave LDS row of bf16 values, stored
 //    in the order each V lane reads them: one 4-, 8- or 16-byte read gives a lane its
 //    token pairs, ready for v_dot2c_f32_bf16.
@@ -113,6 +116,45 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
   const int w = uniform((int)(threadIdx.x >> 6));
   const int kc = lane & 7;    // q.K: chunk column
   const int kt = lane >> 3;   // q.K: token (and kt + 8)
+  // Scores in the reduce-scatter layout. The 2G (head, token half) scores a token row needs
+  // are cut into blocks of 8 values (4 heads), then at most one block of 4 (2 heads) and one
+  // of 2 (1 head). In a block of n values a lane keeps its partial scores in a lane-permuted
+  // register order (register r holds value r ^ (kc & (n - 2)): the head bits follow the lane
+  // through the q addresses it reads, the K registers keep their token order), so a few DPP
+  // adds over the 8 lanes of the row leave every lane with whole scores: in a block of 8,
+  // lane kc holds head (kc >> 1), token half kc & 1, each value once; in a block of 4 each
+  // value sits in two lanes (kc, kc ^ 4), in a block of 2 in four. The exponent, running
+  // max and sum are then computed once per value instead of once per lane of the row.
+  constexpr int NB8 = 2 * G / 8;            // blocks of 4 heads
+  constexpr bool HAS4 = (2 * G) % 8 >= 4;   // a block of 2 heads
+  constexpr bool HAS2 = G % 2 == 1;         // a block of 1 head
+  constexpr int NLV = NB8 + HAS4 + HAS2;    // scores per lane
+  constexpr int H4 = 4 * NB8;               // first head of the 2-head block
+  constexpr int H2 = 4 * NB8 + 2 * HAS4;    // the head of the 1-head block
+  const bool odd = (kc & 1) != 0;
+  // the lane's (head, token) of its k-th score, and whether it is the lane that publishes it
+  auto lv_head = [&](int k) -> int {
+    if (k < NB8) return 4 * k + (kc >> 1);
+    if (HAS4 && k == NB8) return H4 + ((kc >> 1) & 1);
+    return H2;
+  };
+  auto lv_owner = [&](int k) -> bool {
+    if (k < NB8) return true;
+    if (HAS4 && k == NB8) return (kc & 4) == 0;
+    return (kc & 6) == 0;
+  };
+  const int rs_t = kt + 8 * (kc & 1);  // the lane's token within the page (every block)
+  // a lane holding head g's k-th score, for reading head-uniform values back
+  auto lv_src_lane = [&](int g) -> int {
+    if (g < H4) return 2 * (g & 3);
+    if (HAS4 && g < H2) return 2 * (g - H4);
+    return 0;
+  };
+  auto lv_of_head = [&](int g) -> int {
+    if (g < H4) return g >> 2;
+    if (HAS4 && g < H2) return NB8;
+    return NB8 + (HAS4 ? 1 : 0);
+  };
   const int vc = lane % LV;   // P.V token-major: chunk column
   const int vt = lane / LV;   // P.V token-major: first token
   const int H = a.H;
@@ -211,10 +253,6 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
     const int pg_begin = p * ppp;
     const int pg_end = min(pg_begin + ppp, (len + BS - 1) / BS);
     const int n_my = pg_end - pg_begin - w > 0 ? (pg_end - pg_begin - w + W - 1) / W : 0;
-    // ALiBi slope of each head in base-2 units (uniform); unused without ALIBI
-    float slope2[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) slope2[g] = ALIBI ? a.alibi[kvh * G + g] * kLog2e : 0.f;
     const char* kbase = reinterpret_cast<const char*>(a.kc) + (size_t)kvh * PAGEB;
     const char* vbase = reinterpret_cast<const char*>(a.vc) + (size_t)kvh * PAGEB;
     int cache_base = 0;  // first page (in this wave's order) whose id is in pid_cache
@@ -303,6 +341,31 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
       for (int i = 0; i < NACC; ++i) acc[g][i] = 0.f;
     }
     const uint32_t* q_cur = &sm.q_lds[slot][0][0];
+    // per score of the lane: exponent reference (uniform over the lanes of its head), running
+    // max, running sum (over the lane's own tokens) and ALiBi slope in base-2 units
+    float rs_ref[NLV], rs_max[NLV], rs_sum[NLV], rs_slope[NLV];
+#pragma unroll
+    for (int k = 0; k < NLV; ++k) {
+      rs_ref[k] = kNegInf;
+      rs_max[k] = kNegInf;
+      rs_sum[k] = 0.f;
+      rs_slope[k] = ALIBI ? a.alibi[kvh * G + lv_head(k)] * kLog2e : 0.f;
+    }
+    // max / sum over the lanes of one head (token halves and rows; duplicates of a value in
+    // lanes kc ^ 2, kc ^ 4 are not added twice)
+    auto head_max = [&](float v) {
+      v = fmaxf(v, dpp<kDppQuadXor1>(v));
+      v = fmaxf(v, dpp<kDppRor8>(v));
+      v = fmaxf(v, xor_lanes(v, 16));
+      return fmaxf(v, xor_lanes(v, 32));
+    };
+    auto head_sum = [&](float v) {
+      v += dpp<kDppQuadXor1>(v);
+      v += dpp<kDppRor8>(v);
+      v += xor_lanes(v, 16);
+      return v + xor_lanes(v, 32);
+    };
+    auto lane_xor4 = [&](float v) { return dpp<kDppQuadRev>(dpp<kDppHalfMirror>(v)); };
 
     // one page; `nt` is the cache policy of the loads it issues for page nx
     auto page = [&](auto nt, int i) {
@@ -311,11 +374,10 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
       // refill target: the next page, or the last page again past the end (see issue_k)
       const int nx = i + 1 < n_my ? i + 1 : i;
       ensure_ids(nx);
-      // ---- scores of tokens kt and kt + 8, summed over the 8 lanes of a row
+      // ---- scores (reduce-scatter layout, see above)
       asm volatile("" ::: "memory");  // q is re-read from LDS every page (registers are scarce)
-      float s[G][2];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
+      // partial dot products of head g's q row with the lane's two K tokens
+      auto qk2 = [&](int g, float& s0, float& s1) {
         uint4 qv[KCPL];
 #pragma unroll
         for (int k = 0; k < KCPL; ++k) qv[k] = *reinterpret_cast<const uint4*>(q_cur + g * (D / 2) + (kc + 8 * k) * 4);
@@ -330,65 +392,77 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
             d0 = dot2_bf16(qv[k].z, kk.z, d0);
             d1 = dot2_bf16(qv[k].w, kk.w, d1);
           }
-          s[g][j] = d0 + d1;
+          (j == 0 ? s0 : s1) = d0 + d1;
         }
+      };
+      float xs[NLV];
+#pragma unroll
+      for (int bk = 0; bk < NB8; ++bk) {  // 4 heads: partners kc ^ 7, kc ^ 2, kc ^ 1
+        float x8[8];
+#pragma unroll
+        for (int rh = 0; rh < 4; ++rh) qk2(4 * bk + (rh ^ (kc >> 1)), x8[2 * rh], x8[2 * rh + 1]);
+        float y4[4], z2[2];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y4[r] = x8[r] + dpp<kDppHalfMirror>(x8[r ^ 6]);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) z2[r] = y4[r] + dpp<kDppQuadXor2>(y4[r ^ 2]);
+        xs[bk] = (odd ? z2[1] : z2[0]) + dpp<kDppQuadXor1>(odd ? z2[0] : z2[1]);
+      }
+      if constexpr (HAS4) {  // 2 heads: partners kc ^ 2, kc ^ 1, then the copy in kc ^ 4
+        float x4[4];
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh) qk2(H4 + (rh ^ ((kc >> 1) & 1)), x4[2 * rh], x4[2 * rh + 1]);
+        float z2[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) z2[r] = x4[r] + dpp<kDppQuadXor2>(x4[r ^ 2]);
+        const float z = (odd ? z2[1] : z2[0]) + dpp<kDppQuadXor1>(odd ? z2[0] : z2[1]);
+        xs[NB8] = z + lane_xor4(z);
+      }
+      if constexpr (HAS2) {  // 1 head: partner kc ^ 1, then the copies in kc ^ 2, kc ^ 4
+        float x2[2];
+        qk2(H2, x2[0], x2[1]);
+        float z = (odd ? x2[1] : x2[0]) + dpp<kDppQuadXor1>(odd ? x2[0] : x2[1]);
+        z += dpp<kDppQuadXor2>(z);
+        xs[NLV - 1] = z + lane_xor4(z);
       }
       issue_k(nt, nx);
 
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float v = group_sum<8>(s[g][j]);
-          float x = v * a.scale_log2;
-          if constexpr (ALIBI) x = fmaf(slope2[g], (float)(pg * BS + kt + 8 * j - (len - 1)), x);
-          s[g][j] = x;
-        }
-      if (ntok < BS) {  // tail page (uniform): scores of tokens past the end are -inf
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) s[g][j] = (kt + 8 * j < ntok) ? s[g][j] : kNegInf;
-      }
-
-      // ---- softmax: lane-local running max; the wave-uniform reference m_ref moves (and the
-      // accumulators are rescaled) only when some score exceeds it by more than the headroom
+      // ---- softmax: lane-local running max; the exponent reference of a head (uniform over
+      // its lanes) moves, and the head's accumulators are rescaled, only when some score
+      // exceeds it by more than the headroom
       bool over = false;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float pm = fmaxf(s[g][0], s[g][1]);
-        m_true[g] = fmaxf(m_true[g], pm);
-        over |= pm > m_ref[g] + kRebaseBf16;
+      for (int k = 0; k < NLV; ++k) {
+        float x = xs[k] * a.scale_log2;
+        if constexpr (ALIBI) x = fmaf(rs_slope[k], (float)(pg * BS + rs_t - (len - 1)), x);
+        if (ntok < BS) x = rs_t < ntok ? x : kNegInf;  // tail page (uniform branch)
+        xs[k] = x;
+        rs_max[k] = fmaxf(rs_max[k], x);
+        over |= x > rs_ref[k] + kRebaseBf16;
       }
-      if (__builtin_amdgcn_ballot_w64(over) != 0) {
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {  // the first page, and rarely later
+        float alpha[NLV];
+#pragma unroll
+        for (int k = 0; k < NLV; ++k) {
+          const float hm = head_max(rs_max[k]);
+          const float nref = hm > rs_ref[k] + kRebaseBf16 ? hm : rs_ref[k];  // uniform per head
+          alpha[k] = fast_exp2(rs_ref[k] - nref);  // 0 on the first page
+          rs_ref[k] = nref;
+          rs_sum[k] *= alpha[k];
+        }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const float wm = wave_max_uniform<8>(m_true[g]);
-          if (wm > m_ref[g] + kRebaseBf16) {  // uniform
-            const float alpha = fast_exp2(m_ref[g] - wm);  // 0 on the first page
-            m_ref[g] = wm;
-            lsum[g] *= alpha;
+          const float ag = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[lv_of_head(g)]), lv_src_lane(g)));
 #pragma unroll
-            for (int q = 0; q < NACC; ++q) acc[g][q] *= alpha;
-          }
+          for (int q = 0; q < NACC; ++q) acc[g][q] *= ag;
         }
       }
-      float pr[G][2];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        pr[g][0] = fast_exp2(s[g][0] - m_ref[g]);
-        pr[g][1] = fast_exp2(s[g][1] - m_ref[g]);
-        lsum[g] += pr[g][0] + pr[g][1];
-      }
-
       // ---- P to the wave's LDS row (bf16), in the order the V lanes read it
-      if (kc == 0) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const uint32_t pk = pack_bf16x2(pr[g][0], pr[g][1]);
-          sm.p_lds[w][g][p_slot<LV, XP>(kt)] = (uint16_t)(pk & 0xffffu);
-          sm.p_lds[w][g][p_slot<LV, XP>(kt + 8)] = (uint16_t)(pk >> 16);
-        }
+      for (int k = 0; k < NLV; ++k) {
+        const float pv = fast_exp2(xs[k] - rs_ref[k]);
+        rs_sum[k] += pv;
+        if (lv_owner(k)) sm.p_lds[w][lv_head(k)][p_slot<LV, XP>(rs_t)] = (uint16_t)(pack_bf16x2(pv, 0.f) & 0xffffu);
       }
       wave_lds_fence();
 
@@ -477,10 +551,23 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
     if (has_next) fetch_q(nb, nkvh, slot ^ 1);
 
     // ---- merge: l over the q.K token groups; acc over the P.V token groups; then waves
+    {
+      float ls[NLV], mt[NLV];
+#pragma unroll
+      for (int k = 0; k < NLV; ++k) {
+        ls[k] = head_sum(rs_sum[k]);
+        mt[k] = head_max(rs_max[k]);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int k = lv_of_head(g), src = lv_src_lane(g);
+        lsum[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[k]), src));
+        m_true[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mt[k]), src));
+        m_ref[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rs_ref[k]), src));
+      }
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      m_true[g] = wave_max_uniform<8>(m_true[g]);
-      lsum[g] = strided_sum<8>(lsum[g]);
 #pragma unroll
       for (int q = 0; q < NACC; ++q) {
         if constexpr (XP) acc[g][q] = group_sum<2>(acc[g][q]);
