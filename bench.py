@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="KV pool copies to cycle (0 = auto)")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--eager", action="store_true", help="time eager submission instead of a HIP graph replay")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time to spend")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB (read MIB, write MIB) a few times, "
@@ -56,11 +57,18 @@ def _events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
-def bench_decode(case, steps, warmup, copies=0, one_launch=False):
+def bench_decode(case, steps, warmup, copies=0, one_launch=False, graph=True):
     """Time `steps` decode steps; returns a dict of measurements. A step is the two phases
     (paged_decode_partial + paged_decode_reduce), or with `one_launch` the single-launch
     paged_decode (phase 1 with the combine done by the last workgroup of each (sequence,
-    kv head)); the timed kernel is then that one launch."""
+    kv head)); the timed kernel is then that one launch.
+
+    With `graph`, the `steps` steps are captured once into a HIP graph and the timed region
+    is one replay of it (a decode loop submits its kernels that way; eager submission from
+    Python adds tens of microseconds of host latency before the first kernel, which at 20
+    steps is over a microsecond per step). The graph is replayed once untimed first, and the
+    output of the timed replay must equal, bit for bit, an eager run of its last step. The
+    eager time of the same steps is reported beside it."""
     import torch
     import paged_kv_gqa_table_amd as pkv
 
@@ -104,17 +112,42 @@ def bench_decode(case, steps, warmup, copies=0, one_launch=False):
         step(i)
     torch.cuda.synchronize()
 
+    def timed_eager():
+        t_start, t_end = _events(2)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        t_start.record()
+        for i in range(steps):
+            step(i)
+        t_end.record()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, t_start.elapsed_time(t_end)
+
     # Region 1 (the contract): exactly `steps` back-to-back steps between two synchronizes.
-    t_start, t_end = _events(2)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    t_start.record()
-    for i in range(steps):
-        step(i)
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = t_start.elapsed_time(t_end)
+    eager_wall, eager_gpu_ms = timed_eager()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                step(i)
+        g.replay()  # untimed: the first replay uploads the graph
+        torch.cuda.synchronize()
+        t_start, t_end = _events(2)
+        t0 = time.perf_counter()
+        t_start.record()
+        g.replay()
+        t_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_ms = t_start.elapsed_time(t_end)
+        got = out.clone()
+        step(steps - 1)  # the graph's last step, eagerly
+        torch.cuda.synchronize()
+        if not torch.equal(got, out):
+            raise RuntimeError("graph replay and eager step disagree")
+        del g
+    else:
+        wall, gpu_ms = eager_wall, eager_gpu_ms
 
     # Region 2: the same steps with HIP events around every phase-1 launch, on the stream
     # the kernel runs on, for the dominant kernel's own average duration.
@@ -130,8 +163,9 @@ def bench_decode(case, steps, warmup, copies=0, one_launch=False):
 
     kv_bytes = case.kv_bytes()
     return dict(
-        copies=copies, pool_bytes=pool_bytes, kv_bytes=kv_bytes,
+        copies=copies, pool_bytes=pool_bytes, kv_bytes=kv_bytes, graph=graph,
         wall_ms_per_step=wall * 1e3 / steps, gpu_ms_per_step=gpu_ms / steps,
+        eager_wall_ms_per_step=eager_wall * 1e3 / steps, eager_gpu_ms_per_step=eager_gpu_ms / steps,
         partial_avg_ms=avg_part_ms, partial_median_ms=med_part_ms,
         partial_p10_ms=part_ms[len(part_ms) // 10], partial_p90_ms=part_ms[(9 * len(part_ms)) // 10],
     )
@@ -312,18 +346,20 @@ def cpu_baseline_decode(case, budget_s):
             "seconds": round(dt, 2), "ms_per_step_equiv": dt * 1e3 * (case.kv_bytes() / max(done_bytes, 1))}
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_partial_llama_gqa4_hbm_counters.md")
+def traffic_profile_path(workload):
+    return os.path.join(ROOT, "profiles", f"decode_partial_{workload}_hbm_counters.md")
 
 
 def profiled_traffic(workload):
-    """HBM bytes per phase-1 launch from the committed counter summary (FETCH_SIZE + WRITE_SIZE,
-    scaled by a copy kernel of known size), or None when that summary does not cover this
-    workload or the kernel's sources have changed since the counters were read."""
+    """HBM bytes per phase-1 launch from the committed counter summary of this workload
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel of known size), or None when there is
+    none or the kernel's sources have changed since the counters were read."""
     import hashlib
-    if workload != "llama_gqa4" or not os.path.exists(TRAFFIC_PROFILE):
+    path = traffic_profile_path(workload)
+    if not os.path.exists(path):
         return None
     fields = {}
-    for line in open(TRAFFIC_PROFILE):
+    for line in open(path):
         k, sep, v = line.partition(":")
         if sep and k.strip() in ("traffic_bytes_per_launch", "kernel_sources_sha256", "kernel_sources"):
             fields[k.strip()] = v.strip()
@@ -409,7 +445,7 @@ def main():
 
     _log(f"generating workload {args.workload}")
     case = inputs.decode_workload(args.workload)
-    r = bench_decode(case, args.steps, args.warmup, args.copies)
+    r = bench_decode(case, args.steps, args.warmup, args.copies, graph=not args.eager)
     kv = r["kv_bytes"]
     ms = r["wall_ms_per_step"]
     gbs = kv / (ms * 1e-3) / 1e9
@@ -424,7 +460,8 @@ def main():
                    "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
                    "block_size": case.block_size, "partition_size": case.partition_size,
                    "layout": case.layout, "kv_bytes_per_step": kv, "pool_copies_cycled": r["copies"],
-                   "seq_len_total": int(case.seq_lens.sum())},
+                   "seq_len_total": int(case.seq_lens.sum()),
+                   "submission": "hip_graph" if r["graph"] else "eager"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(args.workload),
                      "algorithmic_bytes_per_launch": kv,
@@ -432,9 +469,15 @@ def main():
                      "kernel_median_us": r["partial_median_ms"] * 1e3,
                      "kernel_p10_us": r["partial_p10_ms"] * 1e3, "kernel_p90_us": r["partial_p90_ms"] * 1e3},
         "gpu_event_ms_per_step": r["gpu_ms_per_step"],
+        "eager_us_per_step": r["eager_wall_ms_per_step"] * 1e3,
+        "eager_gpu_event_us_per_step": r["eager_gpu_ms_per_step"] * 1e3,
     }
+    if r["graph"]:
+        result["graph_note"] = (f"the {args.steps} steps are captured once into a HIP graph and timed as one replay, "
+                                "after the warmup steps and one untimed replay; its output equals an eager step "
+                                "bit for bit")
     # warm reference: one pool only, so part of the KV stays in the Infinity Cache between steps
-    rw = bench_decode(case, max(20, args.steps // 4), 5, copies=1)
+    rw = bench_decode(case, max(20, args.steps // 4), 5, copies=1, graph=not args.eager)
     result["warm_single_pool"] = {"us_per_step": rw["wall_ms_per_step"] * 1e3,
                                   "GB_s": kv / (rw["wall_ms_per_step"] * 1e-3) / 1e9,
                                   "kernel_avg_us": rw["partial_avg_ms"] * 1e3}
@@ -448,24 +491,34 @@ def main():
             "us_per_step": rf["ms"] * 1e3, "kv_bytes": rf["kv_bytes"],
             "GB_s": rf["kv_bytes"] / (rf["ms"] * 1e-3) / 1e9,
             "kernel": "paged_attention_v2 (float8 e4m3 x-packed cache, both phases)"}
-        ro = bench_decode(case, max(20, args.steps // 2), 5, one_launch=True)
+        ro = bench_decode(case, max(20, args.steps // 2), 5, one_launch=True, graph=not args.eager)
         extra["llama_gqa4_one_launch"] = {"us_per_step": ro["wall_ms_per_step"] * 1e3,
                                           "GB_s": kv / (ro["wall_ms_per_step"] * 1e-3) / 1e9,
                                           "kernel_avg_us": ro["partial_avg_ms"] * 1e3}
+        secondary = {}
         for name in ("wide_gqa6", "skewed_gqa8"):
             _log(f"secondary workload {name}")
             c2 = inputs.decode_workload(name)
-            r2 = bench_decode(c2, max(10, args.steps // 4), 5)
-            extra[name] = {"us_per_step": r2["wall_ms_per_step"] * 1e3,
-                           "GB_s": c2.kv_bytes() / (r2["wall_ms_per_step"] * 1e-3) / 1e9,
-                           "partial_GB_s": c2.kv_bytes() / (r2["partial_avg_ms"] * 1e-3) / 1e9,
-                           "layout": c2.layout}
-            extra[name]["pct_of_peak"] = 100.0 * extra[name]["GB_s"] / HBM_PEAK_GBS
-            r3 = bench_decode(c2, max(10, args.steps // 4), 5, one_launch=True)
-            extra[name]["one_launch_us_per_step"] = r3["wall_ms_per_step"] * 1e3
-            extra[name]["one_launch_GB_s"] = c2.kv_bytes() / (r3["wall_ms_per_step"] * 1e-3) / 1e9
+            n2 = max(20, min(args.steps, 40))
+            r2 = bench_decode(c2, n2, 5, graph=not args.eager)
+            kv2 = c2.kv_bytes()
+            ach2 = kv2 / (r2["partial_avg_ms"] * 1e-3) / 1e9
+            line = {"steps": n2, "us_per_step": r2["wall_ms_per_step"] * 1e3,
+                    "GB_s": kv2 / (r2["wall_ms_per_step"] * 1e-3) / 1e9,
+                    "eager_us_per_step": r2["eager_wall_ms_per_step"] * 1e3,
+                    "layout": c2.layout, "kv_bytes_per_step": kv2,
+                    "roofline": {"bound": "hbm", "achieved": ach2, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": ach2 / HBM_PEAK_GBS, "traffic": profiled_traffic(name),
+                                 "algorithmic_bytes_per_launch": kv2, "kernel": "paged_decode_partial",
+                                 "kernel_avg_us": r2["partial_avg_ms"] * 1e3}}
+            line["pct_of_peak"] = 100.0 * line["GB_s"] / HBM_PEAK_GBS
+            r3 = bench_decode(c2, n2, 5, one_launch=True, graph=not args.eager)
+            line["one_launch_us_per_step"] = r3["wall_ms_per_step"] * 1e3
+            line["one_launch_GB_s"] = kv2 / (r3["wall_ms_per_step"] * 1e-3) / 1e9
+            secondary[name] = line
             del c2
             torch.cuda.empty_cache()
+        result["secondary"] = secondary
         try:
             _log("secondary workload mla_prefill_b8")
             mc = inputs.mla_prefill_b8()
