@@ -9,6 +9,9 @@
  *                         the same two phases with [FD]'s NUM_SPLITS page-aligned splits
  *   paged_decode          the whole decode in one launch (single pass when every
  *                         sequence fits one partition)
+ *   paged_decode_partial_ex, paged_decode_ex
+ *                         phase 1 / the one-launch decode with cache options: float8
+ *                         e4m3 K/V caches with k_scale / v_scale, and ALiBi slopes
  *   paged_attention_v2    [PAv2]'s launcher: x-packed cache, 512-token partitions,
  *                         normalized partials (tmp_output, exp_sums, max_logits)
  *   mla_paged_prefill     MLA causal paged prefill (page_size 1), base-2 LSE
@@ -62,7 +65,7 @@ typedef enum {
   PKV_EHIP = 3           /* the HIP runtime reported an error for the launch        */
 } pkv_status;
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 /* K/V caches only (paged_attention_v2) */ } pkv_dtype;
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 /* K/V caches only, with a bf16 query */ } pkv_dtype;
 
 typedef enum {
   /* K and V: [num_blocks, num_kv_heads, block_size, head_dim]            ([FD] kernel arguments) */
@@ -212,6 +215,54 @@ int paged_decode(const void* query, int dtype,
                  void* out, float* lse, void* stream);
 
 /*
+ * paged_decode_partial_ex -- paged_decode_partial (num_splits == 0) or
+ * paged_decode_split_partial (num_splits > 0, partition_size ignored) with cache options
+ * ([PAv2]'s launcher names alibi_slopes, kv_cache_dtype, k_scale and v_scale without using
+ * them; the readings here are those of paged_attention_v2 below):
+ *   kv_dtype      `dtype` (the cache holds the query's type; k_scale = v_scale = 1), or
+ *                 PKV_FP8_E4M3: key_cache / value_cache hold float8 e4m3 (OCP) values, one
+ *                 byte each, in `layout` (x-packed with x = 16); the keys and values used are
+ *                 k_scale and v_scale times the stored values. Needs a bf16 query.
+ *   alibi_slopes  [num_heads] float32 device array, or NULL: the score of key t of sequence
+ *                 b for head h becomes scale * <q, k_t> - alibi_slopes[h] * (len_b - 1 - t)
+ *                 (Press, Smith and Lewis, ICLR 2022; the decoded token is the last position).
+ * The partials are those of the plain entry points, with partial_m of each partition
+ * including the bias; combine them with paged_decode_reduce / paged_decode_split_reduce.
+ * Every other argument, status and bound is that of paged_decode_partial (max_num_partitions
+ * >= num_splits under the split policy).
+ * PKV_EINVAL additionally: kv_dtype neither `dtype` nor PKV_FP8_E4M3, scales not finite,
+ *   scales other than 1 without a float8 cache. PKV_EUNSUPPORTED: a float8 cache with a
+ *   query other than bf16.
+ */
+int paged_decode_partial_ex(const void* query, int dtype,
+                            const void* key_cache, const void* value_cache, int layout,
+                            int kv_dtype, float k_scale, float v_scale, const float* alibi_slopes,
+                            const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* seq_lens,
+                            int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                            int block_size, int num_blocks, float scale,
+                            int partition_size, int num_splits, int max_num_partitions,
+                            int max_seq_len,
+                            float* partial_acc, float* partial_m, float* partial_l,
+                            void* stream);
+
+/*
+ * paged_decode_ex -- paged_decode with the cache options of paged_decode_partial_ex
+ * (kv_dtype, k_scale, v_scale, alibi_slopes; same meaning, checks and statuses). Everything
+ * else, including the counters contract, is that of paged_decode.
+ */
+int paged_decode_ex(const void* query, int dtype,
+                    const void* key_cache, const void* value_cache, int layout,
+                    int kv_dtype, float k_scale, float v_scale, const float* alibi_slopes,
+                    const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* seq_lens,
+                    int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                    int block_size, int num_blocks, float scale,
+                    int partition_size, int num_splits, int max_num_partitions, int max_seq_len,
+                    float* partial_acc, float* partial_m, float* partial_l, int32_t* counters,
+                    void* out, float* lse, void* stream);
+
+/*
  * paged_attention_v2 -- [PAv2]'s paged_attention_v2_triton launcher as a C call: both
  * phases on `stream` with its fixed 512-token partitions and its x-packed cache layout
  * (PKV_KV_XPACKED), keeping its normalized partial form:
@@ -235,8 +286,7 @@ int paged_decode(const void* query, int dtype,
  *   or PKV_FP8_E4M3: key_cache / value_cache hold float8 e4m3 (OCP) values, x-packed with
  *   x = 16; the keys and values used are k_scale and v_scale times the stored values
  *   ([PAv2]'s launcher takes these three arguments without using them; this is the plainest
- *   reading, a per-tensor dequantization factor). Needs a bf16 query and at most 8 query
- *   heads per kv head.
+ *   reading, a per-tensor dequantization factor). Needs a bf16 query.
  * PKV_EINVAL / PKV_EUNSUPPORTED: as paged_decode_partial with partition_size = 512.
  */
 int paged_attention_v2(void* out, float* exp_sums, float* max_logits, float* tmp_output,

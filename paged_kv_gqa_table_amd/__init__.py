@@ -33,6 +33,7 @@ import torch
 
 __all__ = ["mla_decode_default_split", "paged_decode_partial", "paged_decode_reduce", "paged_decode_split_partial",
            "paged_decode_split_reduce", "paged_decode", "paged_decode_into", "paged_decode_static",
+           "paged_decode_partial_ex", "paged_decode_ex",
            "paged_attention_v2",
            "mla_paged_prefill", "mla_paged_prefill_pages", "mla_paged_decode", "read_bandwidth", "lib", "library_path", "PkvError", "TOKEN_MAJOR",
            "XPACKED", "num_partitions"]
@@ -93,6 +94,12 @@ def lib() -> ctypes.CDLL:
     L.mla_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                    vp, vp, vp, vp, vp, vp]
     L.mla_paged_decode.restype = i32
+    L.paged_decode_partial_ex.argtypes = [vp, i32, vp, vp, i32, i32, f32, f32, vp, vp, i32, vp, i32, i32, i32, i32,
+                                          i32, i32, f32, i32, i32, i32, i32, vp, vp, vp, vp]
+    L.paged_decode_partial_ex.restype = i32
+    L.paged_decode_ex.argtypes = [vp, i32, vp, vp, i32, i32, f32, f32, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                  f32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.paged_decode_ex.restype = i32
     L.paged_decode_static.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, i32,
                                       i32, i32, vp, vp, vp]
     L.paged_decode_static.restype = i32
@@ -155,13 +162,15 @@ def _pool_geometry(key_cache: torch.Tensor, layout: str) -> Tuple[int, int, int]
     raise ValueError(f"unknown layout {layout!r}")
 
 
-def _check_decode_inputs(query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, layout):
-    """Common checks of the decode inputs; returns (S, H, D, num_blocks, block_size)."""
+def _check_decode_inputs(query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, layout,
+                         kv_dtype=None):
+    """Common checks of the decode inputs; returns (S, H, D, num_blocks, block_size). The
+    caches hold the query's dtype, or ``kv_dtype`` when given (torch.float8_e4m3fn)."""
     if query.dtype not in _DTYPE:
         raise ValueError(f"query dtype {query.dtype} not supported")
     _dev("query", query, ndim=3)
-    _dev("key_cache", key_cache, query.dtype)
-    _dev("value_cache", value_cache, query.dtype)
+    _dev("key_cache", key_cache, kv_dtype or query.dtype)
+    _dev("value_cache", value_cache, kv_dtype or query.dtype)
     _dev("block_tables", block_tables, torch.int32, 2)
     _dev("seq_lens", seq_lens, torch.int32, 1)
     S, H, D = query.shape
@@ -194,15 +203,47 @@ def _check_partials(partial_acc, partial_m, partial_l, S, H, D):
     return P
 
 
+def _cache_options(query, kv_cache_dtype, k_scale, v_scale, alibi_slopes):
+    """(kv dtype code for the C ABI, torch dtype of the caches) for the cache options, or
+    (None, None) when they are all at their defaults (an unquantized cache, no ALiBi)."""
+    if alibi_slopes is not None:
+        _dev("alibi_slopes", alibi_slopes, torch.float32, 1)
+        if alibi_slopes.numel() != query.shape[1]:
+            raise ValueError("alibi_slopes must hold one slope per query head")
+    if kv_cache_dtype in ("fp8", "fp8_e4m3"):
+        return 2, torch.float8_e4m3fn
+    if kv_cache_dtype != "auto":
+        raise NotImplementedError(f"kv_cache_dtype {kv_cache_dtype!r}")
+    if float(k_scale) != 1.0 or float(v_scale) != 1.0:
+        raise ValueError("k_scale / v_scale apply to a float8 cache only")
+    if alibi_slopes is None:
+        return None, None
+    return _DTYPE[query.dtype], None
+
+
 def paged_decode_partial(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
                          block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
                          num_kv_heads: int, partition_size: int, max_seq_len: int,
                          partial_acc: torch.Tensor, partial_m: torch.Tensor, partial_l: torch.Tensor,
-                         layout: str = TOKEN_MAJOR) -> None:
-    """Phase 1 of split-K decode into caller-allocated partials (asynchronous)."""
+                         layout: str = TOKEN_MAJOR, kv_cache_dtype: str = "auto", k_scale: float = 1.0,
+                         v_scale: float = 1.0, alibi_slopes: Optional[torch.Tensor] = None) -> None:
+    """Phase 1 of split-K decode into caller-allocated partials (asynchronous).
+
+    Cache options (the C paged_decode_partial_ex): ``kv_cache_dtype`` "fp8" / "fp8_e4m3"
+    for torch.float8_e4m3fn caches, whose keys and values are k_scale and v_scale times the
+    stored values; ``alibi_slopes`` [H] float32 adds the ALiBi bias -slope_h (len - 1 - t)."""
+    kv_code, kv_dtype = _cache_options(query, kv_cache_dtype, k_scale, v_scale, alibi_slopes)
     S, H, D, nb, bs = _check_decode_inputs(query, key_cache, value_cache, block_tables, seq_lens,
-                                           num_kv_heads, layout)
+                                           num_kv_heads, layout, kv_dtype)
     P = _check_partials(partial_acc, partial_m, partial_l, S, H, D)
+    if kv_code is not None:
+        st = lib().paged_decode_partial_ex(
+            _ptr(query), _DTYPE[query.dtype], _ptr(key_cache), _ptr(value_cache), _LAYOUT[layout], kv_code,
+            float(k_scale), float(v_scale), _ptr(alibi_slopes), _ptr(block_tables), block_tables.shape[1],
+            _ptr(seq_lens), S, H, num_kv_heads, D, bs, nb, float(scale), int(partition_size), 0, P,
+            int(max_seq_len), _ptr(partial_acc), _ptr(partial_m), _ptr(partial_l), _stream(query.device))
+        _check(st, "paged_decode_partial_ex")
+        return
     st = lib().paged_decode_partial(
         _ptr(query), _DTYPE[query.dtype], _ptr(key_cache), _ptr(value_cache), _LAYOUT[layout],
         _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, H, num_kv_heads, D, bs, nb,
@@ -215,12 +256,22 @@ def paged_decode_split_partial(query: torch.Tensor, key_cache: torch.Tensor, val
                                block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
                                num_kv_heads: int, max_seq_len: int, partial_acc: torch.Tensor,
                                partial_m: torch.Tensor, partial_l: torch.Tensor,
-                               layout: str = TOKEN_MAJOR) -> None:
+                               layout: str = TOKEN_MAJOR, kv_cache_dtype: str = "auto", k_scale: float = 1.0,
+                               v_scale: float = 1.0, alibi_slopes: Optional[torch.Tensor] = None) -> None:
     """Phase 1 with NUM_SPLITS page-aligned splits per sequence; num_splits is the partition
-    axis of the partials (asynchronous)."""
+    axis of the partials (asynchronous). Cache options as in paged_decode_partial."""
+    kv_code, kv_dtype = _cache_options(query, kv_cache_dtype, k_scale, v_scale, alibi_slopes)
     S, H, D, nb, bs = _check_decode_inputs(query, key_cache, value_cache, block_tables, seq_lens,
-                                           num_kv_heads, layout)
+                                           num_kv_heads, layout, kv_dtype)
     ns = _check_partials(partial_acc, partial_m, partial_l, S, H, D)
+    if kv_code is not None:
+        st = lib().paged_decode_partial_ex(
+            _ptr(query), _DTYPE[query.dtype], _ptr(key_cache), _ptr(value_cache), _LAYOUT[layout], kv_code,
+            float(k_scale), float(v_scale), _ptr(alibi_slopes), _ptr(block_tables), block_tables.shape[1],
+            _ptr(seq_lens), S, H, num_kv_heads, D, bs, nb, float(scale), 0, ns, ns, int(max_seq_len),
+            _ptr(partial_acc), _ptr(partial_m), _ptr(partial_l), _stream(query.device))
+        _check(st, "paged_decode_partial_ex")
+        return
     st = lib().paged_decode_split_partial(
         _ptr(query), _DTYPE[query.dtype], _ptr(key_cache), _ptr(value_cache), _LAYOUT[layout],
         _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, H, num_kv_heads, D, bs, nb,
@@ -282,13 +333,17 @@ def paged_decode_into(query: torch.Tensor, key_cache: torch.Tensor, value_cache:
                       partition_size: int, num_splits: int, max_seq_len: int, out: torch.Tensor,
                       lse: Optional[torch.Tensor] = None, partial_acc: Optional[torch.Tensor] = None,
                       partial_m: Optional[torch.Tensor] = None, partial_l: Optional[torch.Tensor] = None,
-                      counters: Optional[torch.Tensor] = None, layout: str = TOKEN_MAJOR) -> None:
+                      counters: Optional[torch.Tensor] = None, layout: str = TOKEN_MAJOR,
+                      kv_cache_dtype: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0,
+                      alibi_slopes: Optional[torch.Tensor] = None) -> None:
     """The one-launch C ``paged_decode`` into caller-allocated buffers (asynchronous).
 
     With partials of one partition (or none) it is the single pass; otherwise ``counters``
-    ([S * num_kv_heads] int32) must be zero and is left zero."""
+    ([S * num_kv_heads] int32) must be zero and is left zero. Cache options as in
+    paged_decode_partial (the C paged_decode_ex)."""
+    kv_code, kv_dtype = _cache_options(query, kv_cache_dtype, k_scale, v_scale, alibi_slopes)
     S, H, D, nb, bs = _check_decode_inputs(query, key_cache, value_cache, block_tables, seq_lens,
-                                           num_kv_heads, layout)
+                                           num_kv_heads, layout, kv_dtype)
     _dev("out", out, query.dtype, 3)
     if tuple(out.shape) != (S, H, D):
         raise ValueError("out must be [S, H, D]")
@@ -304,6 +359,15 @@ def paged_decode_into(query: torch.Tensor, key_cache: torch.Tensor, value_cache:
         _dev("counters", counters, torch.int32, 1)
         if counters.numel() < S * num_kv_heads:
             raise ValueError("counters must hold num_seqs * num_kv_heads int32")
+    if kv_code is not None:
+        st = lib().paged_decode_ex(
+            _ptr(query), _DTYPE[query.dtype], _ptr(key_cache), _ptr(value_cache), _LAYOUT[layout], kv_code,
+            float(k_scale), float(v_scale), _ptr(alibi_slopes), _ptr(block_tables), block_tables.shape[1],
+            _ptr(seq_lens), S, H, num_kv_heads, D, bs, nb, float(scale), int(partition_size), int(num_splits), P,
+            int(max_seq_len), _ptr(partial_acc), _ptr(partial_m), _ptr(partial_l), _ptr(counters), _ptr(out),
+            _ptr(lse), _stream(query.device))
+        _check(st, "paged_decode_ex")
+        return
     st = lib().paged_decode(
         _ptr(query), _DTYPE[query.dtype], _ptr(key_cache), _ptr(value_cache), _LAYOUT[layout],
         _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, H, num_kv_heads, D, bs, nb,
@@ -342,7 +406,8 @@ def paged_decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torc
                  partition_size: int = 512, layout: str = TOKEN_MAJOR,
                  max_seq_len: Optional[int] = None, return_lse: bool = False,
                  max_num_partitions: Optional[int] = None, num_splits: int = 0,
-                 one_launch: Optional[bool] = None):
+                 one_launch: Optional[bool] = None, kv_cache_dtype: str = "auto", k_scale: float = 1.0,
+                 v_scale: float = 1.0, alibi_slopes: Optional[torch.Tensor] = None):
     """Decode attention for one new token per sequence; returns ``out`` [S, H, D] in the
     query dtype, or ``(out, lse)``.
 
@@ -352,8 +417,10 @@ def paged_decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torc
     phases run as separate launches. By default (None) one launch is used only when every
     sequence fits one partition (the single pass): with several partitions the launch's
     cross-workgroup combine costs more on MI355X than the second launch it saves.
-    ``max_seq_len`` defaults to ``seq_lens.max()`` (one device-to-host read).
+    ``max_seq_len`` defaults to ``seq_lens.max()`` (one device-to-host read). Cache options
+    (float8 caches with their scales, ALiBi slopes) as in paged_decode_partial.
     """
+    opts = dict(kv_cache_dtype=kv_cache_dtype, k_scale=k_scale, v_scale=v_scale, alibi_slopes=alibi_slopes)
     if max_seq_len is None:
         max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0
     S, H, D = query.shape
@@ -375,14 +442,14 @@ def paged_decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torc
         if P > 1:
             counters = torch.zeros((S * num_kv_heads,), dtype=torch.int32, device=dev)
         paged_decode_into(query, key_cache, value_cache, block_tables, seq_lens, scale, num_kv_heads,
-                          partition_size, num_splits, max_seq_len, out, lse, acc, m, l, counters, layout)
+                          partition_size, num_splits, max_seq_len, out, lse, acc, m, l, counters, layout, **opts)
     elif num_splits > 0:
         paged_decode_split_partial(query, key_cache, value_cache, block_tables, seq_lens, scale, num_kv_heads,
-                                   max_seq_len, acc, m, l, layout=layout)
+                                   max_seq_len, acc, m, l, layout=layout, **opts)
         paged_decode_split_reduce(acc, m, l, seq_lens, _pool_geometry(key_cache, layout)[1], out, lse)
     else:
         paged_decode_partial(query, key_cache, value_cache, block_tables, seq_lens, scale, num_kv_heads,
-                             partition_size, max_seq_len, acc, m, l, layout=layout)
+                             partition_size, max_seq_len, acc, m, l, layout=layout, **opts)
         paged_decode_reduce(acc, m, l, seq_lens, partition_size, out, lse)
     return (out, lse) if return_lse else out
 

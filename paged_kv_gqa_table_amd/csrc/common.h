@@ -59,6 +59,30 @@ PKV_DEVICE uint4 ld16_nt(const void* p) {  // non-temporal: data read once (the 
 // plain read; 4-5 % less phase-1 time at 32 sequences x 2300 tokens).
 PKV_DEVICE uint4 ld16_kv(const void* p) { return ld16_nt(p); }
 
+// float8 e4m3 (OCP) K/V elements as bf16 pairs: every e4m3 value is exactly a bf16 value,
+// so the conversion loses nothing. 8 elements (8 bytes) -> 8 bf16; 4 -> 4.
+PKV_DEVICE uint4 as_bf16x8(const uint4& v) { return v; }
+PKV_DEVICE uint4 as_bf16x8(const uint2& v) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true);
+  return make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]),
+                    pack_bf16x2(d[0], d[1]));
+}
+PKV_DEVICE uint2 as_bf16x4(const uint2& v) { return v; }
+PKV_DEVICE uint2 as_bf16x4(uint32_t v) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v, true);
+  return make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]));
+}
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+PKV_DEVICE uint2 ld8_nt(const void* p) {  // non-temporal 8-byte load (float8 K/V)
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v[0], v[1]);
+}
+PKV_DEVICE uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+
 // ---------------------------------------------------------------- exp2
 PKV_DEVICE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

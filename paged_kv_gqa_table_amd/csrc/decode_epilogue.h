@@ -145,6 +145,17 @@ PKV_DEVICE void reduce_row_wave(const float* acc, const float* pm, const float* 
   if (lse != nullptr && lane == 0) lse[row] = (np > 0) ? (M + __logf(Z)) * lse_scale : kNegInf;
 }
 
+// ALiBi bias (Press, Smith and Lewis, "Train Short, Test Long", ICLR 2022): the score of key
+// t of a sequence of len tokens gets -slope * (len - 1 - t). Inside a partition the kernels
+// add only the partition-relative part -slope * (t_last - t), t_last being the partition's
+// last token, which keeps the scores small and their float32 rounding error relative to
+// them small; the constant rest, -slope * (len - 1 - t_last), shifts the partition's max
+// and nothing else (l and acc are taken relative to that max), so it is added to the
+// stored max once. In base-2 units (the kernels' internal scale).
+PKV_DEVICE float alibi_shift2(const DecodePartialArgs& a, int h, int len, int t_last) {
+  return -a.alibi[h] * kLog2e * (float)(len - 1 - t_last);
+}
+
 // Number of partitions of a sequence of len tokens under the launch's partition map.
 PKV_DEVICE int item_parts(const DecodePartialArgs& a, int len) {
   const int pt = part_tokens(len, a.ps, a.nsplit, 16);

@@ -61,12 +61,18 @@ struct MfmaSmem {
   float red_l[W][16];
 };
 
-template <int D, bool XP, int W, bool FINAL, bool ALIBI>
+// FP8: the K/V pools hold float8 e4m3 values (one byte each, same element order; x-packed
+// keys in 16-element chunks), loaded 8 bytes where bf16 loads 16 and converted exactly to
+// bf16 right before the matrix-core instructions; k_scale is folded into scale_log2 and
+// v_scale multiplies the merged accumulator. ALIBI: scores carry the ALiBi bias
+// (alibi_shift2 in decode_epilogue.h).
+template <int D, bool XP, int W, bool FINAL, bool ALIBI, bool FP8>
 __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const int G, const int b, const int kvh,
                                                const int p, const int len, MfmaSmem<W, D>& sm) {
   constexpr int BS = 16;
-  constexpr int ROWB = D * 2;
-  constexpr int PAGEB = BS * ROWB;
+  constexpr int ROWB = D * 2;                   // bytes of a bf16 query row
+  constexpr int KVROWB = FP8 ? D : ROWB;        // bytes of a K/V token row
+  constexpr int PAGEB = BS * KVROWB;
   constexpr int KS = D / 32;   // k-steps of S^T
   constexpr int NT = D / 16;   // O^T tiles
   constexpr int NB = D / 128;  // 128-dim blocks (token-major V)
@@ -83,6 +89,7 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
   const int pg_begin = p * ppp;
   const int pg_end = min(pg_begin + ppp, npages_seq);
   const int n_my = pg_end - pg_begin - w > 0 ? (pg_end - pg_begin - w + W - 1) / W : 0;
+  const int t_last = min(pg_end * BS, len) - 1;  // the partition's last token (ALiBi reference)
   const int32_t* bt_row = a.bt + (size_t)b * a.mb;
   int pid_cache = 0;
   auto load_ids = [&](int i0) {
@@ -116,34 +123,47 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
     return base + (size_t)id * block_stride;
   };
 
-  uint4 kr[KS];
-  uint4 vt[XP ? 1 : 4][XP ? 1 : NB];  // token-major: tokens 4g+i, chunk 16*blk + hl
-  uint2 vx[XP ? NT : 1];              // x-packed: dim 16 t + hl, tokens 4g .. 4g+3
+  // K/V registers as loaded: 8 elements (16 bytes bf16, 8 bytes float8), or for x-packed V
+  // 4 tokens of one dim (8 bytes bf16, 4 bytes float8); converted to bf16 at use
+  using KV8 = typename std::conditional<FP8, uint2, uint4>::type;
+  using V4 = typename std::conditional<FP8, uint32_t, uint2>::type;
+  KV8 kr[KS];
+  KV8 vt[XP ? 1 : 4][XP ? 1 : NB];  // token-major: tokens 4g+i, chunk 16*blk + hl
+  V4 vx[XP ? NT : 1];               // x-packed: dim 16 t + hl, tokens 4g .. 4g+3
   // Pages are loaded non-temporally, except each wave's last page: the loop refills the
   // registers past the end by re-reading that page (so the loads stay unconditional and
   // need no merge copies), which must then be an L2 hit, not HBM.
-  auto ldkv = [&](auto nt, const char* p) -> uint4 {
-    if constexpr (decltype(nt)::value) return ld16_kv(p);
-    else return ld16(p);
+  auto ldkv = [&](auto nt, const char* p) -> KV8 {
+    if constexpr (FP8) {
+      if constexpr (decltype(nt)::value) return ld8_nt(p);
+      else return ld8(p);
+    } else {
+      if constexpr (decltype(nt)::value) return ld16_kv(p);
+      else return ld16(p);
+    }
+  };
+  // byte offset of the 8 key elements of dims 8c .. 8c + 7 of token t within a page
+  auto k_off = [&](int t, int c) -> int {
+    if constexpr (XP && FP8) return ((c >> 1) * BS + t) * 16 + (c & 1) * 8;
+    else if constexpr (XP) return (c * BS + t) * 16;
+    else return t * KVROWB + c * (FP8 ? 8 : 16);
   };
   auto issue_k = [&](auto nt, int i) {
     const char* kp = page_ptr(kbase, i);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if constexpr (XP) kr[s] = ldkv(nt, kp + ((s * 4 + g) * BS + hl) * 16);  // chunk (dims 32s+8g), token hl
-      else kr[s] = ldkv(nt, kp + hl * ROWB + (s * 32 + g * 8) * 2);
-    }
+    for (int s = 0; s < KS; ++s) kr[s] = ldkv(nt, kp + k_off(hl, 4 * s + g));  // dims 32s+8g.., token hl
   };
   auto issue_v = [&](auto nt, int i) {
     const char* vp = page_ptr(vbase, i);
     if constexpr (XP) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) vx[t] = *reinterpret_cast<const uint2*>(vp + ((16 * t + hl) * BS + 4 * g) * 2);
+      for (int t = 0; t < NT; ++t)
+        vx[t] = *reinterpret_cast<const V4*>(vp + ((16 * t + hl) * BS + 4 * g) * (FP8 ? 1 : 2));
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int k = 0; k < NB; ++k) vt[j][k] = ldkv(nt, vp + (4 * g + j) * ROWB + (16 * k + hl) * 16);
+        for (int k = 0; k < NB; ++k) vt[j][k] = ldkv(nt, vp + (4 * g + j) * KVROWB + (16 * k + hl) * (FP8 ? 8 : 16));
     }
   };
 
@@ -165,7 +185,7 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
 
     f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < KS; ++s) st = mfma_k32(kr[s], qb[s], st);
+    for (int s = 0; s < KS; ++s) st = mfma_k32(as_bf16x8(kr[s]), qb[s], st);
     issue_k(nt, more ? i + 1 : i);
 
     float x[4];
@@ -173,7 +193,7 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float xv = st[j] * a.scale_log2;
-      if constexpr (ALIBI) xv = fmaf(slope2, (float)(pg * BS + 4 * g + j - (len - 1)), xv);
+      if constexpr (ALIBI) xv = fmaf(slope2, (float)(pg * BS + 4 * g + j - t_last), xv);
       x[j] = (4 * g + j < ntok) ? xv : kNegInf;
       tmax = fmaxf(tmax, x[j]);
     }
@@ -199,34 +219,46 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
     }
     const uint2 pb = make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
 
+    // V as bf16 (a conversion under FP8, a plain copy otherwise)
+    uint2 vxb[XP ? NT : 1];
+    uint4 vtb[XP ? 1 : 4][XP ? 1 : NB];
+    if constexpr (XP) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) vxb[t] = as_bf16x4(vx[t]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int k = 0; k < NB; ++k) vtb[j][k] = as_bf16x8(vt[j][k]);
+    }
     if (ntok < BS) {  // tail page: zero V of invalid tokens (their slots may hold NaN)
       if constexpr (XP) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const int t0 = 4 * g;
-          uint32_t lo = vx[t].x, hi = vx[t].y;
+          uint32_t lo = vxb[t].x, hi = vxb[t].y;
           lo = (t0 >= ntok) ? 0u : (t0 + 1 >= ntok ? (lo & 0xffffu) : lo);
           hi = (t0 + 2 >= ntok) ? 0u : (t0 + 3 >= ntok ? (hi & 0xffffu) : hi);
-          vx[t] = make_uint2(lo, hi);
+          vxb[t] = make_uint2(lo, hi);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           if (4 * g + j >= ntok)
 #pragma unroll
-            for (int k = 0; k < NB; ++k) vt[j][k] = make_uint4(0, 0, 0, 0);
+            for (int k = 0; k < NB; ++k) vtb[j][k] = make_uint4(0, 0, 0, 0);
       }
     }
 
     if constexpr (XP) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] = mfma_k16(vx[t], pb, acc[t]);
+      for (int t = 0; t < NT; ++t) acc[t] = mfma_k16(vxb[t], pb, acc[t]);
     } else {
 #pragma unroll
       for (int k = 0; k < NB; ++k)
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-          const uint2 av = make_uint2(pick_pair(vt[0][k], vt[1][k], n), pick_pair(vt[2][k], vt[3][k], n));
+          const uint2 av = make_uint2(pick_pair(vtb[0][k], vtb[1][k], n), pick_pair(vtb[2][k], vtb[3][k], n));
           acc[k * 8 + n] = mfma_k16(av, pb, acc[k * 8 + n]);
         }
     }
@@ -272,6 +304,8 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
       o = fmaf(f, sm.red_acc[v][h][d], o);
       L = fmaf(f, sm.red_l[v][h], L);
     }
+    if constexpr (FP8) o *= a.v_scale;
+    if constexpr (ALIBI) M += alibi_shift2(a, kvh * G + h, len, t_last);  // after the weights
     store_item_value<D, true, FINAL>(a, bh0 + h, p, d, o, M, L, single);
   }
   __syncthreads();
@@ -286,7 +320,7 @@ __device__ __forceinline__ void mfma_partition(const DecodePartialArgs& a, const
 template <int D, bool FINAL>
 constexpr int mfma_min_waves() { return (D <= 128 && !FINAL) ? 4 : 1; }
 
-template <int D, bool XP, int W, bool DENSE, bool FINAL, bool ALIBI>
+template <int D, bool XP, int W, bool DENSE, bool FINAL, bool ALIBI, bool FP8>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(mfma_min_waves<D, FINAL>())))
 void decode_partial_mfma_kernel(DecodePartialArgs a, int G, int grid_parts) {
   __shared__ MfmaSmem<W, D> sm;
@@ -304,7 +338,7 @@ void decode_partial_mfma_kernel(DecodePartialArgs a, int G, int grid_parts) {
       p = uniform(p);
       int len = a.lens[b];
       len = len > a.len_cap ? a.len_cap : len;
-      mfma_partition<D, XP, W, FINAL, ALIBI>(a, G, b, kvh, p, uniform(len), sm);
+      mfma_partition<D, XP, W, FINAL, ALIBI, FP8>(a, G, b, kvh, p, uniform(len), sm);
     }
   } else {
     const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -320,32 +354,39 @@ void decode_partial_mfma_kernel(DecodePartialArgs a, int G, int grid_parts) {
         if (p == 0) write_empty_rows<D, true>(a, b, kvh, G);
       return;
     }
-    mfma_partition<D, XP, W, FINAL, ALIBI>(a, G, b, kvh, p, len, sm);
+    mfma_partition<D, XP, W, FINAL, ALIBI, FP8>(a, G, b, kvh, p, len, sm);
   }
 }
 
-template <int D, bool XP, bool FINAL, bool ALIBI>
+template <int D, bool XP, bool FINAL, bool ALIBI, bool FP8>
 hipError_t launch_mfma_f(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
   constexpr int W = 4;
   if (use_dense_worklist(a.S, a.KVH, grid_parts)) {
     const long upper = (long)a.S * a.KVH * grid_parts;
     const int grid = (int)(upper < dense_grid_cap() ? upper : dense_grid_cap());
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, true, FINAL, ALIBI>), dim3(grid), dim3(64 * W),
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, true, FINAL, ALIBI, FP8>), dim3(grid), dim3(64 * W),
                        worklist_lds_words(a.S) * sizeof(int), s, a, G, grid_parts);
   } else {
     dim3 grid(grid_parts, a.KVH, a.S);
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, false, FINAL, ALIBI>), grid, dim3(64 * W), 0, s, a, G,
-                       grid_parts);
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, false, FINAL, ALIBI, FP8>), grid, dim3(64 * W), 0, s, a,
+                       G, grid_parts);
   }
   return hipGetLastError();
 }
 
+template <int D, bool XP, bool FINAL>
+hipError_t launch_mfma_fin(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
+  if (a.kv_fp8)
+    return a.alibi != nullptr ? launch_mfma_f<D, XP, FINAL, true, true>(a, G, grid_parts, s)
+                              : launch_mfma_f<D, XP, FINAL, false, true>(a, G, grid_parts, s);
+  return a.alibi != nullptr ? launch_mfma_f<D, XP, FINAL, true, false>(a, G, grid_parts, s)
+                            : launch_mfma_f<D, XP, FINAL, false, false>(a, G, grid_parts, s);
+}
+
 template <int D, bool XP>
 hipError_t launch_mfma_d(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
-  if (a.alibi != nullptr)  // ALiBi: partials only
-    return a.out != nullptr ? hipErrorNotSupported : launch_mfma_f<D, XP, false, true>(a, G, grid_parts, s);
-  return a.out != nullptr ? launch_mfma_f<D, XP, true, false>(a, G, grid_parts, s)
-                          : launch_mfma_f<D, XP, false, false>(a, G, grid_parts, s);
+  return a.out != nullptr ? launch_mfma_fin<D, XP, true>(a, G, grid_parts, s)
+                          : launch_mfma_fin<D, XP, false>(a, G, grid_parts, s);
 }
 
 template <bool XP>

@@ -1,4 +1,4 @@
-// Split-K paged decode, phase 1, on the vector ALUs (query-head groups G <= 8).
+// Split-K paged decode, phase 1, float32, on the vector ALUs (query-head groups G <= 8).
 //
 // What it computes is the per-partition online softmax of the PagedAttention V2 Triton
 // page (_partition_attn_kernel) with the unnormalized accumulator of the flash-decode
@@ -19,12 +19,10 @@
 //    is a scalar branch, skipped whenever a page does not raise the max.
 //  * Scores are kept in base 2 (scale * log2 e folded once), so exp is one v_exp_f32; the
 //    stored m is converted back to natural-log units.
-//  * bf16: q.K uses v_dot2c_f32_bf16 on raw bf16 pairs; P.V uses the same instruction on P
-//    rounded to bf16 by v_cvt_pk_bf16_f32 (both decode pages also round P to the V type
-//    before their P.V product). f32: plain FMAs and f32 P.
+//  * Plain float32 FMAs and float32 P (no rounding of P, so the 1e-5 bound holds).
 //  * Token-major V has K's lane layout, so P never leaves the lane. x-packed V ([D][16] per
-//    page) is read linearly (lane i takes 16-byte chunk i: one d, 8 (bf16) or 4 (f32)
-//    consecutive tokens) and P reaches it through a per-wave LDS row.
+//    page) is read linearly (lane i takes 16-byte chunk i: one d, 4 consecutive tokens)
+//    and P reaches it through a per-wave LDS row.
 //  * Page ids are cached one per lane (lane j: the wave's j-th page) and broadcast with
 //    v_readlane, so the page loop issues no dependent vector loads. Single register buffer
 //    with early re-issue: the next page's K loads leave as soon as the current scores are
@@ -42,11 +40,11 @@ namespace pkv {
 
 constexpr float kRebase = 8.f;  // log2 headroom of the lazy softmax rescale
 
-template <bool BF16, int D, int G, bool XP, int LPT, int W>
+template <int D, int G, bool XP, int LPT, int W>
 struct ValuCfg {
   static constexpr int BS = 16;
-  static constexpr int E = BF16 ? 8 : 4;      // elements per 16-byte chunk
-  static constexpr int EB = BF16 ? 2 : 4;     // bytes per element
+  static constexpr int E = 4;                 // float32 elements per 16-byte chunk
+  static constexpr int EB = 4;                // bytes per element
   static constexpr int ROWB = D * EB;         // bytes of one token's K (or V) row
   static constexpr int NC = ROWB / 16;        // chunks per token row
   static constexpr int CPL = NC / LPT;        // chunks per lane per token
@@ -59,7 +57,7 @@ struct ValuCfg {
   static constexpr int NACC = XP ? NVC : CPL * E;
   static constexpr int NVREG = XP ? NVC : TPL * CPL;
   static_assert(NC % LPT == 0 && CPL >= 1, "row must split evenly over LPT lanes");
-  static_assert(TPL >= 1 && (!BF16 || XP || TPL % 2 == 0), "token pairs for bf16 P.V");
+  static_assert(TPL >= 1, "at least one token per lane and page");
   static_assert(!XP || NVC >= 1, "x-packed V needs at least one chunk per lane");
 };
 
@@ -74,10 +72,10 @@ struct ValuSmem {
 };
 
 // One work item: partials of (b, kvh, p) for the G heads of kv head kvh.
-template <bool BF16, int D, int G, bool XP, int LPT, int W, bool FINAL, bool ALIBI>
+template <int D, int G, bool XP, int LPT, int W, bool FINAL, bool ALIBI>
 __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const int b, const int kvh,
                                                const int p, const int len, ValuSmem<W, G, D, XP>& sm) {
-  using C = ValuCfg<BF16, D, G, XP, LPT, W>;
+  using C = ValuCfg<D, G, XP, LPT, W>;
   constexpr int BS = C::BS, E = C::E, ROWB = C::ROWB, CPL = C::CPL, TPI = C::TPI, TPL = C::TPL;
   constexpr int PAGEB = C::PAGEB, TPC = C::TPC, CPD = C::CPD, NVC = C::NVC, NACC = C::NACC;
 
@@ -93,6 +91,7 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
   const int pg_end = min(pg_begin + ppp, npages_seq);
   // pages of this wave: pg_begin + w + W * i, i < n_my
   const int n_my = pg_end - pg_begin - w > 0 ? (pg_end - pg_begin - w + W - 1) / W : 0;
+  const int t_last = min(pg_end * BS, len) - 1;  // the partition's last token (ALiBi reference)
   const int32_t* bt_row = a.bt + (size_t)b * a.mb;
 
   int pid_cache = 0;
@@ -203,17 +202,10 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
 #pragma unroll
         for (int k = 0; k < CPL; ++k) {
           const uint4 kv = kr[j][k];
-          if constexpr (BF16) {
-            d0 = dot2_bf16(qv[k].x, kv.x, d0);
-            d1 = dot2_bf16(qv[k].y, kv.y, d1);
-            d0 = dot2_bf16(qv[k].z, kv.z, d0);
-            d1 = dot2_bf16(qv[k].w, kv.w, d1);
-          } else {
-            d0 = fmaf(__uint_as_float(qv[k].x), __uint_as_float(kv.x), d0);
-            d1 = fmaf(__uint_as_float(qv[k].y), __uint_as_float(kv.y), d1);
-            d0 = fmaf(__uint_as_float(qv[k].z), __uint_as_float(kv.z), d0);
-            d1 = fmaf(__uint_as_float(qv[k].w), __uint_as_float(kv.w), d1);
-          }
+          d0 = fmaf(__uint_as_float(qv[k].x), __uint_as_float(kv.x), d0);
+          d1 = fmaf(__uint_as_float(qv[k].y), __uint_as_float(kv.y), d1);
+          d0 = fmaf(__uint_as_float(qv[k].z), __uint_as_float(kv.z), d0);
+          d1 = fmaf(__uint_as_float(qv[k].w), __uint_as_float(kv.w), d1);
         }
         s[g][j] = d0 + d1;
       }
@@ -229,7 +221,7 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
         const float v = group_sum<LPT>(s[g][j]);
         float x = v * a.scale_log2;
         if constexpr (ALIBI)
-          x = fmaf(a.alibi[kvh * G + g] * kLog2e, (float)(pg * BS + tg + TPI * j - (len - 1)), x);
+          x = fmaf(a.alibi[kvh * G + g] * kLog2e, (float)(pg * BS + tg + TPI * j - t_last), x);
         s[g][j] = (tg + TPI * j < ntok) ? x : kNegInf;
       }
 
@@ -270,44 +262,18 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
 #pragma unroll
             for (int k = 0; k < CPL; ++k) vr[j * CPL + k] = make_uint4(0, 0, 0, 0);
       }
-      if constexpr (BF16) {
-        // token pairs (j, j+1): pair elements of the two tokens and use dot2 over them
 #pragma unroll
-        for (int j = 0; j < TPL; j += 2) {
-          uint32_t pp[G];
+      for (int j = 0; j < TPL; ++j)
 #pragma unroll
-          for (int g = 0; g < G; ++g) pp[g] = pack_bf16x2(pr[g][j], pr[g][j + 1]);
+        for (int k = 0; k < CPL; ++k) {
+          const uint4 v = vr[j * CPL + k];
+          const float f[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                              __uint_as_float(v.w)};
 #pragma unroll
-          for (int k = 0; k < CPL; ++k) {
-            const uint4 va = vr[j * CPL + k], vb = vr[(j + 1) * CPL + k];
-            const uint32_t ua[4] = {va.x, va.y, va.z, va.w};
-            const uint32_t ub[4] = {vb.x, vb.y, vb.z, vb.w};
+          for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t lo = pair_lo(ua[e], ub[e]);
-              const uint32_t hi = pair_hi(ua[e], ub[e]);
-#pragma unroll
-              for (int g = 0; g < G; ++g) {
-                acc[g][k * E + 2 * e] = dot2_bf16(pp[g], lo, acc[g][k * E + 2 * e]);
-                acc[g][k * E + 2 * e + 1] = dot2_bf16(pp[g], hi, acc[g][k * E + 2 * e + 1]);
-              }
-            }
-          }
+            for (int g = 0; g < G; ++g) acc[g][k * E + e] = fmaf(pr[g][j], f[e], acc[g][k * E + e]);
         }
-      } else {
-#pragma unroll
-        for (int j = 0; j < TPL; ++j)
-#pragma unroll
-          for (int k = 0; k < CPL; ++k) {
-            const uint4 v = vr[j * CPL + k];
-            const float f[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                                __uint_as_float(v.w)};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-              for (int g = 0; g < G; ++g) acc[g][k * E + e] = fmaf(pr[g][j], f[e], acc[g][k * E + e]);
-          }
-      }
     } else {
       // publish P to the wave's LDS row: p_lds[w][g][token]
       if (c == 0) {
@@ -324,13 +290,8 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
           uint32_t x[4] = {vr[q].x, vr[q].y, vr[q].z, vr[q].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            if constexpr (BF16) {
-              const int t = u * TPC + 2 * e;
-              x[e] = (t >= ntok) ? 0u : (t + 1 >= ntok ? (x[e] & 0xffffu) : x[e]);
-            } else {
-              const int t = u * TPC + e;
-              x[e] = (t >= ntok) ? 0u : x[e];
-            }
+            const int t = u * TPC + e;
+            x[e] = (t >= ntok) ? 0u : x[e];
           }
           vr[q] = make_uint4(x[0], x[1], x[2], x[3]);
         }
@@ -338,28 +299,14 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float4 pf = *reinterpret_cast<const float4*>(&sm.p_lds[w][g][u * TPC]);
-        if constexpr (BF16) {
-          const float4 pf2 = *reinterpret_cast<const float4*>(&sm.p_lds[w][g][u * TPC + 4]);
-          const uint32_t p01 = pack_bf16x2(pf.x, pf.y), p23 = pack_bf16x2(pf.z, pf.w);
-          const uint32_t p45 = pack_bf16x2(pf2.x, pf2.y), p67 = pack_bf16x2(pf2.z, pf2.w);
 #pragma unroll
-          for (int q = 0; q < NVC; ++q) {
-            float t0 = dot2_bf16(p01, vr[q].x, acc[g][q]);
-            float t1 = dot2_bf16(p23, vr[q].y, 0.f);
-            t0 = dot2_bf16(p45, vr[q].z, t0);
-            t1 = dot2_bf16(p67, vr[q].w, t1);
-            acc[g][q] = t0 + t1;
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < NVC; ++q) {
-            float t = acc[g][q];
-            t = fmaf(pf.x, __uint_as_float(vr[q].x), t);
-            t = fmaf(pf.y, __uint_as_float(vr[q].y), t);
-            t = fmaf(pf.z, __uint_as_float(vr[q].z), t);
-            t = fmaf(pf.w, __uint_as_float(vr[q].w), t);
-            acc[g][q] = t;
-          }
+        for (int q = 0; q < NVC; ++q) {
+          float t = acc[g][q];
+          t = fmaf(pf.x, __uint_as_float(vr[q].x), t);
+          t = fmaf(pf.y, __uint_as_float(vr[q].y), t);
+          t = fmaf(pf.z, __uint_as_float(vr[q].z), t);
+          t = fmaf(pf.w, __uint_as_float(vr[q].w), t);
+          acc[g][q] = t;
         }
       }
       wave_lds_fence();  // this page's P reads finish before the next page overwrites it
@@ -425,14 +372,15 @@ __device__ __forceinline__ void valu_partition(const DecodePartialArgs& a, const
       o = fmaf(f, sm.red_acc[v][g][d], o);
       L = fmaf(f, sm.red_l[v][g], L);
     }
-    store_item_value<D, BF16>(a, bh0 + g, p, d, o, M, L, single);
+    if constexpr (ALIBI) M += alibi_shift2(a, kvh * G + g, len, t_last);  // after the weights
+    store_item_value<D, false, FINAL>(a, bh0 + g, p, d, o, M, L, single);
   }
   __syncthreads();  // LDS is reused by the next item
   if constexpr (FINAL)
-    if (nparts > 1) finish_item_fused<D, BF16, W>(a, b, kvh, G, nparts);
+    if (nparts > 1) finish_item_fused<D, false, W>(a, b, kvh, G, nparts);
 }
 
-template <bool BF16, int D, int G, bool XP, int LPT, int W, bool DENSE, int WPE, bool FINAL, bool ALIBI>
+template <int D, int G, bool XP, int LPT, int W, bool DENSE, int WPE, bool FINAL, bool ALIBI>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(WPE, 8))) void decode_partial_valu_kernel(DecodePartialArgs a, int grid_parts) {
   __shared__ ValuSmem<W, G, D, XP> sm;
   if constexpr (DENSE) {
@@ -440,7 +388,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(WPE, 8))
     __shared__ int s_wave[2 * W];
     const DenseItems it = build_worklist<64 * W>(a.lens, a.S, a.len_cap, a.ps, a.nsplit, a.KVH, s_worklist, s_wave);
     write_sentinels(it, a.H, grid_parts, a.P, a.m, a.l);
-    if constexpr (FINAL) write_empty_outputs<D, BF16>(it, a);
+    if constexpr (FINAL) write_empty_outputs<D, false>(it, a);
     for (int item = blockIdx.x; item < it.n_items; item += gridDim.x) {
       int b, kvh, p;
       decode_item(it, item, b, kvh, p);
@@ -449,7 +397,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(WPE, 8))
       p = uniform(p);
       int len = a.lens[b];
       len = len > a.len_cap ? a.len_cap : len;
-      valu_partition<BF16, D, G, XP, LPT, W, FINAL, ALIBI>(a, b, kvh, p, uniform(len), sm);
+      valu_partition<D, G, XP, LPT, W, FINAL, ALIBI>(a, b, kvh, p, uniform(len), sm);
     }
   } else {
     const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -463,16 +411,16 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(WPE, 8))
         a.l[si] = 0.f;
       }
       if constexpr (FINAL)
-        if (p == 0) write_empty_rows<D, BF16>(a, b, kvh, G);
+        if (p == 0) write_empty_rows<D, false>(a, b, kvh, G);
       return;
     }
-    valu_partition<BF16, D, G, XP, LPT, W, FINAL, ALIBI>(a, b, kvh, p, len, sm);
+    valu_partition<D, G, XP, LPT, W, FINAL, ALIBI>(a, b, kvh, p, len, sm);
   }
 }
 
-template <bool BF16, bool XP, int D, int G, bool FINAL, bool ALIBI>
+template <bool XP, int D, int G, bool FINAL, bool ALIBI>
 hipError_t launch_valu_fin(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
-  constexpr int EB = BF16 ? 2 : 4;
+  constexpr int EB = 4;
 #ifndef PKV_VALU_ROW_BYTES_LPT16
 #define PKV_VALU_ROW_BYTES_LPT16 256
 #endif
@@ -486,47 +434,48 @@ hipError_t launch_valu_fin(const DecodePartialArgs& a, int grid_parts, hipStream
   if (use_dense_worklist(a.S, a.KVH, grid_parts)) {
     const long upper = (long)a.S * a.KVH * grid_parts;
     const int grid = (int)(upper < dense_grid_cap() ? upper : dense_grid_cap());
-    hipLaunchKernelGGL((decode_partial_valu_kernel<BF16, D, G, XP, LPT, W, true, WPE, FINAL, ALIBI>), dim3(grid), dim3(64 * W),
+    hipLaunchKernelGGL((decode_partial_valu_kernel<D, G, XP, LPT, W, true, WPE, FINAL, ALIBI>), dim3(grid), dim3(64 * W),
                        worklist_lds_words(a.S) * sizeof(int), s, a, grid_parts);
   } else {
     dim3 grid(grid_parts, a.KVH, a.S);
-    hipLaunchKernelGGL((decode_partial_valu_kernel<BF16, D, G, XP, LPT, W, false, WPE, FINAL, ALIBI>), grid, dim3(64 * W), 0,
+    hipLaunchKernelGGL((decode_partial_valu_kernel<D, G, XP, LPT, W, false, WPE, FINAL, ALIBI>), grid, dim3(64 * W), 0,
                        s, a, grid_parts);
   }
   return hipGetLastError();
 }
 
-template <bool BF16, bool XP, int D, int G>
+template <bool XP, int D, int G>
 hipError_t launch_valu_one(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
-  if (a.alibi != nullptr)  // ALiBi: partials only
-    return a.out != nullptr ? hipErrorNotSupported : launch_valu_fin<BF16, XP, D, G, false, true>(a, grid_parts, s);
-  return a.out != nullptr ? launch_valu_fin<BF16, XP, D, G, true, false>(a, grid_parts, s)
-                          : launch_valu_fin<BF16, XP, D, G, false, false>(a, grid_parts, s);
+  if (a.kv_fp8) return hipErrorNotSupported;  // float8 caches are read with a bf16 query
+  if (a.alibi != nullptr)
+    return a.out != nullptr ? launch_valu_fin<XP, D, G, true, true>(a, grid_parts, s)
+                            : launch_valu_fin<XP, D, G, false, true>(a, grid_parts, s);
+  return a.out != nullptr ? launch_valu_fin<XP, D, G, true, false>(a, grid_parts, s)
+                          : launch_valu_fin<XP, D, G, false, false>(a, grid_parts, s);
 }
 
-template <bool BF16, bool XP, int D>
+template <bool XP, int D>
 hipError_t launch_valu_d(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
   switch (G) {
-    case 1: return launch_valu_one<BF16, XP, D, 1>(a, grid_parts, s);
-    case 2: return launch_valu_one<BF16, XP, D, 2>(a, grid_parts, s);
-    case 3: return launch_valu_one<BF16, XP, D, 3>(a, grid_parts, s);
-    case 4: return launch_valu_one<BF16, XP, D, 4>(a, grid_parts, s);
-    case 5: return launch_valu_one<BF16, XP, D, 5>(a, grid_parts, s);
-    case 6: return launch_valu_one<BF16, XP, D, 6>(a, grid_parts, s);
-    case 7: return launch_valu_one<BF16, XP, D, 7>(a, grid_parts, s);
-    case 8: return launch_valu_one<BF16, XP, D, 8>(a, grid_parts, s);
+    case 1: return launch_valu_one<XP, D, 1>(a, grid_parts, s);
+    case 2: return launch_valu_one<XP, D, 2>(a, grid_parts, s);
+    case 3: return launch_valu_one<XP, D, 3>(a, grid_parts, s);
+    case 4: return launch_valu_one<XP, D, 4>(a, grid_parts, s);
+    case 5: return launch_valu_one<XP, D, 5>(a, grid_parts, s);
+    case 6: return launch_valu_one<XP, D, 6>(a, grid_parts, s);
+    case 7: return launch_valu_one<XP, D, 7>(a, grid_parts, s);
+    case 8: return launch_valu_one<XP, D, 8>(a, grid_parts, s);
     default: return hipErrorNotSupported;
   }
 }
 
-template <bool BF16, bool XP>
+template <bool XP>
 hipError_t launch_valu(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
   switch (a.D) {
-    case 64: return launch_valu_d<BF16, XP, 64>(a, G, grid_parts, s);
-    case 128: return launch_valu_d<BF16, XP, 128>(a, G, grid_parts, s);
+    case 64: return launch_valu_d<XP, 64>(a, G, grid_parts, s);
+    case 128: return launch_valu_d<XP, 128>(a, G, grid_parts, s);
     case 256:
-      if constexpr (BF16) return launch_valu_d<BF16, XP, 256>(a, G, grid_parts, s);
-      else return hipErrorNotSupported;
+      return hipErrorNotSupported;
     default: return hipErrorNotSupported;
   }
 }

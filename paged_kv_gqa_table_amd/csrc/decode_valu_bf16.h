@@ -35,22 +35,6 @@ namespace pkv {
 
 constexpr float kRebaseBf16 = 8.f;  // log2 headroom of the lazy softmax re-basing
 
-// 8 K/V elements as bf16 pairs: bf16 as loaded, or 8 float8 e4m3 values converted
-// (every e4m3 value is exactly representable in bf16).
-PKV_DEVICE uint4 as_bf16x8(const uint4& v) { return v; }
-PKV_DEVICE uint4 as_bf16x8(const uint2& v) {
-  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, false);
-  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, true);
-  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false);
-  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true);
-  return make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]),
-                    pack_bf16x2(d[0], d[1]));
-}
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-PKV_DEVICE uint2 ld8_nt(const void* p) {  // non-temporal 8-byte load (float8 K/V)
-  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
-  return make_uint2(v[0], v[1]);
-}
 
 template <int D, bool XP>
 struct Bf16Cfg {
@@ -98,7 +82,7 @@ struct Bf16Smem {
 // page ids of the next item are fetched after its length (one more round trip per item).
 // FINAL: the launch produces the output (final mode of DecodePartialArgs); compiled
 // separately so that the plain partial kernel carries none of its code. ALIBI: scores
-// carry the ALiBi bias (compiled only for the plain partial mode). FP8: the K/V pools hold
+// carry the ALiBi bias (alibi_shift2). FP8: the K/V pools hold
 // float8 e4m3 values (one byte each, same element order; x-packed keys in 16-element
 // chunks), loaded 8 bytes where bf16 loads 16 and converted exactly to bf16 right before
 // use; k_scale is folded into scale_log2 and v_scale multiplies the merged accumulator.
@@ -253,6 +237,7 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
     const int pg_begin = p * ppp;
     const int pg_end = min(pg_begin + ppp, (len + BS - 1) / BS);
     const int n_my = pg_end - pg_begin - w > 0 ? (pg_end - pg_begin - w + W - 1) / W : 0;
+    const int t_last = min(pg_end * BS, len) - 1;  // the partition's last token (ALiBi reference)
     const char* kbase = reinterpret_cast<const char*>(a.kc) + (size_t)kvh * PAGEB;
     const char* vbase = reinterpret_cast<const char*>(a.vc) + (size_t)kvh * PAGEB;
     int cache_base = 0;  // first page (in this wave's order) whose id is in pid_cache
@@ -434,7 +419,7 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
 #pragma unroll
       for (int k = 0; k < NLV; ++k) {
         float x = xs[k] * a.scale_log2;
-        if constexpr (ALIBI) x = fmaf(rs_slope[k], (float)(pg * BS + rs_t - (len - 1)), x);
+        if constexpr (ALIBI) x = fmaf(rs_slope[k], (float)(pg * BS + rs_t - t_last), x);
         if (ntok < BS) x = rs_t < ntok ? x : kNegInf;  // tail page (uniform branch)
         xs[k] = x;
         rs_max[k] = fmaxf(rs_max[k], x);
@@ -619,6 +604,7 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
         L = fmaf(f, sm.red_l[v][g], L);
       }
       if constexpr (FP8) o *= a.v_scale;
+      if constexpr (ALIBI) M += alibi_shift2(a, kvh * G + g, len, t_last);  // after the weights
       store_item_value<D, true, FINAL>(a, bh0 + g, p, d, o, M, L, single);
     }
     __syncthreads();
@@ -703,46 +689,52 @@ hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream
   return hipGetLastError();
 }
 
-template <bool XP, int D, int G>
-hipError_t launch_bf16_g(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
-  const bool fin = a.out != nullptr;
-  if (a.kv_fp8) {  // float8 caches: plain partials only (the PagedAttention V2 interface)
-    if (fin || a.nsplit > 0) return hipErrorNotSupported;
-    return a.alibi != nullptr ? launch_bf16_one<XP, D, G, false, false, true, true>(a, grid_parts, s)
-                              : launch_bf16_one<XP, D, G, false, false, false, true>(a, grid_parts, s);
-  }
-  if (a.alibi != nullptr)  // ALiBi: plain partials only
-    return (fin || a.nsplit > 0) ? hipErrorNotSupported : launch_bf16_one<XP, D, G, false, false, true>(a, grid_parts, s);
-  if (a.nsplit > 0)
-    return fin ? launch_bf16_one<XP, D, G, true, true, false>(a, grid_parts, s)
-               : launch_bf16_one<XP, D, G, true, false, false>(a, grid_parts, s);
-  return fin ? launch_bf16_one<XP, D, G, false, true, false>(a, grid_parts, s)
-             : launch_bf16_one<XP, D, G, false, false, false>(a, grid_parts, s);
+// One mode (SPLIT: NUM_SPLITS partitions; FINAL: the one-launch decode) for every head
+// dim, group size, ALiBi and float8 combination; each mode of each layout is compiled in a
+// translation unit of its own (decode_valu_bf16_<layout>_<mode>.hip) so that the build runs
+// them in parallel.
+template <bool XP, int D, int G, bool SPLIT, bool FINAL>
+hipError_t launch_bf16_gm(const DecodePartialArgs& a, int grid_parts, hipStream_t s) {
+  if (a.kv_fp8)
+    return a.alibi != nullptr ? launch_bf16_one<XP, D, G, SPLIT, FINAL, true, true>(a, grid_parts, s)
+                              : launch_bf16_one<XP, D, G, SPLIT, FINAL, false, true>(a, grid_parts, s);
+  return a.alibi != nullptr ? launch_bf16_one<XP, D, G, SPLIT, FINAL, true, false>(a, grid_parts, s)
+                            : launch_bf16_one<XP, D, G, SPLIT, FINAL, false, false>(a, grid_parts, s);
 }
 
-template <bool XP, int D>
-hipError_t launch_bf16_d(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
+template <bool XP, int D, bool SPLIT, bool FINAL>
+hipError_t launch_bf16_dm(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
   switch (G) {
-    case 1: return launch_bf16_g<XP, D, 1>(a, grid_parts, s);
-    case 2: return launch_bf16_g<XP, D, 2>(a, grid_parts, s);
-    case 3: return launch_bf16_g<XP, D, 3>(a, grid_parts, s);
-    case 4: return launch_bf16_g<XP, D, 4>(a, grid_parts, s);
-    case 5: return launch_bf16_g<XP, D, 5>(a, grid_parts, s);
-    case 6: return launch_bf16_g<XP, D, 6>(a, grid_parts, s);
-    case 7: return launch_bf16_g<XP, D, 7>(a, grid_parts, s);
-    case 8: return launch_bf16_g<XP, D, 8>(a, grid_parts, s);
+    case 1: return launch_bf16_gm<XP, D, 1, SPLIT, FINAL>(a, grid_parts, s);
+    case 2: return launch_bf16_gm<XP, D, 2, SPLIT, FINAL>(a, grid_parts, s);
+    case 3: return launch_bf16_gm<XP, D, 3, SPLIT, FINAL>(a, grid_parts, s);
+    case 4: return launch_bf16_gm<XP, D, 4, SPLIT, FINAL>(a, grid_parts, s);
+    case 5: return launch_bf16_gm<XP, D, 5, SPLIT, FINAL>(a, grid_parts, s);
+    case 6: return launch_bf16_gm<XP, D, 6, SPLIT, FINAL>(a, grid_parts, s);
+    case 7: return launch_bf16_gm<XP, D, 7, SPLIT, FINAL>(a, grid_parts, s);
+    case 8: return launch_bf16_gm<XP, D, 8, SPLIT, FINAL>(a, grid_parts, s);
     default: return hipErrorNotSupported;
   }
 }
 
-template <bool XP>
-hipError_t launch_bf16(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
+template <bool XP, bool SPLIT, bool FINAL>
+hipError_t launch_bf16_mode(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
   switch (a.D) {
-    case 64: return launch_bf16_d<XP, 64>(a, G, grid_parts, s);
-    case 128: return launch_bf16_d<XP, 128>(a, G, grid_parts, s);
-    case 256: return launch_bf16_d<XP, 256>(a, G, grid_parts, s);
+    case 64: return launch_bf16_dm<XP, 64, SPLIT, FINAL>(a, G, grid_parts, s);
+    case 128: return launch_bf16_dm<XP, 128, SPLIT, FINAL>(a, G, grid_parts, s);
+    case 256: return launch_bf16_dm<XP, 256, SPLIT, FINAL>(a, G, grid_parts, s);
     default: return hipErrorNotSupported;
   }
 }
+
+// The per-mode launchers of one layout (defined in the per-mode translation units).
+#define PKV_BF16_MODE_LAUNCHERS(L)                                                                          \
+  hipError_t launch_bf16_##L##_plain(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s);       \
+  hipError_t launch_bf16_##L##_split(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s);       \
+  hipError_t launch_bf16_##L##_final(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s);       \
+  hipError_t launch_bf16_##L##_split_final(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s);
+PKV_BF16_MODE_LAUNCHERS(tm)
+PKV_BF16_MODE_LAUNCHERS(xp)
+#undef PKV_BF16_MODE_LAUNCHERS
 
 }  // namespace pkv

@@ -4,6 +4,6 @@
 
 namespace pkv {
 hipError_t launch_decode_valu_f32_xp(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
-  return launch_valu<false, true>(a, G, grid_parts, s);
+  return launch_valu<true>(a, G, grid_parts, s);
 }
 }  // namespace pkv

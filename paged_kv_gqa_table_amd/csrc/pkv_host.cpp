@@ -121,8 +121,8 @@ struct Phase1Mode {
   void* out;            // final mode when not null
   float* lse;
   int* counters;
-  const float* alibi;   // [num_heads] ALiBi slopes or null (plain partials only)
-  int kv_fp8;           // K/V pools in float8 e4m3 (plain partials only)
+  const float* alibi;   // [num_heads] ALiBi slopes or null
+  int kv_fp8;           // K/V pools in float8 e4m3 (bf16 query)
   float k_scale, v_scale;
 };
 
@@ -213,9 +213,7 @@ int decode_phase1(const char* who, const void* query, int dtype, const void* key
 
   hipError_t e;
   const bool xp = layout == PKV_KV_XPACKED;
-  if (mode.kv_fp8) {
-    e = xp ? pkv::launch_decode_valu_bf16_xp(a, G, grid_parts, s) : pkv::launch_decode_valu_bf16_tm(a, G, grid_parts, s);
-  } else if (bf16 && G >= 8) {
+  if (bf16 && G >= 8) {
     e = xp ? pkv::launch_decode_mfma_bf16_xp(a, G, grid_parts, s)
            : pkv::launch_decode_mfma_bf16_tm(a, G, grid_parts, s);
   } else if (bf16) {
@@ -253,6 +251,20 @@ int decode_phase2(const char* who, const float* partial_acc, const float* partia
   std::string what = std::string(who) + " launch";
   return hip_status(pkv::launch_decode_reduce(a, out_dtype == PKV_BF16, reinterpret_cast<hipStream_t>(stream)),
                     what.c_str());
+}
+
+// The cache options of the _ex entry points and the PagedAttention V2 launcher: the K/V
+// element type (the query's, or float8 e4m3 with a bf16 query) and its dequantization scales.
+int check_cache_options(const char* who, int dtype, int kv_dtype, float k_scale, float v_scale) {
+  if (kv_dtype != dtype && kv_dtype != PKV_FP8_E4M3)
+    return fail(PKV_EINVAL, "%s: kv_dtype %d is neither the query dtype nor PKV_FP8_E4M3", who, kv_dtype);
+  if (!std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PKV_EINVAL, "%s: k_scale / v_scale not finite", who);
+  if (kv_dtype != PKV_FP8_E4M3 && (k_scale != 1.f || v_scale != 1.f))
+    return fail(PKV_EINVAL, "%s: k_scale / v_scale apply to a float8 cache only", who);
+  if (kv_dtype == PKV_FP8_E4M3 && dtype != PKV_BF16)
+    return fail(PKV_EUNSUPPORTED, "%s: a float8 cache needs a bf16 query", who);
+  return PKV_OK;
 }
 
 }  // namespace
@@ -317,6 +329,43 @@ extern "C" int paged_decode(const void* query, int dtype, const void* key_cache,
                        stream);
 }
 
+extern "C" int paged_decode_partial_ex(const void* query, int dtype, const void* key_cache, const void* value_cache,
+                                       int layout, int kv_dtype, float k_scale, float v_scale,
+                                       const float* alibi_slopes, const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* seq_lens, int num_seqs, int num_heads, int num_kv_heads,
+                                       int head_dim, int block_size, int num_blocks, float scale, int partition_size,
+                                       int num_splits, int max_num_partitions, int max_seq_len, float* partial_acc,
+                                       float* partial_m, float* partial_l, void* stream) {
+  const int cst = check_cache_options("paged_decode_partial_ex", dtype, kv_dtype, k_scale, v_scale);
+  if (cst != PKV_OK) return cst;
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3;
+  const Phase1Mode mode{partition_size, num_splits, 0, nullptr, nullptr, nullptr, alibi_slopes, fp8 ? 1 : 0, k_scale,
+                        v_scale};
+  return decode_phase1("paged_decode_partial_ex", query, dtype, key_cache, value_cache, layout, block_tables,
+                       max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, scale, max_num_partitions, max_seq_len, partial_acc, partial_m, partial_l, mode,
+                       stream);
+}
+
+extern "C" int paged_decode_ex(const void* query, int dtype, const void* key_cache, const void* value_cache,
+                               int layout, int kv_dtype, float k_scale, float v_scale, const float* alibi_slopes,
+                               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_lens,
+                               int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                               int num_blocks, float scale, int partition_size, int num_splits,
+                               int max_num_partitions, int max_seq_len, float* partial_acc, float* partial_m,
+                               float* partial_l, int32_t* counters, void* out, float* lse, void* stream) {
+  if (!out) return fail(PKV_EINVAL, "paged_decode_ex: NULL pointer argument (out)");
+  const int cst = check_cache_options("paged_decode_ex", dtype, kv_dtype, k_scale, v_scale);
+  if (cst != PKV_OK) return cst;
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3;
+  const Phase1Mode mode{partition_size, num_splits, 0, out, lse, counters, alibi_slopes, fp8 ? 1 : 0, k_scale,
+                        v_scale};
+  return decode_phase1("paged_decode_ex", query, dtype, key_cache, value_cache, layout, block_tables,
+                       max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, scale, max_num_partitions, max_seq_len, partial_acc, partial_m, partial_l, mode,
+                       stream);
+}
+
 extern "C" int paged_attention_v2(void* out, float* exp_sums, float* max_logits, float* tmp_output,
                                   const void* query, int dtype, const void* key_cache, const void* value_cache,
                                   int num_kv_heads, float scale, const int32_t* block_tables,
@@ -324,17 +373,9 @@ extern "C" int paged_attention_v2(void* out, float* exp_sums, float* max_logits,
                                   int head_size, int block_size, int num_blocks, int max_seq_len,
                                   int max_num_partitions, const float* alibi_slopes, int kv_cache_dtype,
                                   float k_scale, float v_scale, void* stream) {
-  if (kv_cache_dtype != dtype && kv_cache_dtype != PKV_FP8_E4M3)
-    return fail(PKV_EINVAL, "paged_attention_v2: kv_cache_dtype %d is neither the query dtype nor PKV_FP8_E4M3",
-                kv_cache_dtype);
+  const int cst = check_cache_options("paged_attention_v2", dtype, kv_cache_dtype, k_scale, v_scale);
+  if (cst != PKV_OK) return cst;
   const bool fp8 = kv_cache_dtype == PKV_FP8_E4M3;
-  if (!std::isfinite(k_scale) || !std::isfinite(v_scale))
-    return fail(PKV_EINVAL, "paged_attention_v2: k_scale / v_scale not finite");
-  if (!fp8 && (k_scale != 1.f || v_scale != 1.f))
-    return fail(PKV_EINVAL, "paged_attention_v2: k_scale / v_scale apply to a float8 cache only");
-  if (fp8 && (dtype != PKV_BF16 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || num_heads / num_kv_heads > 8))
-    return fail(PKV_EUNSUPPORTED, "paged_attention_v2: a float8 cache needs a bf16 query and at most 8 query heads "
-                "per kv head");
   const Phase1Mode mode{kPagedAttentionV2Partition, 0, 1, nullptr, nullptr, nullptr, alibi_slopes, fp8 ? 1 : 0,
                         k_scale, v_scale};
   int st = decode_phase1("paged_attention_v2", query, dtype, key_cache, value_cache, PKV_KV_XPACKED, block_tables,

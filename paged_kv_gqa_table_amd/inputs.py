@@ -66,15 +66,20 @@ def xpacked_to_token_major(k_xp: torch.Tensor, v_xp: torch.Tensor):
     return k_tm, v_tm
 
 
-def fp8_xpacked_pools(case) -> tuple:
-    """The case's K/V pools cast to float8 e4m3 (torch RNE with the format's range) and laid
-    out x-packed with x = 16: the float8 cache the PagedAttention V2 interface reads."""
+def fp8_pools(case, layout: str) -> tuple:
+    """The case's K/V pools cast to float8 e4m3 (torch RNE with the format's range), laid out
+    token-major or x-packed with x = 16 (one byte per element)."""
     k, v = case.key_cache, case.value_cache
     if case.layout == XPACKED:
         k, v = xpacked_to_token_major(k, v)
     k8 = k.to(torch.float32).to(torch.float8_e4m3fn)
     v8 = v.to(torch.float32).to(torch.float8_e4m3fn)
-    return token_major_to_xpacked(k8, v8)
+    return token_major_to_xpacked(k8, v8) if layout == XPACKED else (k8.contiguous(), v8.contiguous())
+
+
+def fp8_xpacked_pools(case) -> tuple:
+    """The float8 cache the PagedAttention V2 interface reads: x-packed, x = 16."""
+    return fp8_pools(case, XPACKED)
 
 
 @dataclasses.dataclass

@@ -198,7 +198,7 @@ def test_paged_attention_v2_validation(L):
     assert call(kv_dtype=0) == EINVAL           # an f32 cache under a bf16 query
     assert call(ks=2.0) == EINVAL               # scales belong to a float8 cache
     assert call(kv_dtype=2, dtype=0) == EUNSUP  # a float8 cache needs a bf16 query
-    assert call(kv_dtype=2, H=32) == EUNSUP     # ... and at most 8 query heads per kv head
+    assert call(kv_dtype=2, H=36) == EUNSUP     # ... and at most 16 query heads per kv head
     with pytest.raises(NotImplementedError):
         pkv.paged_attention_v2(None, None, None, None, None, None, None, 2, 0.1, None, None, 16, 0,
                                kv_cache_dtype="int4")
@@ -226,3 +226,29 @@ def test_mla_decode_validation(L):
     assert call(acc=None) == EINVAL
     assert call(num_pages=0) == EINVAL
     assert call(batch=0) == OK
+
+
+def test_cache_option_entry_points_validation(L):
+    """paged_decode_partial_ex / paged_decode_ex: the cache options are checked before any
+    launch (every call below fails validation or is an empty batch)."""
+    def part(kv_dtype=1, ks=1.0, vs=1.0, dtype=1, S=2, H=8, kvh=2, ns=0, ps=512, P=1, mx=512):
+        return L.paged_decode_partial_ex(FAKE, dtype, FAKE, FAKE, 0, kv_dtype, ks, vs, None, FAKE, 32, FAKE, S, H,
+                                         kvh, 128, 16, 64, 0.1, ps, ns, P, mx, FAKE, FAKE, FAKE, None)
+
+    def one(kv_dtype=1, ks=1.0, vs=1.0, dtype=1, out=FAKE, S=2):
+        return L.paged_decode_ex(FAKE, dtype, FAKE, FAKE, 0, kv_dtype, ks, vs, None, FAKE, 32, FAKE, S, 8, 2, 128, 16,
+                                 64, 0.1, 512, 0, 1, 512, None, None, None, None, out, None, None)
+    assert part(kv_dtype=0) == EINVAL           # an f32 cache under a bf16 query
+    assert part(kv_dtype=5) == EINVAL           # no such element type
+    assert part(ks=0.5) == EINVAL               # scales belong to a float8 cache
+    assert part(kv_dtype=2, ks=float("inf")) == EINVAL
+    assert part(kv_dtype=2, dtype=0) == EUNSUP  # a float8 cache needs a bf16 query
+    assert part(kv_dtype=2, H=36) == EUNSUP     # 18 query heads per kv head
+    assert part(ps=24) == EINVAL                # not a multiple of the block size
+    assert part(ns=4, P=2) == EINVAL            # fewer partial rows than splits
+    assert part(P=1, mx=513) == EINVAL          # 513 tokens need two 512-token partitions
+    assert part(kv_dtype=2, S=0) == OK          # empty batch
+    assert one(out=None) == EINVAL
+    assert one(kv_dtype=0) == EINVAL
+    assert one(kv_dtype=2, dtype=0) == EUNSUP
+    assert one(kv_dtype=2, S=0) == OK
