@@ -21,7 +21,8 @@ ARCH = "gfx950"
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
-    # packed-FP32 VALU instructions stay off: plain scalar/float2 code only
+    # packed-FP32 VALU instructions stay off in the gfx950 code (the device pass honours the
+    # flag; tests/test_build_guard.py checks the built code objects for them)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
@@ -40,8 +41,9 @@ def _compile(src: str, verbose: bool) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l
-                    and "not a recognized feature" not in l)
+    # the x86 host pass has no packed-fp32-ops feature and says so once per file: drop that line
+    out = "\n".join(l for l in r.stdout.splitlines()
+                    if not ("packed-fp32-ops" in l and "not a recognized feature" in l))
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {src}\n{out}")
     if verbose and out.strip():
