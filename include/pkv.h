@@ -106,7 +106,9 @@ typedef enum {
  *   block_size, max_num_partitions < ceil(max_seq_len / partition_size),
  *   max_seq_len > max_blocks_per_seq * block_size.
  * PKV_EUNSUPPORTED: block_size != 16; head_dim not in {64, 128, 256} (f32: {64, 128});
- *   G > 16, or G > 8 for f32 or for bf16 with head_dim 64 in the token-major layout.
+ *   G > 16, or G > 8 for f32 or for bf16 with head_dim 64 in the token-major layout;
+ *   num_seqs * num_kv_heads * ceil(max_seq_len / partition_size) above 2^31 - 1 (one
+ *   workgroup each), or num_seqs * num_heads above 2^30 - 1.
  * Groups of G <= 8 run on the vector ALUs; bf16 groups of 8 < G <= 16 (and G = 8 except
  *   for head_dim 64 token-major) run on the matrix cores, padded to 16 heads.
  * num_seqs == 0 or max_seq_len == 0 launches nothing except the sentinel writes that
@@ -163,8 +165,7 @@ int paged_decode_reduce(const float* partial_acc, const float* partial_m,
  * partial_m, partial_l are [num_seqs, num_heads, num_splits]. The reduce reads the
  * ceil(nb / bps) non-empty splits of each sequence.
  * PKV_EINVAL: num_splits <= 0, and the conditions of the fixed-partition entry points.
- * PKV_EUNSUPPORTED: as paged_decode_partial, and more than 4096 sequences (the work list
- *   the split map needs is held in LDS).
+ * PKV_EUNSUPPORTED: as paged_decode_partial.
  */
 int paged_decode_split_partial(const void* query, int dtype,
                                const void* key_cache, const void* value_cache, int layout,
@@ -202,7 +203,7 @@ int paged_decode_split_reduce(const float* partial_acc, const float* partial_m,
  * len_b == 0 gives out = 0 and lse = -inf.
  * PKV_EINVAL: as paged_decode_partial; NULL out; NULL partial arrays or counters when
  *   max_num_partitions > 1.
- * PKV_EUNSUPPORTED: as paged_decode_partial, and more than 4096 sequences.
+ * PKV_EUNSUPPORTED: as paged_decode_partial.
  */
 int paged_decode(const void* query, int dtype,
                  const void* key_cache, const void* value_cache, int layout,
@@ -319,8 +320,8 @@ int paged_attention_v2(void* out, float* exp_sums, float* max_logits, float* tmp
  *   out        [total_q, num_heads, ckv_dim] bf16        lse [total_q, num_heads] float32
  * PKV_EINVAL: NULL pointers with total_q > 0, negative sizes, sm_scale not finite.
  * PKV_EUNSUPPORTED: anything but num_heads = 16, ckv_dim = 512, kpe_dim = 64, page_size = 1
- *   (the shapes [MLA]'s _forward asserts); batch > 512 (the kernel keeps its per-batch tile
- *   list in LDS).
+ *   (the shapes [MLA]'s _forward asserts). Any batch count: the kernel orders its tiles
+ *   512 batches at a time.
  */
 int mla_paged_prefill(const void* q_nope, const void* q_pe,
                       const void* ckv_cache, const void* kpe_cache,

@@ -340,8 +340,11 @@ void decode_partial_mfma_kernel(DecodePartialArgs a, int G, int grid_parts) {
       len = len > a.len_cap ? a.len_cap : len;
       mfma_partition<D, XP, W, FINAL, ALIBI, FP8>(a, G, b, kvh, p, uniform(len), sm);
     }
-  } else {
-    const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  } else {  // partition-major: empty partitions sit at high indices and are dispatched last
+    const int sk = a.S * a.KVH;
+    const int p = (int)(blockIdx.x / sk);
+    const int r = (int)(blockIdx.x - p * sk);
+    const int b = r / a.KVH, kvh = r - b * a.KVH;
     int len = a.lens[b];
     len = len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
     if (p * part_tokens(len, a.ps, a.nsplit, 16) >= len) {
@@ -367,9 +370,10 @@ hipError_t launch_mfma_f(const DecodePartialArgs& a, int G, int grid_parts, hipS
     hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, true, FINAL, ALIBI, FP8>), dim3(grid), dim3(64 * W),
                        worklist_lds_words(a.S) * sizeof(int), s, a, G, grid_parts);
   } else {
-    dim3 grid(grid_parts, a.KVH, a.S);
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, false, FINAL, ALIBI, FP8>), grid, dim3(64 * W), 0, s, a,
-                       G, grid_parts);
+    const long upper = (long)a.S * a.KVH * grid_parts;
+    if (upper > INT32_MAX) return hipErrorNotSupported;
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, XP, W, false, FINAL, ALIBI, FP8>), dim3((unsigned)upper),
+                       dim3(64 * W), 0, s, a, G, grid_parts);
   }
   return hipGetLastError();
 }

@@ -399,8 +399,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(WPE, 8))
       len = len > a.len_cap ? a.len_cap : len;
       valu_partition<D, G, XP, LPT, W, FINAL, ALIBI>(a, b, kvh, p, uniform(len), sm);
     }
-  } else {
-    const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  } else {  // partition-major: empty partitions sit at high indices and are dispatched last
+    const int sk = a.S * a.KVH;
+    const int p = (int)(blockIdx.x / sk);
+    const int r = (int)(blockIdx.x - p * sk);
+    const int b = r / a.KVH, kvh = r - b * a.KVH;
     int len = a.lens[b];
     len = len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
     if (p * part_tokens(len, a.ps, a.nsplit, 16) >= len) {
@@ -437,9 +440,10 @@ hipError_t launch_valu_fin(const DecodePartialArgs& a, int grid_parts, hipStream
     hipLaunchKernelGGL((decode_partial_valu_kernel<D, G, XP, LPT, W, true, WPE, FINAL, ALIBI>), dim3(grid), dim3(64 * W),
                        worklist_lds_words(a.S) * sizeof(int), s, a, grid_parts);
   } else {
-    dim3 grid(grid_parts, a.KVH, a.S);
-    hipLaunchKernelGGL((decode_partial_valu_kernel<D, G, XP, LPT, W, false, WPE, FINAL, ALIBI>), grid, dim3(64 * W), 0,
-                       s, a, grid_parts);
+    const long upper = (long)a.S * a.KVH * grid_parts;
+    if (upper > INT32_MAX) return hipErrorNotSupported;
+    hipLaunchKernelGGL((decode_partial_valu_kernel<D, G, XP, LPT, W, false, WPE, FINAL, ALIBI>), dim3((unsigned)upper),
+                       dim3(64 * W), 0, s, a, grid_parts);
   }
   return hipGetLastError();
 }

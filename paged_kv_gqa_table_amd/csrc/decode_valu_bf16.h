@@ -680,11 +680,11 @@ hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream
     const int grid = (int)(upper < cap ? upper : cap);
     hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, true, SPLIT, FINAL, ALIBI, FP8>), dim3(grid),
                        dim3(64 * W), lds, s, a, grid_parts);
-  } else if constexpr (!SPLIT) {
-    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, false, false, FINAL, ALIBI, FP8>), dim3((unsigned)upper),
-                       dim3(64 * W), 0, s, a, grid_parts);
   } else {
-    return hipErrorNotSupported;  // NUM_SPLITS uses the work list (kMaxDenseSeqs sequences)
+    // the plain grid: one workgroup per (partition, sequence, kv head), partition-major
+    if (upper > INT32_MAX) return hipErrorNotSupported;
+    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, false, SPLIT, FINAL, ALIBI, FP8>), dim3((unsigned)upper),
+                       dim3(64 * W), 0, s, a, grid_parts);
   }
   return hipGetLastError();
 }

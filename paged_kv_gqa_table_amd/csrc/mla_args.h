@@ -6,7 +6,7 @@
 
 namespace pkv {
 
-constexpr int kMlaMaxBatch = 512;  // batches the kernel's LDS tile list holds
+constexpr int kMlaMaxBatch = 512;  // batches per chunk of the prefill kernel's LDS tile list
 
 struct MlaArgs {
   const void* q_nope;        // [total_q, 16, 512] bf16

@@ -54,7 +54,6 @@ int hip_status(hipError_t e, const char* what) {
   return fail(PKV_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
 }
 
-constexpr int kMaxGridYZ = 65535;
 constexpr int kPagedAttentionV2Partition = 512;  // the PagedAttention V2 launcher's fixed PARTITION_SIZE
 
 }  // namespace
@@ -178,7 +177,9 @@ int decode_phase1(const char* who, const void* query, int dtype, const void* key
     return fail(PKV_EUNSUPPORTED, "%s: head_dim %d for %s", who, head_dim, bf16 ? "bf16" : "f32");
   const int G = num_heads / num_kv_heads;
   if (G > (bf16 ? 16 : 8)) return fail(PKV_EUNSUPPORTED, "%s: %d query heads per kv head", who, G);
-  if (num_kv_heads > kMaxGridYZ || num_seqs > kMaxGridYZ) return fail(PKV_EUNSUPPORTED, "%s: grid too large", who);
+  if ((int64_t)num_seqs * num_kv_heads * std::max(grid_parts, 1) > INT32_MAX ||
+      (int64_t)num_seqs * num_heads > INT32_MAX / 2)
+    return fail(PKV_EUNSUPPORTED, "%s: grid too large (sequences x kv heads x partitions > 2^31 - 1)", who);
   if (grid_parts == 0 && !final_mode) return PKV_OK;  // every sequence is empty: nothing is touched
   if (grid_parts == 0) grid_parts = 1;  // final mode still writes the empty sequences' zeros
 
@@ -403,9 +404,6 @@ extern "C" int mla_paged_prefill(const void* q_nope, const void* q_pe, const voi
     return fail(PKV_EUNSUPPORTED,
                 "mla_paged_prefill: compiled for num_heads 16, ckv_dim 512, kpe_dim 64, page_size 1 "
                 "(got %d, %d, %d, %d)", num_heads, ckv_dim, kpe_dim, page_size);
-  if (batch > pkv::kMlaMaxBatch)
-    return fail(PKV_EUNSUPPORTED, "mla_paged_prefill: batch %d exceeds %d (the tile list is held in LDS)", batch,
-                pkv::kMlaMaxBatch);
   if (total_q == 0 || batch == 0) return PKV_OK;
   if (!q_nope || !q_pe || !ckv_cache || !kpe_cache || !qo_indptr || !kv_indptr || !kv_indices || !out || !lse)
     return fail(PKV_EINVAL, "mla_paged_prefill: NULL pointer argument");
@@ -435,8 +433,6 @@ extern "C" int mla_paged_prefill_pages(const void* q_nope, const void* q_pe, con
     return fail(PKV_EUNSUPPORTED,
                 "mla_paged_prefill_pages: compiled for num_heads 16, ckv_dim 512, kpe_dim 64 (got %d, %d, %d)",
                 num_heads, ckv_dim, kpe_dim);
-  if (batch > pkv::kMlaMaxBatch)
-    return fail(PKV_EUNSUPPORTED, "mla_paged_prefill_pages: batch %d exceeds %d", batch, pkv::kMlaMaxBatch);
   if ((int64_t)num_pages * page_size >= INT32_MAX || (int64_t)num_kv_indices * page_size >= INT32_MAX)
     return fail(PKV_EUNSUPPORTED, "mla_paged_prefill_pages: more than 2^31 tokens");
   if (total_q == 0 || batch == 0) return PKV_OK;

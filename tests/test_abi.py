@@ -72,6 +72,7 @@ def _partial(L, **kw):
     (dict(dtype=0, D=256), EUNSUP),
     (dict(H=34, KVH=2), EUNSUP),                      # G = 17
     (dict(dtype=0, H=18, KVH=2), EUNSUP),             # f32 G = 9
+    (dict(S=1 << 20, H=4096, KVH=4096), EUNSUP),      # 2^32 workgroups
     (dict(S=0, query=None), OK),                      # empty batch: nothing to do
     (dict(max_seq_len=0), OK),                        # every sequence empty: nothing touched
 ])
@@ -116,7 +117,6 @@ def _mla(L, **kw):
     (dict(Dc=256), EUNSUP),
     (dict(Dp=32), EUNSUP),
     (dict(ps=16), EUNSUP),
-    (dict(batch=513), EUNSUP),
     (dict(out=None), EINVAL),
     (dict(max_q_len=0), EINVAL),
     (dict(batch=-1), EINVAL),

@@ -342,3 +342,47 @@ def test_llama_gqa4_num_splits_full():
         check_out(out[b:b + 1], ro, "bf16", f"NS={ns} out b={b}")
         check_lse(lse[b:b + 1], rl, "bf16", f"NS={ns} b={b}")
     say("  every sequence matches the oracle")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dtype,D,H,KVH,layout", [
+    ("bf16", 128, 8, 2, "token_major"),   # G=4, vector ALU
+    ("bf16", 128, 24, 2, "xpacked"),      # G=12, matrix cores
+    ("f32", 64, 4, 2, "token_major"),     # G=2, f32
+])
+def test_num_splits_ten_thousand_sequences(dtype, D, H, KVH, layout):
+    """10,000 sequences under the NUM_SPLITS policy, both phases and the one-launch decode,
+    every sequence against the oracle: past the work list's LDS capacity the plain grid
+    of (split, sequence, kv head) workgroups takes over."""
+    S, ns = 10000, 4
+    rng = np.random.default_rng(S + H)
+    lens = rng.integers(0, 300, S)
+    lens[::9] = 0
+    lens[1::13] = 16 * ns * 3   # splits of whole pages only
+    lens[2::17] = 1
+    case = inputs.make_decode(lens, H, KVH, D, dtype=dtype, layout=layout, seed=S + D + H)
+    dev = to_dev(case)
+    say(f"NUM_SPLITS={ns}, S={S}: {dtype} D={D} H={H} KVH={KVH} {layout}")
+    acc = torch.full((S, H, ns, D), float("nan"), dtype=torch.float32, device="cuda")
+    m = torch.full((S, H, ns), float("nan"), dtype=torch.float32, device="cuda")
+    l = torch.full((S, H, ns), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full((S, H, D), float("nan"), dtype=case.query.dtype, device="cuda")
+    lse = torch.full((S, H), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.paged_decode_split_partial(dev["q"], dev["k"], dev["v"], dev["bt"], dev["lens"], case.scale, KVH,
+                                   case.max_seq_len, acc, m, l, layout=layout)
+    pkv.paged_decode_split_reduce(acc, m, l, dev["lens"], case.block_size, out, lse)
+    torch.cuda.synchronize()
+    say("  oracle")
+    r = oracle.decode_partials(case.query, case.key_cache, case.value_cache, layout, case.block_tables,
+                               case.seq_lens, case.scale, KVH, case.block_size, 0, ns, num_splits=ns)
+    _check_ranged_partials(_np(acc), _np(m), _np(l), r, lens,
+                           lambda n: oracle.partition_ranges(n, case.block_size, 0, ns), dtype, f"NS={ns}")
+    ro, rl = oracle.decode(case.query, case.key_cache, case.value_cache, layout, case.block_tables,
+                           case.seq_lens, case.scale, KVH, case.block_size)
+    check_out(_np(out), ro, dtype, "two phases out")
+    check_lse(_np(lse), rl, dtype, "two phases")
+    say("  one launch")
+    o1, s1, counters = one_launch(case, dev, 0, ns, num_splits=ns)
+    assert int(counters.abs().sum().item()) == 0, "counters not reset"
+    check_out(o1, ro, dtype, "one-launch out")
+    check_lse(s1, rl, dtype, "one-launch")

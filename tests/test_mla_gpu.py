@@ -72,10 +72,11 @@ def test_mla_edge_lengths(q_lens, prefixes):
     check(o, l, ro, rl, "edge")
 
 
-@pytest.mark.parametrize("n_batch,seed", [(48, 21), (512, 22)])
+@pytest.mark.parametrize("n_batch,seed", [(48, 21), (512, 22), (513, 24), (2000, 23)])
 def test_mla_many_batches(n_batch, seed):
     """Many batches, some without query rows, several with equal KV lengths: the tile order
-    (batches by KV length, ties by index) must still cover every row exactly once."""
+    (batches by KV length, ties by index, in chunks of 512 batches) must still cover every
+    row exactly once."""
     rng = np.random.default_rng(seed)
     q_lens = rng.integers(0, 20 if n_batch < 100 else 4, n_batch)
     q_lens[::7] = 0
@@ -160,6 +161,23 @@ def test_mla_multi_token_pages(page_size):
     check(o, l, ro, rl, f"page_size={page_size}")
     o2, l2 = run_gpu_paged(case, nan_tail=True)
     assert np.array_equal(o, o2) and np.array_equal(l, l2), "slots past the last token leaked into the output"
+
+
+@pytest.mark.timeout(300)
+def test_mla_pages_many_batches():
+    """3,000 batches over 16-token pages (some without keys or rows): the token-offset scan
+    runs over several passes and every batch's rows still land in place."""
+    rng = np.random.default_rng(77)
+    B = 3000
+    q_lens = rng.integers(0, 4, B)
+    prefixes = rng.integers(0, 60, B)
+    prefixes[::11] = 0
+    q_lens[::11] = 0   # no keys and no rows
+    case = inputs.make_mla_paged(q_lens.tolist(), prefixes.tolist(), 16, seed=78)
+    say(f"mla pages, many batches: B={B} total_q={case.total_q} pages={case.num_pages}")
+    o, l = run_gpu_paged(case)
+    ro, rl = run_oracle_paged(case)
+    check(o, l, ro, rl, f"B={B} page_size=16")
 
 
 def test_mla_prefill_b8_pages_of_16():
