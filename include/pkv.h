@@ -366,7 +366,7 @@ int mla_paged_prefill_pages(const void* q_nope, const void* q_pe,
 /*
  * mla_paged_decode -- MLA decode: one new token per sequence ([MLA]'s computation with
  * q_len = 1, so the token sees all kv_len keys), split-K over the latent cache on the
- * matrix cores, then the combine; two launches on `stream`.
+ * matrix cores, then the combine; one launch on `stream` with `counters`, else two.
  *
  * Batch b's keys are tok_j = kv_indices[kv_indptr[b] + j], j < kv_len_b (page_size 1).
  * Split s covers keys [s * split_tokens, min((s+1) * split_tokens, kv_len_b)); its partials
@@ -380,6 +380,10 @@ int mla_paged_prefill_pages(const void* q_nope, const void* q_pe,
  *   kv_indptr [batch + 1] int32 (kv_indptr[batch] = num_kv_indices), kv_indices int32 in [0, num_pages)
  *   partial_acc [batch, 16, max_num_splits, 512], partial_m / partial_l [batch, 16, max_num_splits]
  *              float32: caller-owned scratch
+ *   counters   [batch] int32 of device memory, all ZERO on entry and left zero: the combine
+ *              then runs in the same launch (the last workgroup to finish a batch combines
+ *              its splits); NULL: a second launch combines every batch. Calls that overlap
+ *              in time need separate counters and partial arrays.
  *   out [batch, 16, 512] bf16, lse [batch, 16] float32 (base 2)
  * max_kv_len bounds every kv_len_b (a longer batch is cut to max_num_splits splits).
  * PKV_EINVAL: NULL pointers with batch > 0, non-positive split_tokens or max_num_splits,
@@ -392,7 +396,7 @@ int mla_paged_decode(const void* q_nope, const void* q_pe,
                      int batch, int num_pages, int num_kv_indices, int max_kv_len,
                      int num_heads, int ckv_dim, int kpe_dim, int page_size, float sm_scale,
                      int split_tokens, int max_num_splits,
-                     float* partial_acc, float* partial_m, float* partial_l,
+                     float* partial_acc, float* partial_m, float* partial_l, int32_t* counters,
                      void* out, float* lse, void* stream);
 
 /*

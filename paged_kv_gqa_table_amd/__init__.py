@@ -92,7 +92,7 @@ def lib() -> ctypes.CDLL:
                                           i32, f32, vp, vp, vp, vp, vp]
     L.mla_paged_prefill_pages.restype = i32
     L.mla_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
-                                   vp, vp, vp, vp, vp, vp]
+                                   vp, vp, vp, vp, vp, vp, vp]
     L.mla_paged_decode.restype = i32
     L.paged_decode_partial_ex.argtypes = [vp, i32, vp, vp, i32, i32, f32, f32, vp, vp, i32, vp, i32, i32, i32, i32,
                                           i32, i32, f32, i32, i32, i32, i32, vp, vp, vp, vp]
@@ -642,7 +642,8 @@ def mla_paged_decode(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.
                      kv_indptr: torch.Tensor, kv_indices: torch.Tensor, sm_scale: float,
                      split_tokens: Optional[int] = None, max_kv_len: Optional[int] = None,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                     partials: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+                     partials: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                     counters: Optional[torch.Tensor] = None):
     """MLA decode, one new token per sequence: q_nope [B, 16, 512], q_pe [B, 16, 64].
     Returns (out [B, 16, 512] bf16, lse [B, 16] base 2). ``split_tokens`` keys per split,
     by default ``mla_decode_default_split``. Host reads: with both ``split_tokens`` and
@@ -650,7 +651,10 @@ def mla_paged_decode(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.
     or a captured graph needs: compute the split once and pass it); with ``max_kv_len``
     given and no split, the split comes from the length bounds alone, again without a read;
     with neither, kv_indptr is read to the host once (up to 256 batches the split then fits
-    the exact lengths). ``partials`` (acc, m, l) scratch is allocated when not given."""
+    the exact lengths). ``partials`` (acc, m, l) scratch is allocated when not given.
+    ``counters``: an int32 [B] device tensor of zeros (left zero by the call) makes it one
+    launch, the last workgroup of each batch combining its splits; without it a second
+    launch combines."""
     for n, t in (("q_nope", q_nope), ("q_pe", q_pe), ("ckv_cache", ckv_cache), ("kpe_cache", kpe_cache)):
         _dev(n, t, torch.bfloat16, 3)
     _dev("kv_indptr", kv_indptr, torch.int32, 1)
@@ -683,10 +687,15 @@ def mla_paged_decode(q_nope: torch.Tensor, q_pe: torch.Tensor, ckv_cache: torch.
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     _dev("out", out, torch.bfloat16, 3)
     _dev("lse", lse, torch.float32, 2)
+    if counters is not None:
+        _dev("counters", counters, torch.int32, 1)
+        if counters.numel() < B:
+            raise ValueError("counters must hold one int32 per batch")
     st = lib().mla_paged_decode(_ptr(q_nope), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache), _ptr(kv_indptr),
                                 _ptr(kv_indices), B, num_pages, kv_indices.numel(), int(max_kv_len), H, Dc, Dp,
                                 page_size, float(sm_scale), int(split_tokens), m.shape[2], _ptr(acc), _ptr(m),
-                                _ptr(l), _ptr(out), _ptr(lse), _stream(dev))
+                                _ptr(l), None if counters is None else _ptr(counters), _ptr(out), _ptr(lse),
+                                _stream(dev))
     _check(st, "mla_paged_decode")
     return out, lse
 

@@ -52,6 +52,7 @@ struct MlaDecodeArgs {
   float* acc;                 // [batch, 16, P, 512]
   float* m;                   // [batch, 16, P] natural log
   float* l;                   // [batch, 16, P]
+  int32_t* counters;          // [batch], zero; null: the combine is a second launch
   void* out;                  // [batch, 16, 512] bf16
   float* lse;                 // [batch, 16] base 2
 };

@@ -38,10 +38,13 @@
 //    reference by 2^8), with a wave-uniform branch.
 #include "common.h"
 #include "mla_args.h"
+#include "mla_tile.h"
 
 namespace pkv {
 
 namespace {
+
+using namespace mla;
 
 constexpr int kH = 16;          // heads (MFMA rows / cols)
 constexpr int kDc = 512;        // ckv dims (also V dims)
@@ -49,62 +52,18 @@ constexpr int kDp = 64;         // kpe dims
 constexpr int kQT = 8;          // query tokens per workgroup (one per wave)
 constexpr int kNT = kQT * 64;   // threads per workgroup
 constexpr int kKT = 32;         // keys per tile
-constexpr int kCkvChunks = kDc * 2 / 16;     // 64 16-byte chunks of a ckv row
-constexpr int kKpeChunks = kDp * 2 / 16;     // 8 chunks of a kpe row
-constexpr int kCkvStride = kCkvChunks + 2;   // padded LDS row (chunks), see ckv_swz
 constexpr int kKeysPerWave = kKT / kQT;      // keys of a tile gathered by each wave
 static_assert(kKeysPerWave * kQT == kKT, "tile shape");
 constexpr int kMaxBatch = kMlaMaxBatch;  // batches per chunk of the tile list
 constexpr float kMlaRebase = 8.f;
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int idsv_t __attribute__((ext_vector_type(kKeysPerWave), aligned(4)));  // a wave's page ids
-
-PKV_DEVICE f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                 c, 0, 0, 0);
-}
-
-// LDS bank spreading. A ckv row r sits at stride kCkvStride (32 B past a multiple of
-// 1 KiB) with 16-byte chunk c at position c ^ ckv_swz(r). The logits read 16 B per lane
-// from 16 consecutive rows at one chunk; the padding puts rows on even chunk offsets and
-// the swizzle moves every other group of 4 rows to the odd ones, so any 8 (or 16) rows
-// land on distinct chunks of a 128-byte (256-byte) bank line. The transposing V reads
-// take 32 B from each of 4 (8) consecutive rows; the padding alone keeps those apart and
-// the swizzle, which only flips chunk bit 0, never splits a 32-byte pair.
-PKV_DEVICE uint32_t ckv_swz(int r) { return (uint32_t)(((r >> 2) ^ (r >> 3)) & 1); }
-// kpe rows are packed (128 B) because one transfer fills 8 of them; chunk c of row r sits
-// at position c ^ kpe_swz(r), which sends the 8 (16) rows of a logits read to distinct
-// chunks of a bank line.
-PKV_DEVICE uint32_t kpe_swz(int r) { return (uint32_t)((r & 7) ^ ((r >> 3) & 1)); }
-
-PKV_DEVICE void vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-// Transposing 8-byte LDS read (see the header comment for the lane mapping).
-PKV_DEVICE uint2 lds_read_tr16(const void* p) {
-  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(
-      (__attribute__((address_space(3))) void*)p));
-  return __builtin_bit_cast(uint2, v);
-}
-
-// 16 bytes per lane from global memory (scalar base + per-lane offset) straight into LDS
-// (lane i -> lds_base + 16 i; lanes outside the exec mask move nothing). Written as inline
-// assembly so the compiler does not see an LDS write: with the builtin it waits for every
-// outstanding transfer before each later LDS read, which would stall the math on tile kt
-// until tile kt + 1 has landed. The kernel itself waits (vmcnt(0)) and then barriers
-// before any wave reads a buffer that a transfer filled.
-PKV_DEVICE void lds_dma16_s(const void* sbase, uint32_t voff, const void* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base);
-  // M0 (the LDS destination) is an input operand, so the compiler writes it and knows its value
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0));
-}
-
 
 }  // namespace
 
+// CHUNKED: more than kMaxBatch batches (the tile list is built chunk by chunk); the
+// single-chunk instance keeps the chunk bookkeeping out of the key loop's scalar registers.
+template <bool CHUNKED>
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2)))  // 2 waves per SIMD
 void mla_prefill_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) uint4 s_ckv[2][kKT * kCkvStride];  // double-buffered key tiles
@@ -128,8 +87,8 @@ void mla_prefill_kernel(MlaArgs a) {
   // and no workgroup waits for another.
   const int R = gridDim.x;
   int carry = 0;  // tiles of the earlier chunks, mod R
-  for (int c0 = 0; c0 < B; c0 += kMaxBatch) {
-    const int CB = min(kMaxBatch, B - c0);
+  for (int c0 = 0; c0 < (CHUNKED ? B : 1); c0 += kMaxBatch) {
+    const int CB = CHUNKED ? min(kMaxBatch, B - c0) : B;
     {
       const int per = (CB + kNT - 1) / kNT;
       const int i0 = tid * per;
@@ -177,7 +136,7 @@ void mla_prefill_kernel(MlaArgs a) {
       __syncthreads();
     }
     const int n_tiles = uniform(s_tiles[CB]);
-    const int first = blockIdx.x >= carry ? blockIdx.x - carry : blockIdx.x + R - carry;
+    const int first = !CHUNKED ? (int)blockIdx.x : (blockIdx.x >= carry ? blockIdx.x - carry : blockIdx.x + R - carry);
 
     for (int tile = first; tile < n_tiles; tile += R) {
       // sorted position (then batch) of this tile
@@ -399,8 +358,10 @@ void mla_prefill_kernel(MlaArgs a) {
       }
       __syncthreads();  // LDS buffers are reused by the next tile of work
     }
-    carry = (int)(((long)carry + n_tiles) % R);
-    __syncthreads();  // every wave has read this chunk's list before the next one is built
+    if constexpr (CHUNKED) {
+      carry = (int)(((long)carry + n_tiles) % R);
+      __syncthreads();  // every wave has read this chunk's list before the next one is built
+    }
   }
 }
 
@@ -410,7 +371,10 @@ hipError_t launch_mla_prefill(const MlaArgs& a, hipStream_t s) {
   const int cap = dense_grid_cap();
   const int grid = (int)(bound < cap ? bound : cap);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_prefill_kernel, dim3(grid), dim3(kNT), 0, s, a);
+  if (a.batch > kMaxBatch)
+    hipLaunchKernelGGL(mla_prefill_kernel<true>, dim3(grid), dim3(kNT), 0, s, a);
+  else
+    hipLaunchKernelGGL(mla_prefill_kernel<false>, dim3(grid), dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -461,8 +461,8 @@ extern "C" int mla_paged_decode(const void* q_nope, const void* q_pe, const void
                                 const int32_t* kv_indptr, const int32_t* kv_indices, int batch, int num_pages,
                                 int num_kv_indices, int max_kv_len, int num_heads, int ckv_dim, int kpe_dim,
                                 int page_size, float sm_scale, int split_tokens, int max_num_splits,
-                                float* partial_acc, float* partial_m, float* partial_l, void* out, float* lse,
-                                void* stream) {
+                                float* partial_acc, float* partial_m, float* partial_l, int32_t* counters,
+                                void* out, float* lse, void* stream) {
   if (batch < 0 || num_pages < 0 || num_kv_indices < 0 || max_kv_len < 0 || num_heads <= 0 || ckv_dim <= 0 ||
       kpe_dim <= 0 || page_size <= 0 || split_tokens <= 0 || max_num_splits <= 0)
     return fail(PKV_EINVAL, "mla_paged_decode: bad sizes");
@@ -492,6 +492,7 @@ extern "C" int mla_paged_decode(const void* q_nope, const void* q_pe, const void
   a.len_cap = (int)std::min<int64_t>((int64_t)(grid_parts > 0 ? grid_parts : 1) * split_tokens, INT32_MAX);
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
   a.acc = partial_acc; a.m = partial_m; a.l = partial_l; a.out = out; a.lse = lse;
+  a.counters = counters;
   return hip_status(pkv::launch_mla_decode(a, (int)grid_parts, reinterpret_cast<hipStream_t>(stream)),
                     "mla_paged_decode launch");
 }

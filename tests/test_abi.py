@@ -218,7 +218,7 @@ def test_mla_pages_validation(L):
 def test_mla_decode_validation(L):
     def call(heads=16, split=256, P=4, max_kv=1000, batch=2, num_pages=8, ps=1, acc=FAKE):
         return L.mla_paged_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, batch, num_pages, 8, max_kv, heads, 512, 64, ps,
-                                  0.1, split, P, acc, FAKE, FAKE, FAKE, FAKE, None)
+                                  0.1, split, P, acc, FAKE, FAKE, None, FAKE, FAKE, None)
     assert call(heads=8) == EUNSUP
     assert call(ps=16) == EUNSUP
     assert call(split=0) == EINVAL

@@ -205,10 +205,24 @@ def test_mla_decode_shapes():
 # --------------------------------------------------------------------------------------
 
 def run_decode_gpu(case, split, max_kv_len=None):
+    """Both forms of the call: two launches, then one launch (counters) twice on the same
+    counters, which must come back zero and give the two-launch result bit for bit (the
+    combine is the same code, only its loads differ)."""
     t = {k: getattr(case, k).to("cuda") for k in FIELDS}
     out, lse = pkv.mla_paged_decode(t["q_nope"], t["q_pe"], t["ckv_cache"], t["kpe_cache"], t["kv_indptr"],
                                     t["kv_indices"], case.sm_scale, split_tokens=split, max_kv_len=max_kv_len)
     torch.cuda.synchronize()
+    B = case.kv_indptr.numel() - 1
+    counters = torch.zeros(B, dtype=torch.int32, device="cuda")
+    for rep in range(2):
+        o1 = torch.full_like(out, float("nan"))
+        l1 = torch.full_like(lse, float("nan"))
+        pkv.mla_paged_decode(t["q_nope"], t["q_pe"], t["ckv_cache"], t["kpe_cache"], t["kv_indptr"], t["kv_indices"],
+                             case.sm_scale, split_tokens=split, max_kv_len=max_kv_len, out=o1, lse=l1,
+                             counters=counters)
+        torch.cuda.synchronize()
+        assert int(counters.abs().sum().item()) == 0, "counters not reset"
+        assert torch.equal(o1, out) and torch.equal(l1, lse), f"one launch differs from two (call {rep})"
     return out.cpu().to(torch.float64).numpy(), lse.cpu().to(torch.float64).numpy()
 
 
