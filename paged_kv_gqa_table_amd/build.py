@@ -54,6 +54,9 @@ def _compile(src: str, verbose: bool) -> str:
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    # the units with the most kernel instances first, so the slowest ones never start last
+    heavy = ("d256", "_g16", "bf16", "mfma")
+    srcs.sort(key=lambda p: next((i for i, h in enumerate(heavy) if h in os.path.basename(p)), len(heavy)))
     jobs = jobs or min(8, os.cpu_count() or 4)
     t0 = time.time()
     with cf.ThreadPoolExecutor(jobs) as ex:

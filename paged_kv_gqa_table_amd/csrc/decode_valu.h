@@ -1,4 +1,4 @@
-// Split-K paged decode, phase 1, float32, on the vector ALUs (query-head groups G <= 8).
+// Split-K paged decode, phase 1, float32, on the vector ALUs (query-head groups G <= 16).
 //
 // What it computes is the per-partition online softmax of the PagedAttention V2 Triton
 // page (_partition_attn_kernel) with the unnormalized accumulator of the flash-decode
@@ -458,30 +458,27 @@ hipError_t launch_valu_one(const DecodePartialArgs& a, int grid_parts, hipStream
                           : launch_valu_fin<XP, D, G, false, false>(a, grid_parts, s);
 }
 
-template <bool XP, int D>
-hipError_t launch_valu_d(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
-  switch (G) {
-    case 1: return launch_valu_one<XP, D, 1>(a, grid_parts, s);
-    case 2: return launch_valu_one<XP, D, 2>(a, grid_parts, s);
-    case 3: return launch_valu_one<XP, D, 3>(a, grid_parts, s);
-    case 4: return launch_valu_one<XP, D, 4>(a, grid_parts, s);
-    case 5: return launch_valu_one<XP, D, 5>(a, grid_parts, s);
-    case 6: return launch_valu_one<XP, D, 6>(a, grid_parts, s);
-    case 7: return launch_valu_one<XP, D, 7>(a, grid_parts, s);
-    case 8: return launch_valu_one<XP, D, 8>(a, grid_parts, s);
-    default: return hipErrorNotSupported;
+// Group sizes GLO .. GHI of one head dim (the instances of one translation unit).
+template <bool XP, int D, int GLO, int GHI>
+hipError_t launch_valu_g(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
+  if constexpr (GLO > GHI) {
+    return hipErrorNotSupported;
+  } else {
+    if (G == GLO) return launch_valu_one<XP, D, GLO>(a, grid_parts, s);
+    return launch_valu_g<XP, D, GLO + 1, GHI>(a, G, grid_parts, s);
   }
 }
 
-template <bool XP>
-hipError_t launch_valu(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
-  switch (a.D) {
-    case 64: return launch_valu_d<XP, 64>(a, G, grid_parts, s);
-    case 128: return launch_valu_d<XP, 128>(a, G, grid_parts, s);
-    case 256:
-      return hipErrorNotSupported;
-    default: return hipErrorNotSupported;
-  }
-}
+// The float32 instances are split over four translation units per layout so that the
+// build compiles them in parallel: head dims 64 and 128 with G <= 8 (decode_valu_f32_<l>),
+// G 9 .. 16 at head dims 64 and 128 (decode_valu_f32_<l>_g16), head dim 256 with G <= 8
+// (decode_valu_f32_<l>_d256) and with G 9 .. 16 (decode_valu_f32_<l>_d256g16).
+#define PKV_F32_PART_LAUNCHERS(L)                                                                       \
+  hipError_t launch_valu_f32_##L##_d256(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s);    \
+  hipError_t launch_valu_f32_##L##_d256g16(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s); \
+  hipError_t launch_valu_f32_##L##_g16(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s);
+PKV_F32_PART_LAUNCHERS(tm)
+PKV_F32_PART_LAUNCHERS(xp)
+#undef PKV_F32_PART_LAUNCHERS
 
 }  // namespace pkv

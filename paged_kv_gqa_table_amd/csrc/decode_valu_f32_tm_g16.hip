@@ -1,0 +1,12 @@
+// float32 vector-ALU decode instances, token-major layout, G 9 .. 16 at head dims 64 and 128.
+#include "decode_valu.h"
+
+namespace pkv {
+hipError_t launch_valu_f32_tm_g16(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
+  switch (a.D) {
+    case 64: return launch_valu_g<false, 64, 9, 16>(a, G, grid_parts, s);
+    case 128: return launch_valu_g<false, 128, 9, 16>(a, G, grid_parts, s);
+    default: return hipErrorNotSupported;
+  }
+}
+}  // namespace pkv

@@ -173,10 +173,10 @@ int decode_phase1(const char* who, const void* query, int dtype, const void* key
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale is not finite", who);
   if (block_size != 16) return fail(PKV_EUNSUPPORTED, "%s: block_size %d (compiled for 16)", who, block_size);
   const bool bf16 = dtype == PKV_BF16;
-  if (!(head_dim == 64 || head_dim == 128 || (bf16 && head_dim == 256)))
-    return fail(PKV_EUNSUPPORTED, "%s: head_dim %d for %s", who, head_dim, bf16 ? "bf16" : "f32");
+  if (!(head_dim == 64 || head_dim == 128 || head_dim == 256))
+    return fail(PKV_EUNSUPPORTED, "%s: head_dim %d", who, head_dim);
   const int G = num_heads / num_kv_heads;
-  if (G > (bf16 ? 16 : 8)) return fail(PKV_EUNSUPPORTED, "%s: %d query heads per kv head", who, G);
+  if (G > 16) return fail(PKV_EUNSUPPORTED, "%s: %d query heads per kv head", who, G);
   if ((int64_t)num_seqs * num_kv_heads * std::max(grid_parts, 1) > INT32_MAX ||
       (int64_t)num_seqs * num_heads > INT32_MAX / 2)
     return fail(PKV_EUNSUPPORTED, "%s: grid too large (sequences x kv heads x partitions > 2^31 - 1)", who);

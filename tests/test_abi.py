@@ -69,9 +69,7 @@ def _partial(L, **kw):
     (dict(scale=float("nan")), EINVAL),
     (dict(bs=8, ps=512, mb=32), EUNSUP),
     (dict(D=96), EUNSUP),
-    (dict(dtype=0, D=256), EUNSUP),
     (dict(H=34, KVH=2), EUNSUP),                      # G = 17
-    (dict(dtype=0, H=18, KVH=2), EUNSUP),             # f32 G = 9
     (dict(S=1 << 20, H=4096, KVH=4096), EUNSUP),      # 2^32 workgroups
     (dict(S=0, query=None), OK),                      # empty batch: nothing to do
     (dict(max_seq_len=0), OK),                        # every sequence empty: nothing touched

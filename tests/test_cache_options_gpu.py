@@ -158,7 +158,7 @@ def test_cache_options_every_mode(dtype, D, H, KVH, layout, kv_dtype, alibi):
 
 
 @pytest.mark.parametrize("D,H,KVH,layout", [(64, 6, 2, "token_major"), (128, 8, 1, "xpacked"),
-                                            (128, 4, 4, "token_major")])
+                                            (128, 4, 4, "token_major"), (256, 16, 1, "xpacked")])
 def test_f32_alibi_real_slopes_every_mode(D, H, KVH, layout):
     """f32 with the usual geometric ALiBi slopes (maxima of several hundred at 1500 tokens),
     all four modes, under the f32 bounds (m relative, see the module docstring)."""

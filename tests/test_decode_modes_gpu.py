@@ -30,6 +30,7 @@ CONFIGS = [
     ("bf16", 256, 24, 2, "xpacked"),      # G=12, matrix cores
     ("f32", 128, 6, 2, "token_major"),    # G=3, f32
     ("f32", 64, 8, 1, "xpacked"),         # G=8, f32
+    ("f32", 256, 12, 1, "xpacked"),       # G=12, f32 head dim 256
 ]
 
 

@@ -226,6 +226,12 @@ EDGE_LENS = [0, 1, 15, 16, 17, 100, 511, 512, 513, 1024, 1500]
     ("f32", 64, 4, 4, "xpacked"),
     ("f32", 128, 12, 2, "token_major"),   # G=6
     ("f32", 128, 8, 1, "xpacked"),        # G=8
+    ("f32", 256, 4, 2, "token_major"),    # head dim 256
+    ("f32", 256, 8, 1, "xpacked"),        # head dim 256, G=8
+    ("f32", 64, 24, 2, "token_major"),    # G=12
+    ("f32", 128, 16, 1, "xpacked"),       # G=16
+    ("f32", 256, 32, 2, "token_major"),   # head dim 256, G=16
+    ("f32", 256, 30, 3, "xpacked"),       # head dim 256, G=10
 ])
 def test_edge_lengths(dtype, D, H, KVH, layout):
     say(f"edge: {dtype} D={D} H={H} KVH={KVH} {layout}")
