@@ -534,6 +534,15 @@ def main():
         extra["llama_gqa4_one_launch"] = {"us_per_step": ro["wall_ms_per_step"] * 1e3,
                                           "GB_s": kv / (ro["wall_ms_per_step"] * 1e-3) / 1e9,
                                           "kernel_avg_us": ro["partial_avg_ms"] * 1e3}
+        # the same lengths over 32-token blocks: the generic-block-size kernel
+        c32 = inputs.make_decode(case.seq_lens.numpy(), case.num_heads, case.num_kv_heads, case.head_dim,
+                                 dtype=case.dtype, layout=case.layout, block_size=32, seed=5,
+                                 partition_size=case.partition_size, name="llama_gqa4_block32")
+        r32 = bench_decode(c32, 20, 3, graph=not args.eager)
+        extra["llama_gqa4_block32"] = {"us_per_step": r32["wall_ms_per_step"] * 1e3,
+                                       "GB_s": r32["kv_bytes"] / (r32["wall_ms_per_step"] * 1e-3) / 1e9,
+                                       "kernel": "generic-block-size kernel (32-token blocks), both phases"}
+        del c32
         secondary = {}
         for name in ("wide_gqa6", "skewed_gqa8"):
             _log(f"secondary workload {name}")

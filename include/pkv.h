@@ -105,13 +105,13 @@ typedef enum {
  *   size, num_heads % num_kv_heads != 0, partition_size not a positive multiple of
  *   block_size, max_num_partitions < ceil(max_seq_len / partition_size),
  *   max_seq_len > max_blocks_per_seq * block_size.
- * PKV_EUNSUPPORTED: block_size != 16; head_dim not in {64, 128, 256};
- *   G > 16, or G > 8 for bf16 with head_dim 64 in the token-major layout;
+ * PKV_EUNSUPPORTED: head_dim not in {64, 128, 256}; G > 16;
  *   num_seqs * num_kv_heads * ceil(max_seq_len / partition_size) above 2^31 - 1 (one
  *   workgroup each), or num_seqs * num_heads above 2^30 - 1.
  * bf16 groups of G < 8 (and G = 8 at head_dim 64 token-major) and every float32 group run
  *   on the vector ALUs; bf16 groups of 8 <= G <= 16 run on the matrix cores, padded to 16
- *   heads.
+ *   heads. Those kernels take 16-token blocks; any other block_size >= 1, and bf16 groups
+ *   of 9-16 heads at head_dim 64 token-major, run on a generic kernel (not tuned).
  * num_seqs == 0 or max_seq_len == 0 launches nothing except the sentinel writes that
  *   the length rule above asks for.
  * A length above max_seq_len (a broken contract) is cut to max_num_partitions partitions,

@@ -21,6 +21,8 @@ struct DecodePartialArgs {
   int ps;                 // partition size in tokens (multiple of 16); unused when nsplit > 0
   int ppp;                // pages per partition = ps / 16; unused when nsplit > 0
   int nsplit;             // > 0: NUM_SPLITS policy, ceil(pages_b / nsplit) pages per partition
+  int bs;                 // block size (tokens per page) of the pools: 16 for every kernel but
+                          // the generic one
   int normalize;          // != 0: store acc / l instead of acc
   const float* alibi;     // [H] ALiBi slopes (natural-log units), or null: score of key t
                           // gets -slope_h * (len - 1 - t)
@@ -69,6 +71,9 @@ hipError_t launch_decode_valu_bf16_xp(const DecodePartialArgs& a, int G, int gri
 hipError_t launch_decode_mfma_bf16_tm(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s);
 hipError_t launch_decode_mfma_bf16_xp(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeReduceArgs& a, bool out_bf16, hipStream_t s);
+// Any block size (a.bs), head dim 64/128/256, G <= 16, float32 or bf16 query, both layouts.
+hipError_t launch_decode_generic(const DecodePartialArgs& a, int G, int grid_parts, bool xp, bool q_f32,
+                                 hipStream_t s);
 
 // Sets the calling thread's pkv_last_error() message (printf format) and returns `code`.
 int set_last_error(int code, const char* fmt, ...);

@@ -158,7 +158,7 @@ PKV_DEVICE float alibi_shift2(const DecodePartialArgs& a, int h, int len, int t_
 
 // Number of partitions of a sequence of len tokens under the launch's partition map.
 PKV_DEVICE int item_parts(const DecodePartialArgs& a, int len) {
-  const int pt = part_tokens(len, a.ps, a.nsplit, 16);
+  const int pt = part_tokens(len, a.ps, a.nsplit, a.bs);
   return (len + pt - 1) / pt;
 }
 

@@ -410,8 +410,9 @@ hipError_t launch_mfma(const DecodePartialArgs& a, int G, int grid_parts, hipStr
 
 hipError_t launch_decode_mfma_bf16_tm(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {
   // D = 64 token-major rows are 128 bytes: no whole 128-dim V block; the vector-ALU kernel
-  // covers G <= 8 there and larger groups are not compiled.
-  if (a.D == 64) return G <= 8 ? launch_decode_valu_bf16_tm(a, G, grid_parts, s) : hipErrorNotSupported;
+  // covers G <= 8 there and the generic kernel larger groups.
+  if (a.D == 64) return G <= 8 ? launch_decode_valu_bf16_tm(a, G, grid_parts, s)
+                               : launch_decode_generic(a, G, grid_parts, false, false, s);
   return launch_mfma<false>(a, G, grid_parts, s);
 }
 hipError_t launch_decode_mfma_bf16_xp(const DecodePartialArgs& a, int G, int grid_parts, hipStream_t s) {

@@ -171,7 +171,6 @@ int decode_phase1(const char* who, const void* query, int dtype, const void* key
                   max_num_partitions, grid_parts);
   }
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale is not finite", who);
-  if (block_size != 16) return fail(PKV_EUNSUPPORTED, "%s: block_size %d (compiled for 16)", who, block_size);
   const bool bf16 = dtype == PKV_BF16;
   if (!(head_dim == 64 || head_dim == 128 || head_dim == 256))
     return fail(PKV_EUNSUPPORTED, "%s: head_dim %d", who, head_dim);
@@ -199,6 +198,7 @@ int decode_phase1(const char* who, const void* query, int dtype, const void* key
     a.nsplit = mode.num_splits;
   }
   a.ppp = a.ps / block_size;
+  a.bs = block_size;
   // lengths are cut to the partitions this launch covers (a length past max_seq_len breaks
   // the contract; it must still not push a partition index past the launched grid)
   a.len_cap = (int)std::min<int64_t>(table_tokens, a.nsplit > 0 ? table_tokens : (int64_t)grid_parts * a.ps);
@@ -214,7 +214,9 @@ int decode_phase1(const char* who, const void* query, int dtype, const void* key
 
   hipError_t e;
   const bool xp = layout == PKV_KV_XPACKED;
-  if (bf16 && G >= 8) {
+  if (block_size != 16) {  // the tuned kernels take 16-token pages
+    e = pkv::launch_decode_generic(a, G, grid_parts, xp, !bf16, s);
+  } else if (bf16 && G >= 8) {
     e = xp ? pkv::launch_decode_mfma_bf16_xp(a, G, grid_parts, s)
            : pkv::launch_decode_mfma_bf16_tm(a, G, grid_parts, s);
   } else if (bf16) {

@@ -67,7 +67,8 @@ def _partial(L, **kw):
     (dict(S=-1), EINVAL),
     (dict(max_seq_len=-1), EINVAL),
     (dict(scale=float("nan")), EINVAL),
-    (dict(bs=8, ps=512, mb=32), EUNSUP),
+    (dict(bs=8, ps=500, mb=64), EINVAL),             # partition size not a multiple of block size 8
+    (dict(bs=0), EINVAL),
     (dict(D=96), EUNSUP),
     (dict(H=34, KVH=2), EUNSUP),                      # G = 17
     (dict(S=1 << 20, H=4096, KVH=4096), EUNSUP),      # 2^32 workgroups
@@ -161,7 +162,7 @@ def _one_launch(L, **kw):
     (dict(ns=-1), EINVAL),
     (dict(ns=3, P=2), EINVAL),                        # fewer partitions than splits
     (dict(P=1, max_seq_len=128, ps=64, acc=None, m=None, l=None, out=None), EINVAL),
-    (dict(bs=8, mb=16, ps=64), EUNSUP),
+    (dict(bs=32, mb=16, ps=48), EINVAL),             # partition size not a multiple of block size 32
     (dict(D=96), EUNSUP),
     (dict(S=0), OK),                                  # empty batch: nothing to do
 ])
@@ -179,8 +180,8 @@ def test_split_entry_points_validation(L):
     args = [FAKE, 1, FAKE, FAKE, 0, FAKE, 8, FAKE, 2, 8, 2, 128, 16, 64, 0.1]
     assert L.paged_decode_split_partial(*args, 0, 128, FAKE, FAKE, FAKE, None) == EINVAL   # num_splits = 0
     assert L.paged_decode_split_partial(*args, 4, 200, FAKE, FAKE, FAKE, None) == EINVAL   # max_seq_len > table
-    args[12] = 32
-    assert L.paged_decode_split_partial(*args, 4, 128, FAKE, FAKE, FAKE, None) == EUNSUP   # block_size 32
+    args[12] = 0
+    assert L.paged_decode_split_partial(*args, 4, 128, FAKE, FAKE, FAKE, None) == EINVAL   # block_size 0
     assert L.paged_decode_split_reduce(FAKE, FAKE, FAKE, FAKE, 2, 8, 128, 16, 0, FAKE, 1, None, None) == EINVAL
     assert L.paged_decode_split_reduce(FAKE, FAKE, FAKE, FAKE, 2, 8, 96, 16, 4, FAKE, 1, None, None) == EUNSUP
     assert L.paged_decode_split_reduce(FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 16, 4, FAKE, 1, None, None) == OK
