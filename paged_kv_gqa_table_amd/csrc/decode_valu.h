@@ -434,11 +434,19 @@ hipError_t launch_valu_fin(const DecodePartialArgs& a, int grid_parts, hipStream
   constexpr int LPT = (D * EB >= PKV_VALU_ROW_BYTES_LPT16) ? 16 : 8;
   constexpr int W = 4;
   constexpr int WPE = PKV_VALU_WPE;  // target waves per SIMD (4 caps VGPRs at 128)
-  if (use_dense_worklist(a.S, a.KVH, grid_parts)) {
-    const long upper = (long)a.S * a.KVH * grid_parts;
-    const int grid = (int)(upper < dense_grid_cap() ? upper : dense_grid_cap());
-    hipLaunchKernelGGL((decode_partial_valu_kernel<D, G, XP, LPT, W, true, WPE, FINAL, ALIBI>), dim3(grid), dim3(64 * W),
-                       worklist_lds_words(a.S) * sizeof(int), s, a, grid_parts);
+  // The work list pays off on skewed batches; the float32 instances at head dim 256 or
+  // with more than 8 heads per group (a parity path) keep to the plain grid, which halves
+  // what they compile.
+  constexpr bool kListed = D != 256 && G <= 8;
+  bool listed = false;
+  if constexpr (kListed) listed = use_dense_worklist(a.S, a.KVH, grid_parts);
+  if (listed) {
+    if constexpr (kListed) {
+      const long upper = (long)a.S * a.KVH * grid_parts;
+      const int grid = (int)(upper < dense_grid_cap() ? upper : dense_grid_cap());
+      hipLaunchKernelGGL((decode_partial_valu_kernel<D, G, XP, LPT, W, true, WPE, FINAL, ALIBI>), dim3(grid),
+                         dim3(64 * W), worklist_lds_words(a.S) * sizeof(int), s, a, grid_parts);
+    }
   } else {
     const long upper = (long)a.S * a.KVH * grid_parts;
     if (upper > INT32_MAX) return hipErrorNotSupported;
