@@ -31,11 +31,15 @@ constexpr int kGenG = 16;    // most query heads per kv head
 
 template <int D>
 struct GenSmem {
-  float q[kGenG][D];               // the item's query rows, float32
-  float p[kGenW][kGenG][64];       // a wave's P of its current chunk
-  int blk[kGenW][64];              // each chunk token's block id (clamped into the pool)
-  int slot[kGenW][64];             // ... and its slot in the block
-  float red_acc[kGenW][kGenG][D];  // each wave's accumulator, for the merge
+  union {
+    struct {
+      float q[kGenG][D];          // the item's query rows, float32
+      float p[kGenW][kGenG][64];  // a wave's P of its current chunk
+      int blk[kGenW][64];         // each chunk token's block id (clamped into the pool)
+      int slot[kGenW][64];        // ... and its slot in the block
+    } run;
+    float red_acc[kGenW][kGenG][D];  // each wave's accumulator, for the merge (after the chunks)
+  } u;
   float red_m[kGenW][kGenG];       // each wave's running max (base 2), -inf without tokens
   float red_l[kGenW][kGenG];
 };
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(64 * kGenW) void decode_generic_kernel(DecodePartia
     float v;
     if constexpr (QF32) v = reinterpret_cast<const float*>(a.q)[(qrow0 + g) * D + d];
     else v = bf16lo(reinterpret_cast<const uint16_t*>(a.q)[(qrow0 + g) * D + d]);
-    sm.q[g][d] = v;
+    sm.u.run.q[g][d] = v;
   }
   __syncthreads();
 
@@ -187,8 +191,8 @@ __global__ __launch_bounds__(64 * kGenW) void decode_generic_kernel(DecodePartia
 #pragma unroll
       for (int g = 0; g < kGenG; ++g) {
         if (g < G) {
-          const float4 qa = *reinterpret_cast<const float4*>(&sm.q[g][d]);
-          const float4 qb = *reinterpret_cast<const float4*>(&sm.q[g][d + 4]);
+          const float4 qa = *reinterpret_cast<const float4*>(&sm.u.run.q[g][d]);
+          const float4 qb = *reinterpret_cast<const float4*>(&sm.u.run.q[g][d + 4]);
           float x = s[g];
           x = fmaf(qa.x, k8[0], x); x = fmaf(qa.y, k8[1], x); x = fmaf(qa.z, k8[2], x); x = fmaf(qa.w, k8[3], x);
           x = fmaf(qb.x, k8[4], x); x = fmaf(qb.y, k8[5], x); x = fmaf(qb.z, k8[6], x); x = fmaf(qb.w, k8[7], x);
@@ -210,42 +214,54 @@ __global__ __launch_bounds__(64 * kGenW) void decode_generic_kernel(DecodePartia
         m_run[g] = m_new;
 #pragma unroll
         for (int i = 0; i < DPL; ++i) acc[g][i] *= alpha;
-        sm.p[w][g][lane] = pe;
+        sm.u.run.p[w][g][lane] = pe;
       }
     }
-    sm.blk[w][lane] = id;
-    sm.slot[w][lane] = sl;
+    sm.u.run.blk[w][lane] = id;
+    sm.u.run.slot[w][lane] = sl;
     wave_lds_fence();
-    // ---- P V: this lane's D / 64 dims of each token of the chunk
+    // ---- P V: this lane's D / 64 dims of each token of the chunk, eight tokens' V loads
+    // in flight at a time (tokens past the partition read the last one with P = 0)
+    constexpr int U = 8;
     const int nt = min(64, t1 - c0);
-    for (int j = 0; j < nt; ++j) {
-      const size_t hbj = (size_t)sm.blk[w][j] * a.KVH + kvh;
-      const int slj = sm.slot[w][j];
-      float v[DPL];
+    for (int j0 = 0; j0 < nt; j0 += U) {
+      float v[U][DPL];
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        const int d = lane * DPL + i;
-        const size_t e = XP ? (hbj * D + d) * bs + slj : (hbj * bs + slj) * D + d;
-        v[i] = load1<QF32, KV>(vc + e * EB);
+      for (int u = 0; u < U; ++u) {
+        const int j = min(j0 + u, nt - 1);
+        const size_t hbj = (size_t)sm.u.run.blk[w][j] * a.KVH + kvh;
+        const int slj = sm.u.run.slot[w][j];
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) {
+          const int d = lane * DPL + i;
+          const size_t e = XP ? (hbj * D + d) * bs + slj : (hbj * bs + slj) * D + d;
+          v[u][i] = load1<QF32, KV>(vc + e * EB);
+        }
       }
 #pragma unroll
-      for (int g = 0; g < kGenG; ++g) {
-        if (g < G) {
-          const float pj = sm.p[w][g][j];
+      for (int u = 0; u < U; ++u) {
+        if (j0 + u < nt) {
 #pragma unroll
-          for (int i = 0; i < DPL; ++i) acc[g][i] = fmaf(pj, v[i], acc[g][i]);
+          for (int g = 0; g < kGenG; ++g) {
+            if (g < G) {
+              const float pj = sm.u.run.p[w][g][j0 + u];
+#pragma unroll
+              for (int i = 0; i < DPL; ++i) acc[g][i] = fmaf(pj, v[u][i], acc[g][i]);
+            }
+          }
         }
       }
     }
     wave_lds_fence();  // the chunk's P and rows are read before the next chunk overwrites them
   }
 
-  // ---- merge the waves through LDS
+  // ---- merge the waves through LDS (the accumulators take the chunk buffers' space)
+  __syncthreads();
 #pragma unroll
   for (int g = 0; g < kGenG; ++g) {
     if (g < G) {
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) sm.red_acc[w][g][lane * DPL + i] = acc[g][i];
+      for (int i = 0; i < DPL; ++i) sm.u.red_acc[w][g][lane * DPL + i] = acc[g][i];
       if (lane == 0) {
         sm.red_m[w][g] = m_run[g];
         sm.red_l[w][g] = l_run[g];
@@ -265,7 +281,7 @@ __global__ __launch_bounds__(64 * kGenW) void decode_generic_kernel(DecodePartia
 #pragma unroll
     for (int v = 0; v < kGenW; ++v) {
       const float f = fast_exp2(sm.red_m[v][g] - M);  // waves without tokens carry -inf: f = 0
-      o = fmaf(f, sm.red_acc[v][g][d], o);
+      o = fmaf(f, sm.u.red_acc[v][g][d], o);
       L = fmaf(f, sm.red_l[v][g], L);
     }
     if (a.kv_fp8) o *= a.v_scale;

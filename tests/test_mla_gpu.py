@@ -281,3 +281,41 @@ def test_mla_split_decode_b64(split):
     o2, l2 = run_gpu(case)  # the prefill kernel with q_len 1: the same values within bf16
     check(o, l, o2, l2, "split decode vs prefill kernel")
     say(f"  max abs err {e:.3e}, lse err {le:.3e}")
+
+
+def test_mla_decode_lengths_past_max_kv_len_stay_in_bounds():
+    """A kv_len above the max_kv_len the call promises (a broken contract) is cut to the
+    launched splits (len_cap = launched splits x split_tokens): partial rows past them stay
+    untouched (NaN here, in arrays wider than the launch), the long sequence's output is
+    attention over its first len_cap keys, and the other sequences are unaffected; both
+    forms of the call."""
+    kv = [100, 700, 40]
+    split, max_kv = 128, 300  # 3 splits launched, len_cap 384
+    case = inputs.make_mla(np.ones(3, dtype=np.int64), np.array(kv) - 1, seed=41, extra_pages=4)
+    t = {k: getattr(case, k).to("cuda") for k in FIELDS}
+    cap = 384
+    P = 6
+    for fused in (False, True):
+        acc = torch.full((3, 16, P, 512), float("nan"), dtype=torch.float32, device="cuda")
+        m = torch.full((3, 16, P), float("nan"), dtype=torch.float32, device="cuda")
+        l = torch.full((3, 16, P), float("nan"), dtype=torch.float32, device="cuda")
+        ctr = torch.zeros(3, dtype=torch.int32, device="cuda") if fused else None
+        say(f"mla decode past max_kv_len: fused={fused}")
+        out, lse = pkv.mla_paged_decode(t["q_nope"], t["q_pe"], t["ckv_cache"], t["kpe_cache"], t["kv_indptr"],
+                                        t["kv_indices"], case.sm_scale, split_tokens=split, max_kv_len=max_kv,
+                                        partials=(acc, m, l), counters=ctr)
+        torch.cuda.synchronize()
+        assert torch.isnan(m[:, :, 3:]).all() and torch.isnan(acc[:, :, 3:]).all(), "rows past the launched splits"
+        o = out.cpu().to(torch.float64).numpy()
+        ls = lse.cpu().to(torch.float64).numpy()
+        ro, rl = run_oracle(case)
+        check(o[[0, 2]], ls[[0, 2]], ro[[0, 2]], rl[[0, 2]], "untouched sequences")
+        # the long sequence: its first `cap` keys
+        kvp = case.kv_indptr.tolist()
+        idx = torch.cat([case.kv_indices[kvp[1]:kvp[1] + cap]])
+        cut = inputs.MlaCase(name="cut", q_nope=case.q_nope[1:2], q_pe=case.q_pe[1:2], ckv_cache=case.ckv_cache,
+                             kpe_cache=case.kpe_cache, qo_indptr=torch.tensor([0, 1], dtype=torch.int32),
+                             kv_indptr=torch.tensor([0, cap], dtype=torch.int32), kv_indices=idx,
+                             sm_scale=case.sm_scale)
+        co, cl = run_oracle(cut)
+        check(o[1:2], ls[1:2], co, cl, "long sequence cut to len_cap")
