@@ -445,7 +445,7 @@ def main():
     if args.workload == "mla_decode_b64":
         case = inputs.mla_decode_b64()
         r = bench_mla_decode(case, args.steps, args.warmup, split=None, fused=False)
-        r2 = bench_mla_decode(case, args.steps, args.warmup, split=None, fused=True)
+        r2 = None if args.no_extra else bench_mla_decode(case, args.steps, args.warmup, split=None, fused=True)
         kv_b = sum(case.kv_lens()) * (512 + 64) * 2
         gbs = kv_b / (r["ms"] * 1e-3) / 1e9
         result = {
@@ -457,7 +457,7 @@ def main():
                        "kv_bytes_per_step": kv_b},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None},
-            "one_launch_us": r2["ms"] * 1e3,
+            "one_launch_us": None if r2 is None else r2["ms"] * 1e3,
         }
         print(json.dumps(result), flush=True)
         return
