@@ -88,7 +88,7 @@ struct Bf16Smem {
 // use; k_scale is folded into scale_log2 and v_scale multiplies the merged accumulator.
 template <int D, int G, bool XP, int W, bool DENSE, bool SPLIT, bool FINAL, bool ALIBI, bool FP8 = false>
 __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const DenseItems& wl, int first_item,
-                                           Bf16Smem<W, G, D>& sm, int grid_parts) {
+                                           Bf16Smem<W, G, D>& sm) {
   using C = Bf16Cfg<D, XP>;
   constexpr int BS = C::BS, ROWB = C::ROWB, KCPL = C::KCPL, LV = C::LV, VT = C::VT, VCPL = C::VCPL;
   constexpr int NVC = C::NVC, NACC = C::NACC, NVREG = C::NVREG;
@@ -147,15 +147,10 @@ __device__ __forceinline__ void bf16_items(const DecodePartialArgs& a, const Den
   auto item_of = [&](int item, int& b, int& kvh, int& p) {
     if constexpr (DENSE) {
       decode_item(wl, item, b, kvh, p);
-    } else {
-      // partition-major from the highest partition down: the empty partitions of short
-      // sequences are dispatched first and exit at once, so every slot they held goes to
-      // a real partition; in ascending order they sit among the long sequences' last
-      // partitions, each holding a slot for a memory round trip while real work waits
+    } else {  // partition-major: empty partitions sit at high indices and are dispatched last
       const int sk = a.S * a.KVH;
-      const int pr = item / sk;
-      const int r = item - pr * sk;
-      p = grid_parts - 1 - pr;
+      p = item / sk;
+      const int r = item - p * sk;
       b = r / a.KVH;
       kvh = r - b * a.KVH;
     }
@@ -635,9 +630,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(bf16_min
     write_sentinels(wl, a.H, grid_parts, a.P, a.m, a.l);
     if constexpr (FINAL) write_empty_outputs<D, true>(wl, a);
     const int first = wg_item(wl, blockIdx.x, gridDim.x, 0);
-    if (first >= 0) bf16_items<D, G, XP, W, true, SPLIT, FINAL, ALIBI, FP8>(a, wl, first, sm, grid_parts);
+    if (first >= 0) bf16_items<D, G, XP, W, true, SPLIT, FINAL, ALIBI, FP8>(a, wl, first, sm);
   } else {
-    bf16_items<D, G, XP, W, false, SPLIT, FINAL, ALIBI, FP8>(a, DenseItems{}, blockIdx.x, sm, grid_parts);
+    bf16_items<D, G, XP, W, false, SPLIT, FINAL, ALIBI, FP8>(a, DenseItems{}, blockIdx.x, sm);
   }
 }
 
@@ -686,8 +681,7 @@ hipError_t launch_bf16_one(const DecodePartialArgs& a, int grid_parts, hipStream
     hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, true, SPLIT, FINAL, ALIBI, FP8>), dim3(grid),
                        dim3(64 * W), lds, s, a, grid_parts);
   } else {
-    // the plain grid: one workgroup per (partition, sequence, kv head), partition-major from
-    // the highest partition down (see item_of)
+    // the plain grid: one workgroup per (partition, sequence, kv head), partition-major
     if (upper > INT32_MAX) return hipErrorNotSupported;
     hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, XP, W, false, SPLIT, FINAL, ALIBI, FP8>), dim3((unsigned)upper),
                        dim3(64 * W), 0, s, a, grid_parts);
