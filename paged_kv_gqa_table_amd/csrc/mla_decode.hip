@@ -244,7 +244,7 @@ void mla_decode_partial_kernel(MlaDecodeArgs a) {
     for (int k = 0; k < kMdKPW; ++k) {
       const int row_k = kMdKPW * w + k;
       const char* row = reinterpret_cast<const char*>(a.ckv) + (size_t)tok[k] * (kMdDc * 2);
-      lds_dma16_s(row, (uint32_t)(lane ^ ckv_swz(row_k)) * 16, &sm.ckv[buf][row_k * kCkvStride]);
+      lds_dma16_s(row, (uint32_t)lane * 16, &sm.ckv[buf][row_k * kCkvStride]);
     }
     // kpe rows: lanes 8k .. 8k+7 move key k (lane i lands in position i of the wave's 8 rows
     // and loads global chunk (i & 7) ^ kpe_swz(row))
@@ -273,7 +273,7 @@ void mla_decode_partial_kernel(MlaDecodeArgs a) {
 
   // this wave's share of a tile's logits: key rows 16 kh + hq (A), its 9 k-steps
   auto logits_partial = [&](int buf) {
-    const uint4* crow = sm.ckv[buf] + (16 * kh + hq) * kCkvStride + (g ^ ckv_swz(hq));
+    const uint4* crow = sm.ckv[buf] + (16 * kh + hq) * kCkvStride + g;
     const uint4* prow = sm.kpe[buf] + (16 * kh + hq) * kKpeChunks;
     uint4 ka[kMdKSW];
 #pragma unroll
@@ -292,7 +292,7 @@ void mla_decode_partial_kernel(MlaDecodeArgs a) {
   float m_ref = kNegInf, m_true = kNegInf, lsum = 0.f;  // head hq (the same in every wave)
   // V^T reads: this lane is source lane 4k + q of its group (see the prefill kernel)
   const int vr = 4 * g + (hq >> 2);
-  const int vcol = (int)((((uint32_t)hq >> 1) & 1) ^ ckv_swz(vr)) * 16 + (hq & 1) * 8;
+  const int vcol = (int)(((uint32_t)hq >> 1) & 1) * 16 + (hq & 1) * 8;
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt % kMdNBUF;

@@ -210,7 +210,7 @@ void mla_prefill_kernel(MlaArgs a) {
   #pragma unroll
         for (int k = 0; k < kKeysPerWave; ++k) tok_next[k] = t[k];  // clamped when used
       };
-      // LDS position i of a ckv row holds global chunk i ^ ckv_swz(row)
+      // LDS position i of a ckv row holds global chunk i
       auto issue_tile = [&](int buf) {
         int tok[kKeysPerWave];
   #pragma unroll
@@ -220,7 +220,7 @@ void mla_prefill_kernel(MlaArgs a) {
         for (int k = 0; k < kKeysPerWave; ++k) {
           const int row_k = kKeysPerWave * w + k;
           const char* row = reinterpret_cast<const char*>(a.ckv) + (size_t)tok[k] * (kDc * 2);
-          lds_dma16_s(row, (uint32_t)(lane ^ ckv_swz(row_k)) * 16, &s_ckv[buf][row_k * kCkvStride]);
+          lds_dma16_s(row, (uint32_t)lane * 16, &s_ckv[buf][row_k * kCkvStride]);
         }
         // kpe rows of the wave's keys: lanes 8k .. 8k+7 move key k (lane i lands in slot i,
         // i.e. position i & 7 of row kKeysPerWave w + k, and loads global chunk
@@ -267,7 +267,7 @@ void mla_prefill_kernel(MlaArgs a) {
           const uint4* kpe = s_kpe[buf];
           // A: key row (l%16) of each half, dims (l/16)*8.. of each k-step; the two halves'
           // chains interleave so each LDS read has the other chain's MFMA to hide behind
-          const uint4* crow = ckv + hq * kCkvStride + (g ^ ckv_swz(hq));
+          const uint4* crow = ckv + hq * kCkvStride + g;
           const uint4* prow = kpe + hq * kKpeChunks;
   #pragma unroll
           for (int s = 0; s < 16; ++s) {
@@ -323,9 +323,9 @@ void mla_prefill_kernel(MlaArgs a) {
           // ---- O^T += V^T P^T over 32 blocks of 16 dims. This lane is source lane 4k + q of
           // its group: it points at dims 16 n + 4 q .. +3 of keys 4g + k (k-slots 0..3 of the
           // group) and 16 + 4g + k (k-slots 4..7), the key order of P^T.
-          // (rows r and r + 16 share ckv_swz(r); chunk 2n + ((hq >> 1) & 1) sits at 2n + that ^ swz)
+          // (chunk 2n + ((hq >> 1) & 1) of a row, at byte (hq & 1) * 8 in it)
           const int vr = 4 * g + (hq >> 2);
-          const int vcol = (int)((((uint32_t)hq >> 1) & 1) ^ ckv_swz(vr)) * 16 + (hq & 1) * 8;
+          const int vcol = (int)(((uint32_t)hq >> 1) & 1) * 16 + (hq & 1) * 8;
           const char* vrow_lo = reinterpret_cast<const char*>(ckv + vr * kCkvStride) + vcol;
           const char* vrow_hi = reinterpret_cast<const char*>(ckv + (16 + vr) * kCkvStride) + vcol;
   #pragma unroll

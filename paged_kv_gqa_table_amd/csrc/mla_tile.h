@@ -9,7 +9,7 @@ namespace mla {
 
 constexpr int kCkvChunks = 512 * 2 / 16;     // 64 16-byte chunks of a ckv row
 constexpr int kKpeChunks = 64 * 2 / 16;      // 8 chunks of a kpe row
-constexpr int kCkvStride = kCkvChunks + 2;   // padded LDS row (chunks), see ckv_swz
+constexpr int kCkvStride = kCkvChunks + 2;   // padded LDS row (chunks): see the bank note below
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -19,18 +19,19 @@ PKV_DEVICE f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
                                                  c, 0, 0, 0);
 }
 
-// LDS bank spreading. A ckv row r sits at stride kCkvStride (32 B past a multiple of
-// 1 KiB) with 16-byte chunk c at position c ^ ckv_swz(r). The logits read 16 B per lane
-// from 16 consecutive rows at one chunk; the padding puts rows on even chunk offsets and
-// the swizzle moves every other group of 4 rows to the odd ones, so any 8 (or 16) rows
-// land on distinct chunks of a 128-byte (256-byte) bank line. The transposing V reads
-// take 32 B from each of 4 (8) consecutive rows; the padding alone keeps those apart and
-// the swizzle, which only flips chunk bit 0, never splits a 32-byte pair.
-PKV_DEVICE uint32_t ckv_swz(int r) { return (uint32_t)(((r >> 2) ^ (r >> 3)) & 1); }
+// LDS bank spreading, as measured on gfx950 with a read probe (16-byte reads per lane,
+// eight waves per CU): a ckv row sits at stride kCkvStride, 32 B past a multiple of 1 KiB,
+// with its chunks in order. The logits read one 16-byte chunk from each of 16 consecutive
+// rows per 16-lane group, and at this stride those reads run at the rate of a contiguous
+// read (5.8 cycles per instruction per CU); rows at 1 KiB, or at 1 KiB + 16 or + 64 B, or
+// this stride with chunk bit 0 flipped by row bits 2 ^ 3, take 8 to 32 cycles. The
+// transposing V reads (32 B from each of 16 rows) take the same time under every one of
+// those layouts.
 // kpe rows are packed (128 B) because one transfer fills 8 of them; chunk c of row r sits
-// at position c ^ kpe_swz(r), which sends the 8 (16) rows of a logits read to distinct
-// chunks of a bank line.
-PKV_DEVICE uint32_t kpe_swz(int r) { return (uint32_t)((r & 7) ^ ((r >> 3) & 1)); }
+// at position c ^ kpe_swz(r), which puts the 16 rows of a logits read on 16 distinct
+// 16-byte positions of two 128-byte lines (the contiguous rate, where the unswizzled
+// packed rows take 16 cycles and chunk c ^ (r & 7) ^ (r >> 3) 8).
+PKV_DEVICE uint32_t kpe_swz(int r) { return (uint32_t)(r & 7); }
 
 PKV_DEVICE void vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
