@@ -19,18 +19,18 @@ PKV_DEVICE f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
                                                  c, 0, 0, 0);
 }
 
-// LDS bank spreading, as measured on gfx950 with a read probe (16-byte reads per lane,
-// eight waves per CU): a ckv row sits at stride kCkvStride, 32 B past a multiple of 1 KiB,
-// with its chunks in order. The logits read one 16-byte chunk from each of 16 consecutive
-// rows per 16-lane group, and at this stride those reads run at the rate of a contiguous
-// read (5.8 cycles per instruction per CU); rows at 1 KiB, or at 1 KiB + 16 or + 64 B, or
-// this stride with chunk bit 0 flipped by row bits 2 ^ 3, take 8 to 32 cycles. The
-// transposing V reads (32 B from each of 16 rows) take the same time under every one of
-// those layouts.
+// LDS bank spreading, as measured on gfx950 with a read probe (eight waves per CU, cycles
+// per read instruction per CU): a ckv row sits at stride kCkvStride, 32 B past a multiple
+// of 1 KiB, with its chunks in order. The logits read one 16-byte chunk from each of 16
+// consecutive rows per 16-lane group, and at this stride those reads run at the rate of a
+// contiguous read (4.4 cycles); rows at 1 KiB take 22 cycles, rows at 1 KiB + 16 or + 64 B,
+// or this stride with chunk bit 0 flipped by row bits 2 ^ 3, 5.5. The transposing V reads
+// (32 B from each of 16 rows) run at this stride at the rate of a contiguous transposing
+// read (4.6 cycles per 512 B).
 // kpe rows are packed (128 B) because one transfer fills 8 of them; chunk c of row r sits
 // at position c ^ kpe_swz(r), which puts the 16 rows of a logits read on 16 distinct
-// 16-byte positions of two 128-byte lines (the contiguous rate, where the unswizzled
-// packed rows take 16 cycles and chunk c ^ (r & 7) ^ (r >> 3) 8).
+// 16-byte positions of two 128-byte lines: 4.4 cycles, where the unswizzled packed rows
+// take 11 and chunk c ^ (r & 7) ^ (r >> 3) 5.5.
 PKV_DEVICE uint32_t kpe_swz(int r) { return (uint32_t)(r & 7); }
 
 PKV_DEVICE void vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
