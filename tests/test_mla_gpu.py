@@ -319,3 +319,54 @@ def test_mla_decode_lengths_past_max_kv_len_stay_in_bounds():
                              sm_scale=case.sm_scale)
         co, cl = run_oracle(cut)
         check(o[1:2], ls[1:2], co, cl, "long sequence cut to len_cap")
+
+
+def test_mla_pool_past_2_25_pages():
+    """Pools of more than 2^25 pages: a kpe row's byte offset (page x 128) no longer fits in
+    32 bits, so both MLA kernels move the kpe rows one transfer per key instead of one per
+    eight keys. A small batch is placed at page ids above 2^25 of a 34 GB pool (only the rows
+    it uses are written); the prefill and the split-K decode must match the oracle, and the
+    same batch on a small pool bit for bit."""
+    case = inputs.make_mla(np.array([1, 37, 5, 64]), np.array([300, 0, 900, 33]), seed=47, extra_pages=7)
+    big = (1 << 25) + 4096
+    shift = (1 << 25) + 1000
+    assert int(case.kv_indices.max()) + shift < big
+    small = {k: getattr(case, k).to("cuda") for k in FIELDS}
+    say(f"mla pool past 2^25 pages: {big} pages, batch of {case.kv_indptr.numel() - 1}")
+    ckv = torch.empty((big, 1, 512), dtype=torch.bfloat16, device="cuda")
+    kpe = torch.empty((big, 1, 64), dtype=torch.bfloat16, device="cuda")
+    try:
+        rows = torch.arange(case.ckv_cache.shape[0], device="cuda") + shift
+        ckv.index_copy_(0, rows, small["ckv_cache"])
+        kpe.index_copy_(0, rows, small["kpe_cache"])
+        idx = small["kv_indices"] + shift
+        # prefill
+        out_s = torch.full_like(small["q_nope"], float("nan"))
+        lse_s = torch.full(small["q_nope"].shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+        pkv.mla_paged_prefill(small["q_nope"], small["q_pe"], small["ckv_cache"], small["kpe_cache"],
+                              small["qo_indptr"], small["kv_indptr"], small["kv_indices"], case.sm_scale,
+                              out=out_s, lse=lse_s)
+        out_b = torch.full_like(out_s, float("nan"))
+        lse_b = torch.full_like(lse_s, float("nan"))
+        pkv.mla_paged_prefill(small["q_nope"], small["q_pe"], ckv, kpe, small["qo_indptr"], small["kv_indptr"], idx,
+                              case.sm_scale, out=out_b, lse=lse_b)
+        torch.cuda.synchronize()
+        assert torch.equal(out_b, out_s) and torch.equal(lse_b, lse_s), "prefill: large pool differs from small"
+        ro, rl = run_oracle(case)
+        check(out_b.cpu().double().numpy(), lse_b.cpu().double().numpy(), ro, rl, "prefill, pool past 2^25 pages")
+        # split-K decode: the last query token of each batch, over all of that batch's keys
+        last = (small["qo_indptr"][1:] - 1).long()
+        q_nope, q_pe = small["q_nope"][last].contiguous(), small["q_pe"][last].contiguous()
+        o1, l1 = pkv.mla_paged_decode(q_nope, q_pe, small["ckv_cache"], small["kpe_cache"], small["kv_indptr"],
+                                      small["kv_indices"], case.sm_scale, split_tokens=128)
+        o2, l2 = pkv.mla_paged_decode(q_nope, q_pe, ckv, kpe, small["kv_indptr"], idx, case.sm_scale,
+                                      split_tokens=128)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), "decode: large pool differs from small"
+        # the decode's token sees every key of its batch: the prefill rows of the last tokens
+        # (each batch's last query row is its last position) are the same computation
+        check(o2.cpu().double().numpy(), l2.cpu().double().numpy(), ro[last.cpu().numpy()],
+              rl[last.cpu().numpy()], "decode, pool past 2^25 pages")
+    finally:
+        del ckv, kpe
+        torch.cuda.empty_cache()
