@@ -55,7 +55,9 @@ PKV_DEVICE uint32_t pick_pair(const uint4& x, const uint4& y, int e) {
 
 template <int W, int D>
 struct MfmaSmem {
-  float red_acc[W][16][D];
+  // rows padded by one float: a merge store writes one column of the 16 heads' rows, which
+  // at a row stride of D floats (a multiple of the 64 banks) all land in one bank
+  float red_acc[W][16][D + 1];
   float red_m[W][16];
   float red_mref[W][16];
   float red_l[W][16];
