@@ -37,7 +37,7 @@ def test_no_gpu_is_an_error_not_a_fallback():
     assert '"metric"' not in r.stdout
 
 
-@pytest.mark.parametrize("workload", ["llama_gqa4", "wide_gqa6"])
+@pytest.mark.parametrize("workload", ["llama_gqa4", "wide_gqa6", "skewed_gqa8"])
 def test_counter_summaries_match_the_sources(workload):
     bench = _bench_module()
     assert os.path.exists(bench.traffic_profile_path(workload))
